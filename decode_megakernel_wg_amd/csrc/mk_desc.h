@@ -1,0 +1,73 @@
+// Task descriptors and counter layout shared by the host planner and the persistent kernel.
+//
+// A descriptor is 32 int32 words (aimodeling.com "Cohere megakernel engine: one CUDA file, 1.58x vLLM
+// on H100", section "Caveats and takeaways": one uniform ABI of 32-int32 task descriptors).  The word
+// meanings below and the opcode set are this library's own.
+#pragma once
+#include <stdint.h>
+
+namespace mk {
+
+enum Op : int32_t {
+  OP_EMBED = 1,   // x[b][rows] = embed[token_b][rows]; partial sum of squares            -> XREADY[0]
+  OP_ROUTER = 2,  // router logits for experts [r0, r1) (fp64 accumulation)             -> ROUTER_DONE[l]
+  OP_QKV = 3,     // rows [r0, r1) of KV group g's fused [q heads; k; v] projection     -> QKV_DONE[l][g]
+  OP_ATTN = 4,    // split s of (sequence b, KV group g): partial softmax(qK^T)V; last arriver combines -> ATTN_DONE[l][g]
+  OP_UP = 5,      // gate+up rows [r0, r1) of expert slot s, SwiGLU                      -> UP_DONE[l][s]
+  OP_OPROJ = 6,   // rows [r0, r1) of Wo restricted to group g's columns                -> RESID_IN[l][tile]
+  OP_DOWN = 7,    // rows [r0, r1) of expert slot s's down projection, times the gate   -> RESID_IN[l][tile]
+  OP_RESID = 8,   // x += sum of branch partials on rows [r0, r1); partial sum of squares -> XREADY[l+1]
+  OP_LMHEAD = 9,  // logits for vocab rows [r0, r1); tile argmax; last arriver picks the next tokens
+  OP_COUNT = 10
+};
+
+// Descriptor words.
+enum Word : int {
+  W_OP = 0,
+  W_LAYER = 1,
+  W_A = 2,  // EMBED/RESID: row tile; QKV/OPROJ: KV group; UP/DOWN: slot; ATTN: sequence; LMHEAD: tile
+  W_B = 3,  // ATTN: KV group
+  W_C = 4,  // ATTN: split index
+  W_D = 5,  // ATTN: split count
+  W_R0 = 6,
+  W_R1 = 7,
+  W_WAIT0 = 8,  // 4 waits of (counter, target): words 8..15; counter -1 = none
+  W_SIG = 16,   // counter to increment on completion (-1 = none)
+  W_SIGN = 17,  // increment
+  W_ARR = 18,   // arrival counter for the last-arriver epilogue (-1 = none)
+  W_ARRN = 19,  // arrivals expected
+  W_SEQ = 31    // task index (debug)
+};
+constexpr int N_WAITS = 4;
+constexpr int DESC_WORDS = 32;
+
+// Tile sizes chosen by the planner (rows per task); the kernel reads r0/r1 from the descriptor.
+constexpr int ATTN_SPLIT_POS = 512;  // positions per attention split (before clamping)
+constexpr int ATTN_MAX_SPLITS = 256;
+
+// Counter index layout for a model/batch; computed identically by planner and host launcher.
+struct CounterLayout {
+  int32_t ticket, done, xready, qkv_done, router_done, attn_arrive, attn_done, up_done, resid_in, lm_arrive, total;
+  int32_t n_layers, n_kv, n_slots, n_row_tiles, batch;
+  void build(int L, int Hkv, int B, int slots, int nrt) {
+    n_layers = L;
+    n_kv = Hkv;
+    n_slots = slots;
+    n_row_tiles = nrt;
+    batch = B;
+    int32_t o = 0;
+    ticket = o; o += 32;     // own cache line
+    done = o; o += 32;
+    xready = o; o += L + 1;
+    qkv_done = o; o += L * Hkv;
+    router_done = o; o += L;
+    attn_arrive = o; o += L * B * Hkv;
+    attn_done = o; o += L * Hkv;
+    up_done = o; o += L * slots;
+    resid_in = o; o += L * nrt;
+    lm_arrive = o; o += 1;
+    total = (o + 31) & ~31;
+  }
+};
+
+}  // namespace mk

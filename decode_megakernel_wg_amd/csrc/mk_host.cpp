@@ -1,0 +1,357 @@
+// C ABI of the decode megakernel: handle management, task-list upload and the per-step launch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_desc.h"
+#include "mk_kargs.h"
+#include "mk_plan.h"
+
+extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int grid, hipStream_t stream);
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIPCHK(expr)                                                                                  \
+  do {                                                                                                \
+    hipError_t e_ = (expr);                                                                           \
+    if (e_ != hipSuccess) return fail(MK_E_HIP, std::string(#expr " failed: ") + hipGetErrorString(e_)); \
+  } while (0)
+
+struct DevBuf {
+  void* p = nullptr;
+  size_t bytes = 0;
+};
+
+}  // namespace
+
+struct mk_model {
+  mk_model_desc desc{};
+  std::vector<float> bias;
+  int device = 0;
+  int n_cu = 0;
+  int grid = 0;
+  uint32_t dbg = 0;
+  mk::Tiling tiling{};
+  int max_slots = 0;
+  int64_t max_tasks = 0;
+  int32_t max_counters = 0;
+  // device memory owned by the handle
+  std::vector<DevBuf> owned;
+  mk::LayerW* layers = nullptr;
+  const uint16_t *embed = nullptr, *lm_head = nullptr, *final_norm = nullptr;
+  float* router_bias = nullptr;
+  double* inv_freq = nullptr;
+  int32_t* tasks = nullptr;
+  uint32_t* ctr = nullptr;
+  uint32_t* err = nullptr;
+  float *x = nullptr, *ssq = nullptr, *rope_cs = nullptr, *qkv = nullptr, *apart = nullptr, *attn_o = nullptr, *opart = nullptr;
+  float *rlogits = nullptr, *route_gate = nullptr, *h = nullptr, *ypart = nullptr, *lmbest_v = nullptr, *dump_n = nullptr;
+  int32_t *route_sel = nullptr, *lmbest_i = nullptr, *next_tok = nullptr;
+  uint32_t *task_done = nullptr, *ctr_snapshot = nullptr;
+  // task list
+  mk::Plan plan;
+  bool have_plan = false, dirty = false;
+  int32_t* staging = nullptr;  // pinned host copy of the task list
+  hipEvent_t upload_done = nullptr;
+  bool upload_pending = false;
+  bool stepped = false;
+
+  template <class T>
+  int alloc(T** out, size_t count) {
+    void* p = nullptr;
+    const size_t bytes = std::max<size_t>(count * sizeof(T), 256);
+    if (hipMalloc(&p, bytes) != hipSuccess) return fail(MK_E_NOMEM, "hipMalloc of " + std::to_string(bytes) + " bytes failed");
+    if (hipMemset(p, 0, bytes) != hipSuccess) return fail(MK_E_HIP, "hipMemset failed");
+    owned.push_back({p, bytes});
+    *out = static_cast<T*>(p);
+    return MK_OK;
+  }
+  void release() {
+    for (auto& b : owned) (void)hipFree(b.p);
+    owned.clear();
+    if (staging) (void)hipHostFree(staging);
+    staging = nullptr;
+    if (upload_done) (void)hipEventDestroy(upload_done);
+    upload_done = nullptr;
+  }
+};
+
+extern "C" {
+
+const char* mk_last_error(void) { return g_err.c_str(); }
+
+int mk_plan_tasks(const mk_model_desc* desc, const mk_batch* batch, int32_t* tasks_out, int64_t cap, int64_t* n_tasks,
+                  int32_t* n_counters) {
+  if (!n_tasks) return fail(MK_E_INVAL, "null n_tasks");
+  mk::Plan P;
+  std::string msg;
+  int rc = mk::plan_step(desc, batch, &P, &msg);
+  if (rc) return fail(rc, msg);
+  *n_tasks = P.n_tasks();
+  if (n_counters) *n_counters = P.cl.total;
+  if (tasks_out) {
+    if (cap < P.n_tasks()) return fail(MK_E_RANGE, "tasks_out holds fewer descriptors than the plan");
+    std::memcpy(tasks_out, P.desc.data(), P.desc.size() * sizeof(int32_t));
+  }
+  return MK_OK;
+}
+
+int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out) {
+  if (!out) return fail(MK_E_INVAL, "null output handle");
+  *out = nullptr;
+  std::string msg;
+  int rc = mk::validate_desc(desc, &msg);
+  if (rc) return fail(rc, msg);
+  if (!w || !w->embed || !w->lm_head || !w->final_norm || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->w_router ||
+      !w->w_gate || !w->w_up || !w->w_down)
+    return fail(MK_E_INVAL, "null weight pointer");
+  const int L = desc->n_layers;
+  for (int l = 0; l < L; ++l)
+    if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->w_router[l] || !w->w_gate[l] || !w->w_up[l] ||
+        !w->w_down[l])
+      return fail(MK_E_INVAL, "null per-layer weight pointer at layer " + std::to_string(l));
+
+  mk_model* m = new mk_model();
+  m->desc = *desc;
+  m->desc.router_bias = nullptr;
+  HIPCHK(hipGetDevice(&m->device));
+  HIPCHK(hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, m->device));
+  m->grid = m->n_cu;
+  m->tiling = mk::choose_tiling(desc);
+  const mk::Tiling& t = m->tiling;
+  const int d = desc->d_model, Hq = desc->n_q_heads, Hkv = desc->n_kv_heads, dh = desc->d_head, E = desc->n_experts;
+  const int k = desc->top_k, F = desc->d_ffn, maxB = desc->max_batch, grp = Hq / Hkv;
+  m->max_slots = std::min(E, maxB * k);
+  mk::CounterLayout cl;
+  cl.build(L, Hkv, maxB, m->max_slots, t.n_rt);
+  m->max_counters = cl.total;
+  m->max_tasks = (int64_t)t.n_rt + (int64_t)L * (t.n_router + Hkv * t.n_qkv_per_group + (int64_t)Hkv * maxB * mk::ATTN_MAX_SPLITS +
+                                                 (int64_t)m->max_slots * t.n_up + Hkv * t.n_rt + (int64_t)m->max_slots * t.n_rt + t.n_rt) +
+                 t.n_lm;
+
+  auto cleanup = [&](int code) {
+    m->release();
+    delete m;
+    return code;
+  };
+  std::vector<mk::LayerW> lw(L);
+  for (int l = 0; l < L; ++l)
+    lw[l] = mk::LayerW{(const uint16_t*)w->attn_norm[l], (const uint16_t*)w->wq[l], (const uint16_t*)w->wk[l], (const uint16_t*)w->wv[l],
+                       (const uint16_t*)w->wo[l],        (const uint16_t*)w->w_router[l], (const uint16_t*)w->w_gate[l],
+                       (const uint16_t*)w->w_up[l],      (const uint16_t*)w->w_down[l]};
+  m->bias.assign(E, 0.0f);
+  if (desc->router_bias) std::copy(desc->router_bias, desc->router_bias + E, m->bias.begin());
+  std::vector<double> invf(dh / 2);
+  for (int i = 0; i < dh / 2; ++i) invf[i] = std::pow((double)desc->rope_base, -2.0 * i / dh);
+
+  if ((rc = m->alloc(&m->layers, L)) || (rc = m->alloc(&m->router_bias, E)) || (rc = m->alloc(&m->inv_freq, dh / 2)) ||
+      (rc = m->alloc(&m->tasks, (size_t)m->max_tasks * mk::DESC_WORDS)) || (rc = m->alloc(&m->ctr, m->max_counters)) ||
+      (rc = m->alloc(&m->err, 8)) || (rc = m->alloc(&m->x, (size_t)maxB * d)) || (rc = m->alloc(&m->ssq, (size_t)maxB * t.n_rt)) ||
+      (rc = m->alloc(&m->rope_cs, (size_t)maxB * dh)) || (rc = m->alloc(&m->qkv, (size_t)maxB * Hkv * (grp + 2) * dh)) ||
+      (rc = m->alloc(&m->apart, (size_t)maxB * Hkv * mk::ATTN_MAX_SPLITS * grp * (dh + 2))) ||
+      (rc = m->alloc(&m->attn_o, (size_t)maxB * Hq * dh)) || (rc = m->alloc(&m->opart, (size_t)Hkv * maxB * d)) ||
+      (rc = m->alloc(&m->rlogits, (size_t)L * maxB * E)) || (rc = m->alloc(&m->route_sel, (size_t)L * maxB * k)) ||
+      (rc = m->alloc(&m->route_gate, (size_t)L * maxB * k)) || (rc = m->alloc(&m->h, (size_t)m->max_slots * maxB * F)) ||
+      (rc = m->alloc(&m->ypart, (size_t)maxB * k * d)) || (rc = m->alloc(&m->lmbest_v, (size_t)maxB * t.n_lm)) ||
+      (rc = m->alloc(&m->lmbest_i, (size_t)maxB * t.n_lm)) || (rc = m->alloc(&m->next_tok, maxB)) ||
+      (rc = m->alloc(&m->ctr_snapshot, m->max_counters)))
+    return cleanup(rc);
+  if (hipHostMalloc((void**)&m->staging, (size_t)m->max_tasks * mk::DESC_WORDS * sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
+    m->staging = nullptr;
+    return cleanup(fail(MK_E_NOMEM, "pinned staging allocation failed"));
+  }
+  if (hipEventCreateWithFlags(&m->upload_done, hipEventDisableTiming) != hipSuccess) return cleanup(fail(MK_E_HIP, "hipEventCreate failed"));
+  if (hipMemcpy(m->layers, lw.data(), sizeof(mk::LayerW) * L, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(m->router_bias, m->bias.data(), sizeof(float) * E, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(m->inv_freq, invf.data(), sizeof(double) * invf.size(), hipMemcpyHostToDevice) != hipSuccess)
+    return cleanup(fail(MK_E_HIP, "upload of the model tables failed"));
+  m->embed = (const uint16_t*)w->embed;
+  m->lm_head = (const uint16_t*)w->lm_head;
+  m->final_norm = (const uint16_t*)w->final_norm;
+  *out = m;
+  return MK_OK;
+}
+
+int mk_build_tasks(mk_model* m, const mk_batch* batch, int32_t* tasks_out, int64_t cap, int64_t* n_tasks) {
+  if (!m || !n_tasks) return fail(MK_E_INVAL, "null handle or n_tasks");
+  std::string msg;
+  mk::Plan P;
+  int rc = mk::plan_step(&m->desc, batch, &P, &msg);
+  if (rc) return fail(rc, msg);
+  *n_tasks = P.n_tasks();
+  if (P.n_tasks() > m->max_tasks) return fail(MK_E_INVAL, "task list larger than the handle's bound");
+  if (tasks_out && cap < P.n_tasks()) return fail(MK_E_RANGE, "tasks_out holds fewer descriptors than the plan");
+  if (tasks_out) std::memcpy(tasks_out, P.desc.data(), P.desc.size() * sizeof(int32_t));
+  m->plan = std::move(P);
+  m->have_plan = true;
+  m->dirty = true;
+  return MK_OK;
+}
+
+int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* page_tables, void* kv_pages,
+                   float* logits_out, void* stream) {
+  if (!m) return fail(MK_E_INVAL, "null handle");
+  if (!m->have_plan) return fail(MK_E_STATE, "mk_build_tasks has not been called");
+  if (!tokens || !seq_lens || !page_tables || !kv_pages || !logits_out) return fail(MK_E_INVAL, "null step pointer");
+  hipStream_t s = (hipStream_t)stream;
+  const mk::Plan& P = m->plan;
+  if (m->dirty) {
+    if (m->upload_pending) HIPCHK(hipEventSynchronize(m->upload_done));  // staging may still feed the previous copy
+    std::memcpy(m->staging, P.desc.data(), P.desc.size() * sizeof(int32_t));
+    HIPCHK(hipMemcpyAsync(m->tasks, m->staging, P.desc.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
+    HIPCHK(hipEventRecord(m->upload_done, s));
+    m->upload_pending = true;
+    m->dirty = false;
+  }
+  if (m->task_done) HIPCHK(hipMemsetAsync(m->task_done, 0, sizeof(uint32_t) * P.n_tasks(), s));
+  const mk_model_desc& D = m->desc;
+  mk::KArgs a{};
+  a.L = D.n_layers;
+  a.d = D.d_model;
+  a.Hq = D.n_q_heads;
+  a.Hkv = D.n_kv_heads;
+  a.dh = D.d_head;
+  a.E = D.n_experts;
+  a.k = D.top_k;
+  a.F = D.d_ffn;
+  a.V = D.vocab;
+  a.B = P.B;
+  a.n_slots = P.n_slots;
+  a.max_pages = D.max_pages_per_seq;
+  a.n_rt = P.t.n_rt;
+  a.n_lm = P.t.n_lm;
+  a.n_pages = D.n_pages;
+  a.eps = D.rms_eps;
+  a.n_tasks = (int32_t)P.n_tasks();
+  a.n_counters = P.cl.total;
+  a.c_ticket = P.cl.ticket;
+  a.c_done = P.cl.done;
+  a.layers = m->layers;
+  a.embed = m->embed;
+  a.lm_head = m->lm_head;
+  a.final_norm = m->final_norm;
+  a.router_bias = m->router_bias;
+  a.inv_freq = m->inv_freq;
+  a.tokens = tokens;
+  a.seq_lens = seq_lens;
+  a.page_tables = page_tables;
+  a.kv = (uint16_t*)kv_pages;
+  a.logits = logits_out;
+  a.tasks = m->tasks;
+  a.ctr = m->ctr;
+  a.err = m->err;
+  a.x = m->x;
+  a.ssq = m->ssq;
+  a.rope_cs = m->rope_cs;
+  a.qkv = m->qkv;
+  a.apart = m->apart;
+  a.attn_o = m->attn_o;
+  a.opart = m->opart;
+  a.rlogits = m->rlogits;
+  a.route_sel = m->route_sel;
+  a.route_gate = m->route_gate;
+  a.h = m->h;
+  a.ypart = m->ypart;
+  a.lmbest_v = m->lmbest_v;
+  a.lmbest_i = m->lmbest_i;
+  a.next_tok = m->next_tok;
+  a.dump_n = (m->dbg & MK_DBG_DUMP_N) ? m->dump_n : nullptr;
+  a.task_done = m->task_done;
+  a.ctr_snapshot = m->ctr_snapshot;
+  HIPCHK(mk_launch_persistent(&a, m->grid, s));
+  m->stepped = true;
+  return MK_OK;
+}
+
+int mk_next_tokens(mk_model* m, int32_t** dev_ptr) {
+  if (!m || !dev_ptr) return fail(MK_E_INVAL, "null argument");
+  *dev_ptr = m->next_tok;
+  return MK_OK;
+}
+
+int mk_status(mk_model* m, void* stream) {
+  if (!m) return fail(MK_E_INVAL, "null handle");
+  HIPCHK(hipStreamSynchronize((hipStream_t)stream));
+  uint32_t e[8];
+  HIPCHK(hipMemcpy(e, m->err, sizeof(e), hipMemcpyDeviceToHost));
+  if (e[mk::ERR_CODE] == 0 && e[mk::ERR_ABORT] == 0) return MK_OK;
+  static const char* names[] = {"none", "dependency wait timed out", "token out of range", "page index out of range",
+                                "sequence length out of range", "unknown opcode"};
+  const uint32_t c = e[mk::ERR_CODE];
+  std::string msg = std::string("device fault: ") + (c < 6 ? names[c] : "unknown") + " (task " + std::to_string(e[mk::ERR_TASK]) + ")";
+  HIPCHK(hipMemset(m->err, 0, sizeof(e)));
+  HIPCHK(hipMemset(m->ctr, 0, sizeof(uint32_t) * m->max_counters));
+  return fail(MK_E_DEVICE, msg);
+}
+
+int mk_debug_set(mk_model* m, uint32_t flags) {
+  if (!m) return fail(MK_E_INVAL, "null handle");
+  if ((flags & MK_DBG_DUMP_N) && !m->dump_n) {
+    int rc = m->alloc(&m->dump_n, (size_t)m->desc.n_layers * m->desc.max_batch * m->desc.d_model);
+    if (rc) return rc;
+  }
+  if (!m->task_done) {
+    int rc = m->alloc(&m->task_done, (size_t)m->max_tasks);
+    if (rc) return rc;
+  }
+  m->dbg = flags;
+  return MK_OK;
+}
+
+int mk_debug_read(mk_model* m, int kind, void* host_dst, int64_t bytes) {
+  if (!m || !host_dst || bytes < 0) return fail(MK_E_INVAL, "null argument");
+  if (!m->have_plan) return fail(MK_E_STATE, "no step has been planned");
+  HIPCHK(hipDeviceSynchronize());
+  const mk_model_desc& D = m->desc;
+  const int64_t L = D.n_layers, B = m->plan.B;
+  const void* src = nullptr;
+  int64_t avail = 0;
+  switch (kind) {
+    case MK_DBGK_ROUTE_SEL: src = m->route_sel; avail = L * B * D.top_k * 4; break;
+    case MK_DBGK_ROUTE_GATE: src = m->route_gate; avail = L * B * D.top_k * 4; break;
+    case MK_DBGK_ROUTER_LOGITS: src = m->rlogits; avail = L * B * D.n_experts * 4; break;
+    case MK_DBGK_NORM_IN:
+      if (!(m->dbg & MK_DBG_DUMP_N)) return fail(MK_E_STATE, "MK_DBG_DUMP_N is not enabled");
+      src = m->dump_n;
+      avail = L * B * D.d_model * 4;
+      break;
+    case MK_DBGK_COUNTERS: src = m->ctr_snapshot; avail = (int64_t)m->plan.cl.total * 4; break;
+    case MK_DBGK_TASK_DONE:
+      if (!m->task_done) return fail(MK_E_STATE, "mk_debug_set has not been called");
+      src = m->task_done;
+      avail = m->plan.n_tasks() * 4;
+      break;
+    default: return fail(MK_E_INVAL, "unknown debug kind");
+  }
+  if (bytes > avail) return fail(MK_E_RANGE, "request larger than the debug buffer");
+  HIPCHK(hipMemcpy(host_dst, src, (size_t)bytes, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+int mk_set_grid(mk_model* m, int32_t n_workgroups) {
+  if (!m || n_workgroups < 0) return fail(MK_E_INVAL, "bad argument");
+  m->grid = n_workgroups == 0 ? m->n_cu : n_workgroups;
+  return MK_OK;
+}
+
+int mk_free_model(mk_model* m) {
+  if (!m) return fail(MK_E_INVAL, "null handle");
+  m->release();
+  delete m;
+  return MK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,244 @@
+// Host-side task planning for one decode step (no device code, no HIP calls).
+//
+// The step's graph is expressed as per-tile tasks in topological order, the way the pages describe the
+// task list: each task is one operation on one tile, and dependencies are counters, not kernel
+// boundaries (agenticcommons.xyz "Cohere North Mini Code megakernel serving engine", section
+// Megakernel 的運作方式).  Per layer the order is
+//   ROUTER, QKV, ATTN, UP, OPROJ, DOWN, RESID
+// so that workgroups claiming the next layer's router and QKV tasks start their weight loads while the
+// current layer's tail still runs (same page, section 三個實際的加速來源, item 3: router and QKV weights
+// are prefetched most aggressively, from the previous layer's O-proj tail), attention and MoE tasks of
+// one layer interleave to backfill idle compute units (item 1, parallel layer), and each KV group's
+// O-proj waits only on that group's attention and each expert's down projection only on its own up
+// projection (item 2, false dependencies).
+#include "mk_plan.h"
+
+#include <algorithm>
+#include <cstring>
+
+namespace mk {
+
+static bool is_pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+int validate_desc(const mk_model_desc* d, std::string* msg) {
+  if (!d) {
+    *msg = "null model descriptor";
+    return MK_E_INVAL;
+  }
+  if (d->abi_version != MK_ABI_VERSION) {
+    *msg = "abi_version mismatch";
+    return MK_E_INVAL;
+  }
+  if (d->n_layers < 1 || d->d_model < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->d_head < 1 || d->n_experts < 1 ||
+      d->top_k < 1 || d->d_ffn < 1 || d->vocab < 1 || d->max_batch < 1 || d->max_pages_per_seq < 1 || d->n_pages < 1) {
+    *msg = "non-positive dimension";
+    return MK_E_INVAL;
+  }
+  if (d->page_size != MK_PAGE_SIZE) {
+    *msg = "page_size must be 16";
+    return MK_E_UNSUPPORTED;
+  }
+  if (d->max_batch > MK_MAX_BATCH) {
+    *msg = "max_batch above 8";
+    return MK_E_UNSUPPORTED;
+  }
+  if (d->d_head != 64 && d->d_head != 128) {
+    *msg = "d_head must be 64 or 128";
+    return MK_E_UNSUPPORTED;
+  }
+  if (d->n_q_heads % d->n_kv_heads || !is_pow2_in(d->n_q_heads / d->n_kv_heads, 2, 8)) {
+    *msg = "n_q_heads / n_kv_heads must be 2, 4 or 8";
+    return MK_E_UNSUPPORTED;
+  }
+  if (d->d_model % 256 || d->d_model > 4096) {
+    *msg = "d_model must be a multiple of 256, at most 4096";
+    return MK_E_UNSUPPORTED;
+  }
+  if (d->d_ffn % 32 || d->d_ffn > 2048) {
+    *msg = "d_ffn must be a multiple of 32, at most 2048";
+    return MK_E_UNSUPPORTED;
+  }
+  if (d->n_q_heads * d->d_head > 8192) {
+    *msg = "n_q_heads * d_head above 8192";
+    return MK_E_UNSUPPORTED;
+  }
+  if (d->n_experts > 256 || d->top_k > 8 || d->top_k > d->n_experts) {
+    *msg = "n_experts <= 256 and top_k <= min(8, n_experts) required";
+    return MK_E_UNSUPPORTED;
+  }
+  if (d->vocab % 64) {
+    *msg = "vocab must be a multiple of 64";
+    return MK_E_UNSUPPORTED;
+  }
+  if (!(d->rms_eps >= 0.0f) || !(d->rope_base > 0.0f)) {
+    *msg = "bad rms_eps or rope_base";
+    return MK_E_INVAL;
+  }
+  return MK_OK;
+}
+
+Tiling choose_tiling(const mk_model_desc* d) {
+  Tiling t{};
+  t.rt = d->d_model >= 1024 ? 128 : 32;
+  t.n_rt = d->d_model / t.rt;
+  t.qkv_rows = 32;
+  t.n_qkv_per_group = (d->n_q_heads / d->n_kv_heads + 2) * d->d_head / t.qkv_rows;
+  t.router_rows = std::min(d->n_experts, 16);
+  t.n_router = (d->n_experts + t.router_rows - 1) / t.router_rows;
+  t.up_rows = 32;
+  t.n_up = d->d_ffn / t.up_rows;
+  t.lm_rows = 128;
+  t.n_lm = (d->vocab + t.lm_rows - 1) / t.lm_rows;
+  return t;
+}
+
+namespace {
+struct Emitter {
+  std::vector<int32_t>* out;
+  int32_t* add(int op, int layer) {
+    size_t o = out->size();
+    out->resize(o + DESC_WORDS, 0);
+    int32_t* w = out->data() + o;
+    w[W_OP] = op;
+    w[W_LAYER] = layer;
+    for (int i = 0; i < N_WAITS; ++i) {
+      w[W_WAIT0 + 2 * i] = -1;
+      w[W_WAIT0 + 2 * i + 1] = 0;
+    }
+    w[W_SIG] = -1;
+    w[W_ARR] = -1;
+    w[W_SEQ] = (int32_t)(o / DESC_WORDS);
+    return w;
+  }
+};
+void set_wait(int32_t* w, int i, int32_t c, int32_t target) {
+  w[W_WAIT0 + 2 * i] = c;
+  w[W_WAIT0 + 2 * i + 1] = target;
+}
+void set_sig(int32_t* w, int32_t c, int32_t n = 1) {
+  w[W_SIG] = c;
+  w[W_SIGN] = n;
+}
+}  // namespace
+
+int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::string* msg) {
+  int rc = validate_desc(d, msg);
+  if (rc) return rc;
+  if (!batch || !batch->seq_lens) {
+    *msg = "null batch";
+    return MK_E_INVAL;
+  }
+  const int B = batch->batch;
+  if (B < 1 || B > d->max_batch) {
+    *msg = "batch outside 1..max_batch";
+    return MK_E_INVAL;
+  }
+  P->B = B;
+  P->t = choose_tiling(d);
+  const Tiling& t = P->t;
+  const int L = d->n_layers, Hkv = d->n_kv_heads, E = d->n_experts;
+  P->n_slots = std::min(E, B * d->top_k);
+  P->cl.build(L, Hkv, B, P->n_slots, t.n_rt);
+  const CounterLayout& cl = P->cl;
+  P->splits.assign(B, 1);
+  for (int b = 0; b < B; ++b) {
+    const int32_t len = batch->seq_lens[b];
+    if (len < 0 || (int64_t)len / MK_PAGE_SIZE >= d->max_pages_per_seq) {
+      *msg = "sequence length negative or beyond max_pages_per_seq";
+      return MK_E_INVAL;
+    }
+    int64_t s = ((int64_t)len + 1 + ATTN_SPLIT_POS - 1) / ATTN_SPLIT_POS;
+    P->splits[b] = (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, ATTN_MAX_SPLITS));
+  }
+  P->desc.clear();
+  Emitter em{&P->desc};
+  const int grp = d->n_q_heads / Hkv;
+
+  for (int r = 0; r < t.n_rt; ++r) {
+    int32_t* w = em.add(OP_EMBED, 0);
+    w[W_A] = r;
+    w[W_R0] = r * t.rt;
+    w[W_R1] = (r + 1) * t.rt;
+    set_sig(w, cl.xready + 0);
+  }
+  for (int l = 0; l < L; ++l) {
+    for (int i = 0; i < t.n_router; ++i) {
+      int32_t* w = em.add(OP_ROUTER, l);
+      w[W_R0] = i * t.router_rows;
+      w[W_R1] = std::min(E, (i + 1) * t.router_rows);
+      set_wait(w, 0, cl.xready + l, t.n_rt);
+      set_sig(w, cl.router_done + l);
+    }
+    for (int g = 0; g < Hkv; ++g)
+      for (int i = 0; i < t.n_qkv_per_group; ++i) {
+        int32_t* w = em.add(OP_QKV, l);
+        w[W_A] = g;
+        w[W_R0] = i * t.qkv_rows;
+        w[W_R1] = (i + 1) * t.qkv_rows;
+        set_wait(w, 0, cl.xready + l, t.n_rt);
+        set_sig(w, cl.qkv_done + l * Hkv + g);
+      }
+    for (int g = 0; g < Hkv; ++g)
+      for (int b = 0; b < B; ++b)
+        for (int s = 0; s < P->splits[b]; ++s) {
+          int32_t* w = em.add(OP_ATTN, l);
+          w[W_A] = b;
+          w[W_B] = g;
+          w[W_C] = s;
+          w[W_D] = P->splits[b];
+          set_wait(w, 0, cl.qkv_done + l * Hkv + g, t.n_qkv_per_group);
+          set_sig(w, cl.attn_done + l * Hkv + g);  // issued only by the split that arrives last
+          w[W_ARR] = cl.attn_arrive + (l * B + b) * Hkv + g;
+          w[W_ARRN] = P->splits[b];
+        }
+    for (int s = 0; s < P->n_slots; ++s)
+      for (int i = 0; i < t.n_up; ++i) {
+        int32_t* w = em.add(OP_UP, l);
+        w[W_A] = s;
+        w[W_R0] = i * t.up_rows;
+        w[W_R1] = (i + 1) * t.up_rows;
+        set_wait(w, 0, cl.router_done + l, t.n_router);
+        set_sig(w, cl.up_done + l * P->n_slots + s);
+      }
+    for (int g = 0; g < Hkv; ++g)
+      for (int r = 0; r < t.n_rt; ++r) {
+        int32_t* w = em.add(OP_OPROJ, l);
+        w[W_A] = g;
+        w[W_R0] = r * t.rt;
+        w[W_R1] = (r + 1) * t.rt;
+        set_wait(w, 0, cl.attn_done + l * Hkv + g, B);
+        set_sig(w, cl.resid_in + l * t.n_rt + r);
+      }
+    for (int s = 0; s < P->n_slots; ++s)
+      for (int r = 0; r < t.n_rt; ++r) {
+        int32_t* w = em.add(OP_DOWN, l);
+        w[W_A] = s;
+        w[W_R0] = r * t.rt;
+        w[W_R1] = (r + 1) * t.rt;
+        set_wait(w, 0, cl.router_done + l, t.n_router);             // routing known: expert weights can stream
+        set_wait(w, 1, cl.up_done + l * P->n_slots + s, t.n_up);    // this expert's hidden state is complete
+        set_sig(w, cl.resid_in + l * t.n_rt + r);
+      }
+    for (int r = 0; r < t.n_rt; ++r) {
+      int32_t* w = em.add(OP_RESID, l);
+      w[W_A] = r;
+      w[W_R0] = r * t.rt;
+      w[W_R1] = (r + 1) * t.rt;
+      set_wait(w, 0, cl.resid_in + l * t.n_rt + r, Hkv + P->n_slots);
+      set_sig(w, cl.xready + l + 1);
+    }
+  }
+  for (int i = 0; i < t.n_lm; ++i) {
+    int32_t* w = em.add(OP_LMHEAD, L);
+    w[W_A] = i;
+    w[W_R0] = i * t.lm_rows;
+    w[W_R1] = std::min(d->vocab, (i + 1) * t.lm_rows);
+    set_wait(w, 0, cl.xready + L, t.n_rt);
+    w[W_ARR] = cl.lm_arrive;
+    w[W_ARRN] = t.n_lm;
+  }
+  (void)grp;
+  return MK_OK;
+}
+
+}  // namespace mk

@@ -1,0 +1,164 @@
+/* C ABI of the MI355X decode megakernel (gfx950).
+ *
+ * One call of mk_decode_step runs one autoregressive decode step of a
+ * parallel-transformer MoE decoder as ONE persistent HIP kernel: one workgroup
+ * per compute unit pulls per-tile tasks from a task list in global memory and
+ * producers and consumers synchronise through global atomic counters, not
+ * kernel boundaries.
+ *
+ * Passages this interface follows (page title, section):
+ *  - agenticcommons.xyz "Cohere North Mini Code megakernel serving engine",
+ *    section Megakernel 的運作方式: a single resident block per SM reads a task
+ *    list (one operation on one tile per task) from global memory; completed
+ *    tasks increment counters that consumers spin on.
+ *  - aimodeling.com "Cohere megakernel engine: one CUDA file, 1.58x vLLM on
+ *    H100", section "Caveats and takeaways": fixed-size task descriptors of 32
+ *    int32 words; batch size at most 8; BF16.  Section "From demo to a full
+ *    serving system": paged attention, ragged sequence lengths, continuous
+ *    batching.
+ *  - agenticcommons.xyz, section 對產品開發者的意義: one calling convention over
+ *    tiled GEMM and paged attention.
+ *
+ * Conventions.  Every call returns int: MK_OK (0) or a negative MK_E_* code;
+ * mk_last_error() gives the text of the calling thread's last error.  No C++
+ * exception crosses this boundary.  A handle serves one stream at a time and
+ * is not re-entrant.  All pointers named "device" are HIP device memory owned
+ * by the caller unless stated otherwise.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MK_ABI_VERSION 1
+#define MK_DESC_WORDS 32   /* int32 words per task descriptor (128 bytes) */
+#define MK_MAX_BATCH 8
+#define MK_PAGE_SIZE 16
+
+enum {
+  MK_OK = 0,
+  MK_E_INVAL = -1,       /* bad argument: null pointer, bad shape, out-of-range value */
+  MK_E_UNSUPPORTED = -2, /* shape outside the compiled kernel variants */
+  MK_E_NOMEM = -3,       /* device or pinned-host allocation failed */
+  MK_E_HIP = -4,         /* a HIP runtime call failed */
+  MK_E_STATE = -5,       /* call out of order (e.g. decode before a task list is built) */
+  MK_E_RANGE = -6,       /* output buffer too small; the needed size is still reported */
+  MK_E_DEVICE = -7       /* the kernel reported a fault (bad token/page, wait timeout) */
+};
+
+/* Model shape.  Supported: d_head in {64, 128}; n_q_heads / n_kv_heads in {2, 4, 8};
+ * d_model a multiple of 256, at most 4096; d_ffn a multiple of 32, at most 2048;
+ * n_experts <= 256, top_k <= 8 and <= n_experts; vocab a multiple of 64; page_size 16;
+ * 1 <= max_batch <= 8. */
+typedef struct mk_model_desc {
+  int32_t abi_version; /* MK_ABI_VERSION */
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, d_head, n_experts, top_k, d_ffn, vocab;
+  int32_t page_size;         /* tokens per KV page; must be 16 */
+  int32_t max_batch;         /* largest batch any step will use */
+  int32_t max_pages_per_seq; /* row length of page_tables */
+  int64_t n_pages;           /* pages per layer in the KV pool */
+  float rms_eps;             /* RMSNorm epsilon */
+  float rope_base;           /* RoPE base (rotate-half pairing (i, i + d_head/2)) */
+  const float* router_bias;  /* host [n_experts] added to router logits, or NULL; copied */
+} mk_model_desc;
+
+/* Weights: device pointers to BF16, row-major [out][in].  Per-layer entries are host arrays of
+ * n_layers device pointers.  Read-only; they must stay valid until mk_free_model. */
+typedef struct mk_weights {
+  const void* embed;            /* [vocab][d_model] */
+  const void* lm_head;          /* [vocab][d_model] (untied) */
+  const void* final_norm;       /* [d_model] */
+  const void* const* attn_norm; /* [L] -> [d_model] (the layer's RMSNorm gain) */
+  const void* const* wq;        /* [L] -> [n_q_heads*d_head][d_model] */
+  const void* const* wk;        /* [L] -> [n_kv_heads*d_head][d_model] */
+  const void* const* wv;        /* [L] -> [n_kv_heads*d_head][d_model] */
+  const void* const* wo;        /* [L] -> [d_model][n_q_heads*d_head] */
+  const void* const* w_router;  /* [L] -> [n_experts][d_model] */
+  const void* const* w_gate;    /* [L] -> [n_experts][d_ffn][d_model] */
+  const void* const* w_up;      /* [L] -> [n_experts][d_ffn][d_model] */
+  const void* const* w_down;    /* [L] -> [n_experts][d_model][d_ffn] */
+} mk_weights;
+
+/* A step's batch as seen by the task builder. */
+typedef struct mk_batch {
+  int32_t batch;            /* 1..max_batch */
+  const int32_t* seq_lens;  /* host [batch]: prior positions of each sequence (its new token's position) */
+} mk_batch;
+
+typedef struct mk_model mk_model;
+
+/* Create a handle: validates the shape, records the weight pointers, allocates the handle's own
+ * device scratch (counters, fp32 activations, partials, routing and debug buffers) and sizes the
+ * grid to one workgroup per compute unit of the current device.
+ * Errors: MK_E_INVAL, MK_E_UNSUPPORTED, MK_E_NOMEM, MK_E_HIP. */
+int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out);
+
+/* Build the step's task list on the host (deterministic, no device work): fixed-size descriptors of
+ * MK_DESC_WORDS int32 in topological order (every wait refers to an earlier task).  The list is kept
+ * in the handle and uploaded by the next mk_decode_step.  Attention split counts follow the host
+ * lengths; split bounds are recomputed on the device from the step's seq_lens, so a list stays valid
+ * while lengths grow.  tasks_out (nullable, host) receives a copy when cap >= the task count;
+ * *n_tasks always receives the count.
+ * Errors: MK_E_INVAL (batch outside 1..max_batch, negative length, null batch), MK_E_RANGE (cap too small). */
+int mk_build_tasks(mk_model* m, const mk_batch* batch, int32_t* tasks_out, int64_t cap, int64_t* n_tasks);
+
+/* Enqueue one decode step on `stream` (a hipStream_t; NULL = default stream); asynchronous.
+ *  tokens      device int32 [B]                      input token of each sequence
+ *  seq_lens    device int32 [B]                      prior positions (= position of the new token); not modified
+ *  page_tables device int32 [B][max_pages_per_seq]   logical page -> physical page; page_tables[b][seq_lens[b]/16] must be valid
+ *  kv_pages    device BF16  [n_layers][n_pages][2 (K,V)][n_kv_heads][16][d_head]; positions [0, seq_lens[b]) are read and
+ *              position seq_lens[b] is written (post-RoPE K and V) in every layer
+ *  logits_out  device fp32  [B][vocab]
+ * B is the batch of the last mk_build_tasks.  The greedy next tokens go to the buffer of mk_next_tokens.
+ * Errors before launch: MK_E_STATE (no task list), MK_E_INVAL (null pointer), MK_E_HIP.  Faults found by the
+ * kernel (token or page out of range, a dependency wait that timed out) are reported by mk_status. */
+int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* page_tables, void* kv_pages,
+                   float* logits_out, void* stream);
+
+/* Device buffer int32 [max_batch] holding the last step's greedy tokens (argmax, lowest index on ties);
+ * it may be passed straight back as the next step's `tokens`.  Owned by the handle. */
+int mk_next_tokens(mk_model* m, int32_t** dev_ptr);
+
+/* Synchronise `stream`, then return MK_OK or MK_E_DEVICE if the kernel raised a fault since the last
+ * call (the fault word is cleared and the handle's counters are reset). */
+int mk_status(mk_model* m, void* stream);
+
+/* Debug switches (bit flags, MK_DBG_*) and read-back of the handle's debug buffers. */
+enum { MK_DBG_DUMP_N = 1 };
+enum {
+  MK_DBGK_ROUTE_SEL = 1,     /* int32 [n_layers][batch][top_k]: last step's expert selection (always recorded) */
+  MK_DBGK_ROUTE_GATE = 2,    /* fp32  [n_layers][batch][top_k]: its gates (always recorded) */
+  MK_DBGK_ROUTER_LOGITS = 3, /* fp32  [n_layers][batch][n_experts] (always recorded) */
+  MK_DBGK_NORM_IN = 4,       /* fp32  [n_layers][batch][d_model]: each layer's RMSNorm output (MK_DBG_DUMP_N) */
+  MK_DBGK_COUNTERS = 5,      /* uint32 [n_counters] as left by the last step (all zero after a clean step) */
+  MK_DBGK_TASK_DONE = 6      /* uint32 [n_tasks]: completions per task in the last step (must be 1 each) */
+};
+int mk_debug_set(mk_model* m, uint32_t flags);
+/* Copies `bytes` of debug buffer `kind` to host memory; synchronises the device first.
+ * Errors: MK_E_INVAL (unknown kind), MK_E_STATE (kind not enabled), MK_E_RANGE (bytes larger than the buffer). */
+int mk_debug_read(mk_model* m, int kind, void* host_dst, int64_t bytes);
+
+/* Override the grid: n_workgroups persistent workgroups (0 = one per compute unit).  Results do not
+ * depend on it (every reduction has a fixed order); it exists for testing and tuning. */
+int mk_set_grid(mk_model* m, int32_t n_workgroups);
+
+/* Release the handle and its device memory (after the stream's work has finished). */
+int mk_free_model(mk_model* m);
+
+/* Text of the calling thread's last error ("" if none). */
+const char* mk_last_error(void);
+
+/* Pure host planning, for tools and tests (no device needed): the task list mk_build_tasks would emit
+ * for `desc` on a grid of n_workgroups.  n_counters (nullable) receives the counter count. */
+int mk_plan_tasks(const mk_model_desc* desc, const mk_batch* batch, int32_t* tasks_out, int64_t cap, int64_t* n_tasks,
+                  int32_t* n_counters);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -3,7 +3,7 @@
 // without a host round trip.  No arithmetic of the decode method lives here.
 #include <hip/hip_runtime.h>
 
-#define SYNTH_FN __device__ static inline
+#define SYNTH_FN __host__ __device__ static inline
 #include "synth_core.h"
 #include "../include/synth.h"
 

@@ -1,0 +1,108 @@
+"""Drives the CPU oracle over the same synthetic workload the GPU runs, teacher-forced with the GPU's tokens.
+
+Routing near-ties: where the oracle's own top-k differs from the GPU's and the oracle's gap between
+its k-th and (k+1)-th logit is below DELTA_ROUTE, both selections are correct; the oracle then adopts
+the GPU's selection for that (layer, token) and counts it ("follow mode").  Anywhere else a routing
+difference is a failure.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import oracle as O
+from synth import workloads as W
+
+DELTA_ROUTE = 1e-3
+
+
+def dims(shape):
+    return O.Dims(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.d_head, shape.n_experts, shape.top_k,
+                  shape.d_ffn, shape.vocab, 16, shape.rms_eps, shape.rope_base)
+
+
+def kth_gap(logits, k):
+    s = np.sort(logits.astype(np.float64))[::-1]
+    return s[k - 1] - s[k] if k < len(s) else np.inf
+
+
+class OracleRun:
+    """Oracle state (KV cache, per-layer weights) for a workload.  For small models every weight is kept
+    in memory; for large ones `layer_source(l)` generates a layer's dense weights on demand and experts
+    are generated when selected."""
+
+    def __init__(self, w: W.Workload, pt, n_pages, keep_all=None):
+        self.w = w
+        s = self.shape = w.shape
+        self.D = dims(s)
+        self.pt = pt
+        self.n_pages = n_pages
+        self.kv = W.host_kv(w, pt, n_pages)
+        small = s.n_layers * (s.layer_attn_bytes() + s.n_experts * s.expert_bytes()) < 2e9
+        self.keep_all = small if keep_all is None else keep_all
+        self.final_norm = np.full(s.d_model, W.ONE_BF16, np.uint16)
+        self.lm_head = W.host_lm_head(s)
+        self._layers = {}
+        self._experts = {}
+        self.bias = w.router_bias
+        self.near_ties = 0
+        self.route_checked = 0
+
+    def layer_weights(self, l, experts):
+        s = self.shape
+        if l not in self._layers:
+            hl = W.host_layer(s, l)
+            if not self.keep_all:
+                self._layers.clear()
+                self._experts.clear()
+            self._layers[l] = hl
+        hl = self._layers[l]
+        ex = {}
+        for e in experts:
+            key = (l, int(e))
+            if key not in self._experts:
+                self._experts[key] = W.host_expert(s, l, int(e))
+            ex[int(e)] = self._experts[key]
+        return O.LayerWeights(hl["attn_norm"], hl["wq"], hl["wk"], hl["wv"], hl["wo"], hl["w_router"], ex, s.n_experts, self.bias)
+
+    def step(self, tokens, pos, gpu_sel=None):
+        """One oracle decode step for tokens at positions pos (prior lengths).  gpu_sel: [L][B][k] GPU selections
+        (for the near-tie rule).  Returns logits [B][V], next [B], sel [L][B][k], n [L][B][d]."""
+        s = self.shape
+        B = len(tokens)
+        x = O.embed(self.D, W.host_embed_rows(s, tokens), np.arange(B, dtype=np.int32))
+        sels, ns = [], []
+        for l in range(s.n_layers):
+            # own routing first (on this layer's normalised input)
+            hl = self.layer_weights(l, [])
+            n = np.stack([O.rmsnorm(x[b], hl.arrs[0]) for b in range(B)])
+            force = np.full((B, s.top_k), -1, np.int32)
+            need = set()
+            for b in range(B):
+                sel, _, lg = O.router(n[b], hl.arrs[5], s.top_k, self.bias)
+                self.route_checked += 1
+                if gpu_sel is not None and not np.array_equal(np.asarray(gpu_sel[l][b]), sel):
+                    if kth_gap(lg, s.top_k) < DELTA_ROUTE:
+                        force[b] = gpu_sel[l][b]
+                        self.near_ties += 1
+                        need.update(int(e) for e in gpu_sel[l][b])
+                        continue
+                    raise AssertionError(f"routing differs at layer {l} token {b}: gpu {list(gpu_sel[l][b])} oracle {list(sel)} "
+                                         f"(k-th gap {kth_gap(lg, s.top_k):.3g})")
+                need.update(int(e) for e in sel)
+            Wl = self.layer_weights(l, sorted(need))
+            x, aux = O.layer(self.D, Wl, pos, self.pt, self.kv[l], x, sel_force=force if (force >= 0).any() else None)
+            sels.append(aux["sel"])
+            ns.append(aux["n"])
+        logits, nxt = O.head(self.D, x, self.final_norm, self.lm_head)
+        return logits, nxt, np.stack(sels), np.stack(ns)
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def top2_gap(logits):
+    s = np.sort(np.asarray(logits, np.float64))[-2:]
+    return s[1] - s[0]

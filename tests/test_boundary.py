@@ -1,0 +1,162 @@
+"""Host-side checks of the C-ABI library: it loads, exports every declared entry point, validates shapes,
+and its task lists are deadlock-free topological orders (CPU simulation of the counter protocol)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from decode_megakernel_wg_amd import mk
+from synth import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# descriptor words (mirrors the library's layout)
+W_OP, W_LAYER, W_A, W_B, W_C, W_D, W_R0, W_R1, W_WAIT0, W_SIG, W_SIGN, W_ARR, W_ARRN = 0, 1, 2, 3, 4, 5, 6, 7, 8, 16, 17, 18, 19
+OP_ATTN, OP_LMHEAD = 4, 9
+
+
+def declared(header):
+    txt = open(os.path.join(ROOT, "include", header)).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:mk|synth)_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_libraries_load_and_export_every_declared_symbol():
+    L = mk.lib()
+    for name in declared("mk.h"):
+        assert hasattr(L, name), name
+    assert set(declared("mk.h")) == set(mk.EXPORTS)
+    from synth import synth
+
+    H = synth.host()
+    D = C.CDLL(synth.DEV_LIB)
+    for name in declared("synth.h"):
+        assert hasattr(D if name.startswith("synth_dev_") else H, name), name
+
+
+def desc_for(shape, B=1, pages=64, n_pages=1024, **over):
+    d = mk.make_desc(shape, B, pages, n_pages)
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("field,value,code", [("d_head", 96, mk.MK_E_UNSUPPORTED), ("page_size", 32, mk.MK_E_UNSUPPORTED),
+                                              ("max_batch", 9, mk.MK_E_UNSUPPORTED), ("n_q_heads", 6, mk.MK_E_UNSUPPORTED),
+                                              ("abi_version", 99, mk.MK_E_INVAL), ("n_layers", 0, mk.MK_E_INVAL),
+                                              ("top_k", 9, mk.MK_E_UNSUPPORTED)])
+def test_shape_validation(field, value, code):
+    d = desc_for(W.TINY, **{field: value})
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan_tasks(d, [10])
+    assert e.value.code == code
+
+
+def test_batch_validation():
+    d = desc_for(W.TINY, B=2, pages=4)
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan_tasks(d, [1, 2, 3])
+    assert e.value.code == mk.MK_E_INVAL
+    with pytest.raises(mk.MkError):
+        mk.mk_plan_tasks(d, [10, 64])   # 64 // 16 = 4 pages: beyond max_pages_per_seq
+    with pytest.raises(mk.MkError):
+        mk.mk_plan_tasks(d, [-1])
+
+
+def simulate(tasks, n_counters, n_workers, rng):
+    """Tasks are claimed in list order by n_workers workers, each holding its current task and one pre-claimed
+    next task; among held tasks any whose waits are met may finish, in random order.  Returns final counters
+    and completion counts; raises on deadlock."""
+    ctr = np.zeros(n_counters, np.int64)
+    done = np.zeros(len(tasks), np.int64)
+    nxt = 0
+    held = []
+    completed = 0
+
+    def ready(t):
+        w = tasks[t]
+        for i in range(4):
+            c, tgt = w[W_WAIT0 + 2 * i], w[W_WAIT0 + 2 * i + 1]
+            if c >= 0 and ctr[c] < tgt:
+                return False
+        return True
+
+    while completed < len(tasks):
+        while len(held) < 2 * n_workers and nxt < len(tasks):
+            held.append(nxt)
+            nxt += 1
+        # a worker may only run its current (older) task; model each worker's queue order
+        runnable = [t for i, t in enumerate(sorted(held)) if ready(t)]
+        # deadlock freedom: the oldest held task must always be runnable
+        oldest = min(held)
+        assert ready(oldest), f"deadlock: oldest claimed task {oldest} waits on an unfinished producer"
+        t = runnable[rng.integers(len(runnable))]
+        held.remove(t)
+        w = tasks[t]
+        done[t] += 1
+        completed += 1
+        if w[W_ARR] >= 0:
+            ctr[w[W_ARR]] += 1
+            if ctr[w[W_ARR]] == w[W_ARRN] and w[W_SIG] >= 0:
+                ctr[w[W_SIG]] += w[W_SIGN]
+        elif w[W_SIG] >= 0:
+            ctr[w[W_SIG]] += w[W_SIGN]
+    return ctr, done
+
+
+@pytest.mark.parametrize("name,B_lens", [("tiny", [128]), ("tiny", [5, 300, 17, 0]), ("full", [8192]),
+                                         ("full", [1024, 30000, 4000, 70000, 2000, 9000, 1500, 12000])])
+def test_task_list_is_a_deadlock_free_topological_order(name, B_lens):
+    shape = W.TINY if name == "tiny" else W.FULL
+    maxp = max(B_lens) // 16 + 2
+    d = desc_for(shape, B=len(B_lens), pages=maxp, n_pages=maxp * len(B_lens))
+    tasks, n_ctr = mk.mk_plan_tasks(d, B_lens)
+    assert tasks.shape[1] == mk.MK_DESC_WORDS
+    assert np.array_equal(tasks[:, 31], np.arange(len(tasks)))
+    # every wait is reachable from earlier tasks only
+    signalled = {}
+    for t, w in enumerate(tasks):
+        for i in range(4):
+            c, tgt = w[W_WAIT0 + 2 * i], w[W_WAIT0 + 2 * i + 1]
+            if c >= 0:
+                assert signalled.get(c, 0) >= tgt, f"task {t} waits on counter {c} beyond earlier signals"
+        if w[W_SIG] >= 0:
+            inc = w[W_SIGN] if w[W_ARR] < 0 else (w[W_SIGN] if 1 else 0)
+            if w[W_ARR] < 0:
+                signalled[w[W_SIG]] = signalled.get(w[W_SIG], 0) + inc
+            else:  # one signal per arrival group, from whichever member arrives last
+                key = ("arr", w[W_ARR])
+                signalled[key] = signalled.get(key, 0) + 1
+                if signalled[key] == w[W_ARRN]:
+                    signalled[w[W_SIG]] = signalled.get(w[W_SIG], 0) + w[W_SIGN]
+    rng = np.random.default_rng(0)
+    for workers in (1, 3, 256):
+        if name == "full" and workers != 256 and len(B_lens) > 1:
+            continue
+        ctr, done = simulate(tasks, n_ctr, workers, rng)
+        assert np.all(done == 1)
+        for w in tasks:
+            for i in range(4):
+                c, tgt = w[W_WAIT0 + 2 * i], w[W_WAIT0 + 2 * i + 1]
+                if c >= 0:
+                    assert ctr[c] == tgt or ctr[c] >= tgt
+
+
+def test_dropped_producer_is_detected_by_the_simulator():
+    d = desc_for(W.TINY, B=1, pages=16)
+    tasks, n_ctr = mk.mk_plan_tasks(d, [100])
+    t = tasks.copy()
+    first_resid = int(np.nonzero(t[:, W_OP] == 8)[0][0])
+    t[first_resid, W_SIG] = -1      # a residual tile that never signals
+    with pytest.raises(AssertionError, match="deadlock"):
+        simulate(t, n_ctr, 4, np.random.default_rng(1))
+
+
+def test_task_counts_full_model():
+    d = desc_for(W.FULL, B=1, pages=600, n_pages=600)
+    tasks, _ = mk.mk_plan_tasks(d, [8192])
+    ops = np.bincount(tasks[:, W_OP], minlength=10)
+    assert ops[OP_LMHEAD] == 262144 // 128
+    assert ops[OP_ATTN] == 48 * 4 * 17
