@@ -1,0 +1,184 @@
+"""Decode throughput of the persistent megakernel on one MI355X, and its fraction of HBM speed-of-light.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload b1_8k] [--no-cpu-baseline]
+
+A step is one decode step (one launch of the persistent kernel over the whole model) for the
+workload's batch; inputs (weights, KV cache, page tables, lengths) are resident in HBM before the
+timed region and every step feeds the previous step's greedy tokens back on the device.  Prints one
+JSON line.  Speed-of-light bytes per step are the active weights (distinct experts counted once per
+layer, from the kernel's own routing record) plus the K/V read over every attended position, at 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD_TEXT = {
+    "b1_8k": "48-layer parallel-transformer MoE decoder (d_model 2048, 32 q heads / 4 KV heads x 128, 128 SwiGLU experts "
+             "top-8, d_ffn 768, vocab 262144, BF16 weights), batch 1, 8192 prior KV positions in 16-token pages, greedy decode",
+    "b8_ragged_uniform": "same 48-layer model, batch 8, contexts log-uniform in [1024, 32768], shuffled pages, uniform routing",
+    "b8_ragged_skewed": "same 48-layer model, batch 8, contexts log-uniform in [1024, 32768], shuffled pages, "
+                        "router bias -1.5 ln(rank) (skewed routing)",
+    "long_64k": "same 48-layer model, batch 1, 65536 prior positions, split-KV attention",
+    "long_128k": "same 48-layer model, batch 1, 131072 prior positions, split-KV attention",
+    "long_256k": "same 48-layer model, batch 1, 262144 prior positions, split-KV attention",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def unique_experts_per_layer(sess):
+    import numpy as np
+
+    from decode_megakernel_wg_amd import mk
+
+    s = sess.shape
+    sel = sess.h.mk_debug_read(mk.MK_DBGK_ROUTE_SEL, (s.n_layers, sess.B, s.top_k), np.int32)
+    return [len(np.unique(sel[l])) for l in range(s.n_layers)]
+
+
+def run_gpu(workload, steps, warmup, model=None):
+    import numpy as np
+    import torch
+
+    from decode_megakernel_wg_amd import roofline as R
+    from decode_megakernel_wg_amd.session import Session
+    from synth import workloads as W
+
+    w = W.make(workload, steps=steps + warmup)
+    t0 = time.time()
+    if model is None or model.shape != w.shape:
+        log(f"generating {w.shape.n_layers}-layer synthetic weights in HBM")
+        model = W.DeviceModel(w.shape)
+    log(f"generating KV prefixes {w.ctx}")
+    sess = Session(w, model=model)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f} s; warmup {warmup} steps")
+    for _ in range(warmup):
+        sess.step()
+    sess.status()
+    # bytes per timed step: weights with the distinct experts actually used + KV read at each step's lengths
+    sess.rewind(0)
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    uniq = []
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(steps):
+        sess.step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    sess.status()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    total_ms = evs[0].elapsed_time(evs[-1])
+    # routing of the last step (the kernel records it every step); distinct tokens of the step
+    uniq = unique_experts_per_layer(sess)
+    n_tok = len(set(int(t) for t in sess.next_tokens())) if sess.B > 1 else 1
+    bytes_steps = [R.step_bytes(w.shape, sess.seq_rows_host[i], uniq, n_tok) for i in range(steps)]
+    avg_bytes = sum(bytes_steps) / steps
+    ms_per_step = total_ms / steps
+    return dict(w=w, sess=sess, model=model, ms_per_step=ms_per_step, per_step_ms=per, avg_bytes=avg_bytes, uniq=uniq,
+                tok_s=steps * w.B / (total_ms * 1e-3), kernel_ms=sum(per) / steps)
+
+
+def cpu_baseline(workload):
+    """The CPU oracle, timed on one decode step of the same workload (all layers and the LM head), with each
+    layer's synthetic weights generated before its timed call."""
+    import numpy as np
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import oracle as O
+    from oracle_runner import OracleRun
+    from synth import workloads as W
+
+    w = W.make(workload, steps=1)
+    pt, n_pages = W.page_tables(w)
+    t0 = time.time()
+    orc = OracleRun(w, pt, n_pages, keep_all=False)
+    log(f"oracle setup (KV + LM head generation) {time.time() - t0:.1f} s")
+    s = w.shape
+    x = O.embed(orc.D, W.host_embed_rows(s, w.tokens), np.arange(w.B, dtype=np.int32))
+    timed = 0.0
+    for l in range(s.n_layers):
+        hl = orc.layer_weights(l, [])
+        n = np.stack([O.rmsnorm(x[b], hl.arrs[0]) for b in range(w.B)])
+        need = set()
+        for b in range(w.B):
+            sel, _, _ = O.router(n[b], hl.arrs[5], s.top_k, w.router_bias)
+            need.update(int(e) for e in sel)
+        Wl = orc.layer_weights(l, sorted(need))
+        t1 = time.perf_counter()
+        x, _ = O.layer(orc.D, Wl, np.array(w.ctx, np.int64), pt, orc.kv[l], x)
+        timed += time.perf_counter() - t1
+        if l % 12 == 11:
+            log(f"oracle layer {l + 1}/{s.n_layers}, timed {timed:.2f} s")
+    t1 = time.perf_counter()
+    O.head(orc.D, x, orc.final_norm, orc.lm_head)
+    timed += time.perf_counter() - t1
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(w.B / timed, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"one decode step of {workload} (all {s.n_layers} layers + LM head, batch {w.B}); fp64-accumulating C oracle; "
+                      f"{timed:.2f} s of timed CPU work; weight generation excluded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="b1_8k", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from decode_megakernel_wg_amd import roofline as R
+
+    r = run_gpu(args.workload, args.steps, args.warmup)
+    w = r["w"]
+    achieved = r["avg_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+    sol_tok_s = R.sol_tokens_per_s(r["avg_bytes"], w.B)
+    line = {
+        "metric": "decode tok/s + % HBM speed-of-light, batch 1 @8K ctx and batch 8 ragged",
+        "value": round(r["tok_s"], 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}", "global_batch": w.B,
+                   "seq_len": int(max(w.ctx)), "parallelism": "single GPU, persistent megakernel"},
+        "sol_tok_s": round(sol_tok_s, 1),
+        "pct_of_sol": round(100 * r["tok_s"] / sol_tok_s, 2),
+        "sol_bytes_per_step": int(r["avg_bytes"]),
+        "unique_experts_per_layer": int(round(sum(r["uniq"]) / len(r["uniq"]))),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(achieved / 8000.0, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        del r
+        torch.cuda.empty_cache()
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

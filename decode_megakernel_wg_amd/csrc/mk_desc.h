@@ -10,7 +10,7 @@ namespace mk {
 
 enum Op : int32_t {
   OP_EMBED = 1,   // x[b][rows] = embed[token_b][rows]; partial sum of squares            -> XREADY[0]
-  OP_ROUTER = 2,  // router logits for experts [r0, r1) (fp64 accumulation)             -> ROUTER_DONE[l]
+  OP_ROUTER = 2,  // router logits for experts [r0, r1) (fp64 accumulation); the last tile routes -> ROUTER_DONE[l]
   OP_QKV = 3,     // rows [r0, r1) of KV group g's fused [q heads; k; v] projection     -> QKV_DONE[l][g]
   OP_ATTN = 4,    // split s of (sequence b, KV group g): partial softmax(qK^T)V; last arriver combines -> ATTN_DONE[l][g]
   OP_UP = 5,      // gate+up rows [r0, r1) of expert slot s, SwiGLU                      -> UP_DONE[l][s]
@@ -42,12 +42,14 @@ constexpr int N_WAITS = 4;
 constexpr int DESC_WORDS = 32;
 
 // Tile sizes chosen by the planner (rows per task); the kernel reads r0/r1 from the descriptor.
-constexpr int ATTN_SPLIT_POS = 512;  // positions per attention split (before clamping)
+constexpr int ATTN_SPLIT_POS = 256;  // positions per attention split (before clamping)
+constexpr int ATTN_MAX_SPLIT_PAGES = 256;  // pages one split may cover (its page list is staged in LDS)
 constexpr int ATTN_MAX_SPLITS = 256;
+constexpr int SLOT_WORDS = 32;  // routing table entry per expert slot: expert, token count, (token, rank, gate) x 8
 
 // Counter index layout for a model/batch; computed identically by planner and host launcher.
 struct CounterLayout {
-  int32_t ticket, done, xready, qkv_done, router_done, attn_arrive, attn_done, up_done, resid_in, lm_arrive, total;
+  int32_t ticket, done, xready, qkv_done, router_arrive, router_done, attn_arrive, attn_done, up_done, resid_in, lm_arrive, total;
   int32_t n_layers, n_kv, n_slots, n_row_tiles, batch;
   void build(int L, int Hkv, int B, int slots, int nrt) {
     n_layers = L;
@@ -60,6 +62,7 @@ struct CounterLayout {
     done = o; o += 32;
     xready = o; o += L + 1;
     qkv_done = o; o += L * Hkv;
+    router_arrive = o; o += L;
     router_done = o; o += L;
     attn_arrive = o; o += L * B * Hkv;
     attn_done = o; o += L * Hkv;

@@ -13,7 +13,8 @@
 #include "mk_kargs.h"
 #include "mk_plan.h"
 
-extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int grid, hipStream_t stream);
+extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int kclass, int grid, hipStream_t stream);
+extern "C" int mk_kernel_class(int d_head, int group, int d_model, int d_ffn);
 
 namespace {
 
@@ -43,6 +44,7 @@ struct mk_model {
   int device = 0;
   int n_cu = 0;
   int grid = 0;
+  int kclass = 0;
   uint32_t dbg = 0;
   mk::Tiling tiling{};
   int max_slots = 0;
@@ -59,8 +61,9 @@ struct mk_model {
   uint32_t* err = nullptr;
   float *x = nullptr, *ssq = nullptr, *rope_cs = nullptr, *qkv = nullptr, *apart = nullptr, *attn_o = nullptr, *opart = nullptr;
   float *rlogits = nullptr, *route_gate = nullptr, *h = nullptr, *ypart = nullptr, *lmbest_v = nullptr, *dump_n = nullptr;
-  int32_t *route_sel = nullptr, *lmbest_i = nullptr, *next_tok = nullptr;
+  int32_t *route_sel = nullptr, *lmbest_i = nullptr, *next_tok = nullptr, *slots = nullptr;
   uint32_t *task_done = nullptr, *ctr_snapshot = nullptr;
+  uint64_t* ts = nullptr;
   // task list
   mk::Plan plan;
   bool have_plan = false, dirty = false;
@@ -124,7 +127,12 @@ int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out
         !w->w_down[l])
       return fail(MK_E_INVAL, "null per-layer weight pointer at layer " + std::to_string(l));
 
+  const int kclass = mk_kernel_class(desc->d_head, desc->n_q_heads / desc->n_kv_heads, desc->d_model, desc->d_ffn);
+  if (!kclass)
+    return fail(MK_E_UNSUPPORTED, "no compiled kernel for this shape (d_head 128 with group 8, d_model <= 2048, d_ffn <= 1024; or "
+                                  "d_head 64 with group 2, d_model <= 512, d_ffn <= 512)");
   mk_model* m = new mk_model();
+  m->kclass = kclass;
   m->desc = *desc;
   m->desc.router_bias = nullptr;
   HIPCHK(hipGetDevice(&m->device));
@@ -167,7 +175,8 @@ int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out
       (rc = m->alloc(&m->route_gate, (size_t)L * maxB * k)) || (rc = m->alloc(&m->h, (size_t)m->max_slots * maxB * F)) ||
       (rc = m->alloc(&m->ypart, (size_t)maxB * k * d)) || (rc = m->alloc(&m->lmbest_v, (size_t)maxB * t.n_lm)) ||
       (rc = m->alloc(&m->lmbest_i, (size_t)maxB * t.n_lm)) || (rc = m->alloc(&m->next_tok, maxB)) ||
-      (rc = m->alloc(&m->ctr_snapshot, m->max_counters)))
+      (rc = m->alloc(&m->ctr_snapshot, m->max_counters)) ||
+      (rc = m->alloc(&m->slots, (size_t)L * m->max_slots * mk::SLOT_WORDS)))
     return cleanup(rc);
   if (hipHostMalloc((void**)&m->staging, (size_t)m->max_tasks * mk::DESC_WORDS * sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
     m->staging = nullptr;
@@ -217,6 +226,7 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
     m->dirty = false;
   }
   if (m->task_done) HIPCHK(hipMemsetAsync(m->task_done, 0, sizeof(uint32_t) * P.n_tasks(), s));
+  if (m->ts && (m->dbg & MK_DBG_TIMESTAMPS)) HIPCHK(hipMemsetAsync(m->ts, 0, sizeof(uint64_t) * 8 * P.n_tasks(), s));
   const mk_model_desc& D = m->desc;
   mk::KArgs a{};
   a.L = D.n_layers;
@@ -262,6 +272,7 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   a.opart = m->opart;
   a.rlogits = m->rlogits;
   a.route_sel = m->route_sel;
+  a.slots = m->slots;
   a.route_gate = m->route_gate;
   a.h = m->h;
   a.ypart = m->ypart;
@@ -270,8 +281,9 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   a.next_tok = m->next_tok;
   a.dump_n = (m->dbg & MK_DBG_DUMP_N) ? m->dump_n : nullptr;
   a.task_done = m->task_done;
+  a.ts = (m->dbg & MK_DBG_TIMESTAMPS) ? m->ts : nullptr;
   a.ctr_snapshot = m->ctr_snapshot;
-  HIPCHK(mk_launch_persistent(&a, m->grid, s));
+  HIPCHK(mk_launch_persistent(&a, m->kclass, m->grid, s));
   m->stepped = true;
   return MK_OK;
 }
@@ -307,6 +319,10 @@ int mk_debug_set(mk_model* m, uint32_t flags) {
     int rc = m->alloc(&m->task_done, (size_t)m->max_tasks);
     if (rc) return rc;
   }
+  if ((flags & MK_DBG_TIMESTAMPS) && !m->ts) {
+    int rc = m->alloc(&m->ts, (size_t)m->max_tasks * 8);
+    if (rc) return rc;
+  }
   m->dbg = flags;
   return MK_OK;
 }
@@ -333,6 +349,11 @@ int mk_debug_read(mk_model* m, int kind, void* host_dst, int64_t bytes) {
       if (!m->task_done) return fail(MK_E_STATE, "mk_debug_set has not been called");
       src = m->task_done;
       avail = m->plan.n_tasks() * 4;
+      break;
+    case MK_DBGK_TIMESTAMPS:
+      if (!(m->dbg & MK_DBG_TIMESTAMPS)) return fail(MK_E_STATE, "MK_DBG_TIMESTAMPS is not enabled");
+      src = m->ts;
+      avail = m->plan.n_tasks() * 64;
       break;
     default: return fail(MK_E_INVAL, "unknown debug kind");
   }

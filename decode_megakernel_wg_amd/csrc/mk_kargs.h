@@ -54,6 +54,7 @@ struct KArgs {
   float* opart;      // [Hkv][B][d] O-projection partial per KV group
   float* rlogits;    // [L][B][E] router logits
   int32_t* route_sel;
+  int32_t* slots;    // [L][n_slots][SLOT_WORDS] routing table: expert, token count, (token, rank, gate bits) x 8
   float* route_gate; // [L][B][k]
   float* h;          // [n_slots][B][F] SwiGLU hidden state per expert slot and token of the slot
   float* ypart;      // [B][k][d] gated expert outputs
@@ -62,6 +63,7 @@ struct KArgs {
   int32_t* next_tok; // [max_batch]
   float* dump_n;     // [L][B][d] or null
   uint32_t* task_done;     // [n_tasks] or null
+  uint64_t* ts;            // [n_tasks][8] (claim, dependencies met, end, hardware id, 4 sub-phase marks) or null
   uint32_t* ctr_snapshot;  // [n_counters] or null
 };
 

@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mk_desc.h"
 #include "mk_kargs.h"
 
@@ -32,14 +34,30 @@ constexpr uint32_t SPIN_LIMIT = 1u << 21;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 template <int N, int R>
 struct NVR {
   static constexpr int nv = N, rpw = R;
 };
+// Rows per wave per GEMV pass for NV 16-byte vectors per row and lane (passes hold 4-8 vectors per lane).
+template <int NV>
+struct RpwOf {
+  static constexpr int value = NV == 1 ? 4 : NV == 2 ? 4 : NV == 4 ? 2 : 1;
+};
+// A compiled shape class of the kernel: head dim, GQA group, and the 16-byte-vector counts per lane of
+// the three GEMV reduction lengths (d_model, d_ffn, group * d_head).  One kernel is instantiated per
+// class so that each task type has a single code path (the register allocator handles one variant per
+// task far better than a switch over many).
+template <int DH_, int GRP_, int NVD_, int NVF_, int NVO_>
+struct Cfg {
+  static constexpr int DH = DH_, GRP = GRP_, NVD = NVD_, NVF = NVF_, NVO = NVO_;
+};
 // Global-address-space views: loads through them are global_load (vmcnt only), never flat loads,
 // which would also count against lgkmcnt and make every LDS wait wait for in-flight weight loads.
 typedef const __attribute__((address_space(1))) u4 gu4;
+typedef const __attribute__((address_space(1))) u2 gu2;
 __device__ __forceinline__ gu4* as_global(const void* p) { return (gu4*)(p); }
+__device__ __forceinline__ gu2* as_global2(const void* p) { return (gu2*)(p); }
 
 // The kernel's argument block, read in place from the kernarg segment (constant address space) so
 // that task functions take it by reference without a private-memory copy.
@@ -48,10 +66,13 @@ typedef const __attribute__((address_space(4))) KArgs KA;
 struct Lds {
   float xs[XS_FLOATS];   // activation staging (GEMV inputs), attention reduction scratch
   float q[8 * 128];      // attention: RoPE'd, scaled queries of one KV group
-  float sc[8 * 64];      // attention: scores / probabilities of one chunk
+  float sc[8 * 256];     // attention: scores of one chunk [head][position]
+  float pt[256 * 8];     // attention: probabilities of one chunk [position][head]
+  int pages[ATTN_MAX_SPLIT_PAGES];  // attention: physical pages of the split
   float kn[128], vn[128];// attention: the new token's K and V (BF16-rounded)
   float hm[8], hl[8], hscale[8], pnew[8];
   float inv[8];          // per-token RMSNorm scale
+  float ssqv[8 * 32];    // per-token partial sums of squares (row tiles)
   float gu[2 * 32 * 8];  // UP: gate/up values [row][token]
   float bestv[8 * NW];
   int besti[8 * NW];
@@ -61,6 +82,7 @@ struct Lds {
   uint32_t used[8];      // bitmask of selected experts (256 bits)
   int slot_e, slot_n, slot_b[8], slot_j[8];
   float slot_g[8];
+  int slotw[SLOT_WORDS];
   int task, next, flag;
 };
 
@@ -101,6 +123,8 @@ __device__ __forceinline__ float row8_sum(float v) {
   v += dpp<0x141>(v);
   return v;
 }
+// value of lane (i ^ 16) within each 32-lane half (ds_swizzle, bit mode: and 0x1f, xor 0x10)
+__device__ __forceinline__ float swz_xor16(float v) { return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)); }
 __device__ __forceinline__ float rdl(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
 // full-wave sum, uniform result, fixed order
 __device__ __forceinline__ float wave_sum(float v) {
@@ -137,11 +161,17 @@ __device__ __forceinline__ void spin_ge(KA& a, int32_t c, int32_t target, int ta
   }
 }
 
+// Debug trace: sub-phase mark k (0..3) of task t.
+__device__ __forceinline__ void mark(KA& a, int t, int k) {
+  if (a.ts && threadIdx.x == 0) a.ts[(int64_t)t * 8 + 4 + k] = wall_clock64();
+}
+
 // Wait for descriptor waits [i0, i1), then make the producers' data visible to the whole workgroup.
 __device__ __forceinline__ void wait_deps(KA& a, const int32_t* w, int i0, int i1, int task) {
   if (threadIdx.x == 0) {
     for (int i = i0; i < i1; ++i) spin_ge(a, w[W_WAIT0 + 2 * i], w[W_WAIT0 + 2 * i + 1], task);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (a.ts) a.ts[(int64_t)task * 8 + 1] = wall_clock64();
   }
   __syncthreads();
 }
@@ -169,19 +199,37 @@ __device__ __forceinline__ bool arrive_last(KA& a, int32_t c, int32_t n, Lds& S)
 // RMSNorm of the residual stream into LDS: xs[b][i] = x[b][i] * gamma[i] * inv_rms[b], for b < nb
 // (token list tok[] maps staging row -> batch row; null = identity).
 __device__ __forceinline__ void stage_norm(KA& a, const uint16_t* gamma, int nb, const int* tok, Lds& S) {
-  const int d = a.d;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (wave < nb && lane == 0) {
-    const int b = tok ? tok[wave] : wave;
-    float ss = 0.f;
-    for (int r = 0; r < a.n_rt; ++r) ss += a.ssq[b * a.n_rt + r];
-    S.inv[wave] = 1.0f / sqrtf(ss / (float)d + a.eps);
+  const int d = a.d, nrt = a.n_rt;
+  // one round trip: raw x rows, the partial sums of squares and the gain are loaded together
+  constexpr int MAXE = 4096 / NT;  // gain elements per thread (d_model <= 4096)
+  float gv[MAXE];
+#pragma unroll
+  for (int e = 0; e < MAXE; ++e) {
+    const int c = threadIdx.x + e * NT;
+    gv[e] = c < d ? bf2f(gamma[c]) : 0.f;
   }
-  __syncthreads();
   for (int i = threadIdx.x; i < nb * d; i += NT) {
     const int j = i / d, c = i - j * d;
     const int b = tok ? tok[j] : j;
-    S.xs[j * d + c] = a.x[b * d + c] * bf2f(gamma[c]) * S.inv[j];
+    S.xs[i] = a.x[b * d + c];
+  }
+  if (threadIdx.x < nb * nrt) {
+    const int j = threadIdx.x / nrt, r = threadIdx.x - j * nrt;
+    const int b = tok ? tok[j] : j;
+    S.ssqv[threadIdx.x] = a.ssq[b * nrt + r];
+  }
+  __syncthreads();
+  if (threadIdx.x < nb) {
+    float ss = 0.f;
+    for (int r = 0; r < nrt; ++r) ss += S.ssqv[threadIdx.x * nrt + r];
+    S.inv[threadIdx.x] = 1.0f / sqrtf(ss / (float)d + a.eps);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < MAXE; ++e) {
+    const int c = threadIdx.x + e * NT;
+    if (c < d)
+      for (int j = 0; j < nb; ++j) S.xs[j * d + c] *= gv[e] * S.inv[j];
   }
   __syncthreads();
 }
@@ -290,19 +338,25 @@ __device__ __forceinline__ void gemv_compute(const WBuf<NV, RPW>& buf, const flo
   }
 }
 
-// Drive a whole tile: pass 0 must already be in buf0.
+// Drive a whole tile: pass 0 is in buf0 and, when the tile has more passes, pass 1 is in buf1.
 template <int NV, int RPW, int NB, class RowPtr, class Out>
-__device__ __forceinline__ void gemv_run(WBuf<NV, RPW>& buf0, const RowPtr& W, int nrows, int K, const float* xs, int xp, int nb, Out& out) {
+__device__ __forceinline__ void gemv_run2(WBuf<NV, RPW>& buf0, WBuf<NV, RPW>& buf1, const RowPtr& W, int nrows, int K, const float* xs,
+                                          int xp, int nb, Out& out) {
   const int K8 = K >> 3;
   const int np = (nrows + NW * RPW - 1) / (NW * RPW);
-  WBuf<NV, RPW> buf1;
   for (int p = 0; p < np; p += 2) {
-    if (p + 1 < np) gemv_load(buf1, W, nrows, K8, p + 1);
     for (int b0 = 0; b0 < nb; b0 += NB) gemv_compute<NV, RPW, NB>(buf0, xs, xp, nb, nrows, K8, p, out, b0);
-    if (p + 1 >= np) break;
     if (p + 2 < np) gemv_load(buf0, W, nrows, K8, p + 2);
+    if (p + 1 >= np) break;
     for (int b0 = 0; b0 < nb; b0 += NB) gemv_compute<NV, RPW, NB>(buf1, xs, xp, nb, nrows, K8, p + 1, out, b0);
+    if (p + 3 < np) gemv_load(buf1, W, nrows, K8, p + 3);
   }
+}
+template <int NV, int RPW, int NB, class RowPtr, class Out>
+__device__ __forceinline__ void gemv_run(WBuf<NV, RPW>& buf0, const RowPtr& W, int nrows, int K, const float* xs, int xp, int nb, Out& out) {
+  WBuf<NV, RPW> buf1;
+  if (nrows > NW * RPW) gemv_load(buf1, W, nrows, K >> 3, 1);
+  gemv_run2<NV, RPW, NB>(buf0, buf1, W, nrows, K, xs, xp, nb, out);
 }
 
 // fp64-accumulating variant for the router (products of BF16 and fp32 are exact in fp64).
@@ -341,68 +395,51 @@ __device__ __forceinline__ void gemv_run_f64(WBuf<NV, RPW>& buf0, int nrows, int
 }
 
 // ------------------------------------------------------------------------------------------ routing
-// Top-k of the router logits per token (logit descending, lower index first on ties), gates = softmax
-// of the selected logits, and the compacted list of distinct experts (ascending id): slot s is the s-th
-// distinct expert.  Every task that needs it recomputes it from the logits (deterministic), so no task
-// has to publish it.
-__device__ __forceinline__ void compute_routing(KA& a, int l, Lds& S) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int E = a.E, k = a.k;
-  if (threadIdx.x < 8) S.used[threadIdx.x] = 0u;
+// Done once per layer by the router tile that finishes last: top-k of each token's router logits (logit
+// descending, lower index first on ties; a NaN ranks lowest), gates = softmax of the selected logits,
+// and the table of expert slots (slot s = the s-th distinct selected expert in ascending id, with the
+// tokens that chose it, their selection rank and gate).  Expert tasks read their slot's entry.
+__device__ __forceinline__ void route_layer(KA& a, int l, Lds& S) {
+  const int E = a.E, k = a.k, B = a.B, tid = threadIdx.x;
+  const float* lg = a.rlogits + (int64_t)l * B * E;
+  float* key = S.xs;  // [B][E] logits with NaN replaced by -inf
+  for (int i = tid; i < B * E; i += NT) {
+    const float v = lg[i];
+    key[i] = v == v ? v : -INFINITY;
+  }
+  if (tid < 8) S.used[tid] = 0u;
   __syncthreads();
-  if (wave < a.B) {
-    const int b = wave;
-    const float* lg = a.rlogits + ((int64_t)l * a.B + b) * E;
-    float v[4];
-    uint32_t taken = 0;  // bit i: expert lane + 64 i already selected (or absent)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      const float x = e < E ? lg[e] : -INFINITY;
-      v[i] = x == x ? x : -INFINITY;  // a NaN logit ranks lowest
-      if (e >= E) taken |= 1u << i;
+  // rank of (b, e) among the token's logits
+  for (int i = tid; i < B * E; i += NT) {
+    const int b = i / E, e = i - b * E;
+    const float v = key[i];
+    const float* kb = key + b * E;
+    int rank = 0;
+    for (int q = 0; q < E; ++q) {
+      const float u = kb[q];
+      rank += (u > v) || (u == v && q < e);
     }
-    float selv[8];
-    for (int j = 0; j < k; ++j) {
-      // best untaken entry: larger logit first, lower index on ties
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        if (!(taken >> i & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
-          bv = v[i];
-          be = e;
-        }
-      }
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oe = __shfl_xor(be, o);
-        if (ov > bv || (ov == bv && oe < be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      selv[j] = bv;
-      if (lane == 0) S.sel[b * 8 + j] = be;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + 64 * i == be) taken |= 1u << i;
-    }
-    if (lane == 0) {
-      const float mx = selv[0];
-      float z = 0.f;
-      for (int j = 0; j < k; ++j) z += expf(selv[j] - mx);
-      for (int j = 0; j < k; ++j) S.gate[b * 8 + j] = expf(selv[j] - mx) / z;
-      for (int j = 0; j < k; ++j) atomicOr(&S.used[S.sel[b * 8 + j] >> 5], 1u << (S.sel[b * 8 + j] & 31));
+    if (rank < k) {
+      S.sel[b * 8 + rank] = e;
+      atomicOr(&S.used[e >> 5], 1u << (e & 31));
     }
   }
   __syncthreads();
-}
-
-// Expert and token list of slot s (valid after compute_routing); returns false if the slot is unused.
-__device__ __forceinline__ bool slot_info(KA& a, int s, Lds& S) {
-  if (threadIdx.x == 0) {
+  if (tid < B) {
+    const int b = tid;
+    const float mx = key[b * E + S.sel[b * 8]];
+    float z = 0.f;
+    for (int j = 0; j < k; ++j) z += expf(key[b * E + S.sel[b * 8 + j]] - mx);
+    for (int j = 0; j < k; ++j) {
+      const float gt = expf(key[b * E + S.sel[b * 8 + j]] - mx) / z;
+      S.gate[b * 8 + j] = gt;
+      pubi(&a.route_sel[((int64_t)l * B + b) * k + j], S.sel[b * 8 + j]);
+      pub(&a.route_gate[((int64_t)l * B + b) * k + j], gt);
+    }
+  }
+  __syncthreads();
+  // slot table
+  for (int s = tid; s < a.n_slots; s += NT) {
     int e = -1, cnt = 0;
     for (int wd = 0; wd < 8 && e < 0; ++wd) {
       const uint32_t m = S.used[wd];
@@ -414,21 +451,37 @@ __device__ __forceinline__ bool slot_info(KA& a, int s, Lds& S) {
       }
       cnt += pc;
     }
-    S.slot_e = e;
+    int32_t* ent = a.slots + ((int64_t)l * a.n_slots + s) * SLOT_WORDS;
     int n = 0;
     if (e >= 0)
-      for (int b = 0; b < a.B; ++b)
-        for (int j = 0; j < a.k; ++j)
+      for (int b = 0; b < B; ++b)
+        for (int j = 0; j < k; ++j)
           if (S.sel[b * 8 + j] == e && n < 8) {
-            S.slot_b[n] = b;
-            S.slot_j[n] = j;
-            S.slot_g[n] = S.gate[b * 8 + j];
+            pubi(ent + 2 + 3 * n, b);
+            pubi(ent + 3 + 3 * n, j);
+            pubi(ent + 4 + 3 * n, __float_as_int(S.gate[b * 8 + j]));
             ++n;
           }
-    S.slot_n = n;
+    pubi(ent + 0, e);
+    pubi(ent + 1, n);
+  }
+}
+
+// Load slot s's routing entry into LDS (valid after the layer's routing was published); false if unused.
+__device__ __forceinline__ bool load_slot(KA& a, int l, int s, Lds& S) {
+  if (threadIdx.x < SLOT_WORDS) S.slotw[threadIdx.x] = a.slots[((int64_t)l * a.n_slots + s) * SLOT_WORDS + threadIdx.x];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    S.slot_e = S.slotw[0];
+    S.slot_n = S.slot_e >= 0 ? min(S.slotw[1], 8) : 0;
+    for (int i = 0; i < S.slot_n; ++i) {
+      S.slot_b[i] = S.slotw[2 + 3 * i];
+      S.slot_j[i] = S.slotw[3 + 3 * i];
+      S.slot_g[i] = __int_as_float(S.slotw[4 + 3 * i]);
+    }
   }
   __syncthreads();
-  return S.slot_e >= 0;
+  return S.slot_e >= 0 && S.slot_e < a.E;
 }
 
 // ------------------------------------------------------------------------------------------ task bodies
@@ -488,38 +541,33 @@ __device__ __forceinline__ void task_resid(KA& a, const int32_t* w, int t, Lds& 
   signal(a, w[W_SIG], w[W_SIGN]);
 }
 
-// K/8 bucket -> (NV, RPW) and batch bucket dispatch
-template <class F>
-__device__ __forceinline__ void dispatch_nb(int nb, F&& f) {
-  if (nb <= 1) f.template operator()<1>();
-  else if (nb <= 2) f.template operator()<2>();
-  else f.template operator()<4>();
-}
 
-// Generic "prefetch, wait, stage, stream" GEMV task.  Stage(): fills S.xs after the wait.
-// Passes hold 8 16-byte vectors per lane (64 KB per workgroup); two passes are in flight.
-template <int NV, int RPW, class RowPtr, class Stage, class Out>
-__device__ __forceinline__ void gemv_task(KA& a, const int32_t* w, int t, const RowPtr& W, int nrows, int K, int nb, int wait0, int wait1,
-                          Stage&& stage, Out&& out, Lds& S) {
-  WBuf<NV, RPW> buf0;
-  gemv_load(buf0, W, nrows, K >> 3, 0);  // weights stream while the inputs are still being produced
+// Generic "prefetch, wait, stage, stream" GEMV task.  Stage(): fills S.xs after the wait.  The first two
+// passes of the tile are loaded before the dependency wait (a one-token tile uses 16-vector passes, so up
+// to 256 KB per workgroup is in flight while its inputs are being produced).
+template <int NV>
+struct RpwBig {
+  static constexpr int value = NV == 1 ? 8 : NV == 2 ? 8 : NV == 4 ? 4 : 2;
+};
+template <int NV, int RPW, int NB, class RowPtr, class Stage, class Out>
+__device__ __forceinline__ void gemv_task_nb(KA& a, const int32_t* w, int t, const RowPtr& W, int nrows, int K, int nb, int wait0,
+                                             int wait1, Stage& stage, Out& out, Lds& S) {
+  WBuf<NV, RPW> buf0, buf1;
+  gemv_load(buf0, W, nrows, K >> 3, 0);
+  if (nrows > NW * RPW) gemv_load(buf1, W, nrows, K >> 3, 1);
   wait_deps(a, w, wait0, wait1, t);
   stage();
-  if (nb <= 1) gemv_run<NV, RPW, 1>(buf0, W, nrows, K, S.xs, K, nb, out);
-  else if (nb <= 2) gemv_run<NV, RPW, 2>(buf0, W, nrows, K, S.xs, K, nb, out);
-  else gemv_run<NV, RPW, 4>(buf0, W, nrows, K, S.xs, K, nb, out);  // 5..8 tokens: two groups of 4
+  gemv_run2<NV, RPW, NB>(buf0, buf1, W, nrows, K, S.xs, K, nb, out);
+}
+template <int NV, class RowPtr, class Stage, class Out>
+__device__ __forceinline__ void gemv_task(KA& a, const int32_t* w, int t, const RowPtr& W, int nrows, int K, int nb, int wait0, int wait1,
+                                          Stage&& stage, Out&& out, Lds& S) {
+  if (nb <= 1) gemv_task_nb<NV, RpwBig<NV>::value, 1>(a, w, t, W, nrows, K, nb, wait0, wait1, stage, out, S);
+  else if (nb <= 2) gemv_task_nb<NV, RpwOf<NV>::value, 2>(a, w, t, W, nrows, K, nb, wait0, wait1, stage, out, S);
+  else gemv_task_nb<NV, RpwOf<NV>::value, 4>(a, w, t, W, nrows, K, nb, wait0, wait1, stage, out, S);  // 5..8 tokens: two groups
 }
 
-template <class RowPtr, class Stage, class Out>
-__device__ __forceinline__ void gemv_task_k(KA& a, const int32_t* w, int t, const RowPtr& W, int nrows, int K, int nb, int wait0, int wait1,
-                            Stage&& stage, Out&& out, Lds& S) {
-  const int K8 = K >> 3;
-  if (K8 <= 64) gemv_task<1, 4>(a, w, t, W, nrows, K, nb, wait0, wait1, stage, out, S);
-  else if (K8 <= 128) gemv_task<2, 4>(a, w, t, W, nrows, K, nb, wait0, wait1, stage, out, S);
-  else if (K8 <= 256) gemv_task<4, 2>(a, w, t, W, nrows, K, nb, wait0, wait1, stage, out, S);
-  else gemv_task<8, 1>(a, w, t, W, nrows, K, nb, wait0, wait1, stage, out, S);
-}
-
+template <class C>
 __device__ __forceinline__ void task_qkv(KA& a, const int32_t* w, int t, Lds& S) {
   const int l = w[W_LAYER], g = w[W_A], r0 = w[W_R0], r1 = w[W_R1];
   const int grp = a.Hq / a.Hkv, dh = a.dh, d = a.d;
@@ -531,12 +579,13 @@ __device__ __forceinline__ void task_qkv(KA& a, const int32_t* w, int t, Lds& S)
   const int rows = (grp + 2) * dh;
   float* out = a.qkv + (int64_t)g * rows + r0;
   const int64_t bstride = (int64_t)a.Hkv * rows;
-  gemv_task_k(
+  gemv_task<C::NVD>(
       a, w, t, Rows1{W, d}, r1 - r0, d, a.B, 0, N_WAITS, [&] { stage_norm(a, L.attn_norm, a.B, nullptr, S); },
       [&](int r, int b, float v) { pub(out + b * bstride + r, v); }, S);
   signal(a, w[W_SIG], w[W_SIGN]);
 }
 
+template <class C>
 __device__ __forceinline__ void task_router(KA& a, const int32_t* w, int t, Lds& S) {
   const int l = w[W_LAYER], r0 = w[W_R0], r1 = w[W_R1];
   const LayerW& L = a.layers[l];
@@ -558,19 +607,21 @@ __device__ __forceinline__ void task_router(KA& a, const int32_t* w, int t, Lds&
     else if (nb <= 4) gemv_run_f64<NV, RPW, 4>(buf0, nrows, d, S.xs, d, nb, out);
     else gemv_run_f64<NV, RPW, 8>(buf0, nrows, d, S.xs, d, nb, out);
   };
-  if (K8 <= 64) go(NVR<1, 2>{});
-  else if (K8 <= 128) go(NVR<2, 2>{});
-  else if (K8 <= 256) go(NVR<4, 2>{});
-  else go(NVR<8, 2>{});
-  signal(a, w[W_SIG], w[W_SIGN]);
+  (void)K8;
+  go(NVR<C::NVD, 2>{});
+  if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) {
+    route_layer(a, l, S);
+    signal(a, w[W_SIG], w[W_SIGN]);
+  }
 }
 
+template <class C>
 __device__ __forceinline__ void task_oproj(KA& a, const int32_t* w, int t, Lds& S) {
   const int l = w[W_LAYER], g = w[W_A], r0 = w[W_R0], r1 = w[W_R1];
   const int grp = a.Hq / a.Hkv, K = grp * a.dh, ldo = a.Hq * a.dh, B = a.B, d = a.d;
   const uint16_t* W = a.layers[l].wo + (int64_t)r0 * ldo + (int64_t)g * K;
   float* out = a.opart + (int64_t)g * B * d + r0;
-  gemv_task_k(
+  gemv_task<C::NVO>(
       a, w, t, Rows1{W, ldo}, r1 - r0, K, B, 0, N_WAITS,
       [&] {
         for (int i = threadIdx.x; i < B * K; i += NT) {
@@ -583,36 +634,30 @@ __device__ __forceinline__ void task_oproj(KA& a, const int32_t* w, int t, Lds& 
   signal(a, w[W_SIG], w[W_SIGN]);
 }
 
+template <class C>
 __device__ __forceinline__ void task_up(KA& a, const int32_t* w, int t, Lds& S) {
   const int l = w[W_LAYER], s = w[W_A], r0 = w[W_R0], r1 = w[W_R1];
   const int d = a.d, F = a.F, nr = r1 - r0;
   wait_deps(a, w, 0, N_WAITS, t);
-  compute_routing(a, l, S);
-  if (s == 0 && r0 == 0 && threadIdx.x < a.B * a.k) {  // routing record (debug read-back)
-    const int b = threadIdx.x / a.k, j = threadIdx.x - b * a.k;
-    a.route_sel[((int64_t)l * a.B + b) * a.k + j] = S.sel[b * 8 + j];
-    a.route_gate[((int64_t)l * a.B + b) * a.k + j] = S.gate[b * 8 + j];
-  }
-  if (slot_info(a, s, S)) {
+  if (load_slot(a, l, s, S)) {
     const int e = S.slot_e, n = S.slot_n;
     const LayerW& L = a.layers[l];
     // gate rows then up rows of this tile, as one 2*nr-row tile (two bases)
     const uint16_t* Wg = L.w_gate + ((int64_t)e * F + r0) * d;
     const uint16_t* Wu = L.w_up + ((int64_t)e * F + r0) * d;
-    stage_norm(a, L.attn_norm, n, S.slot_b, S);
     const Rows2 rows{Wg, Wu, d, nr};
     auto out = [&](int r, int b, float v) { S.gu[r * 8 + b] = v; };
-    auto run = [&](auto nvr) {
-      constexpr int NV = decltype(nvr)::nv, RPW = decltype(nvr)::rpw;
-      WBuf<NV, RPW> b0;
-      gemv_load(b0, rows, 2 * nr, d >> 3, 0);
-      dispatch_nb(n, [&]<int NB>() { gemv_run<NV, RPW, NB>(b0, rows, 2 * nr, d, S.xs, d, n, out); });
+    auto run = [&](auto nvr, auto nbc) {
+      constexpr int NV = decltype(nvr)::nv, RPW = decltype(nvr)::rpw, NB = decltype(nbc)::value;
+      WBuf<NV, RPW> b0, b1;
+      gemv_load(b0, rows, 2 * nr, d >> 3, 0);  // the expert's weights stream while its inputs are staged
+      if (2 * nr > NW * RPW) gemv_load(b1, rows, 2 * nr, d >> 3, 1);
+      stage_norm(a, L.attn_norm, n, S.slot_b, S);
+      gemv_run2<NV, RPW, NB>(b0, b1, rows, 2 * nr, d, S.xs, d, n, out);
     };
-    const int K8 = d >> 3;
-    if (K8 <= 64) run(NVR<1, 4>{});
-    else if (K8 <= 128) run(NVR<2, 4>{});
-    else if (K8 <= 256) run(NVR<4, 2>{});
-    else run(NVR<8, 1>{});
+    if (n <= 1) run(NVR<C::NVD, RpwBig<C::NVD>::value>{}, std::integral_constant<int, 1>{});
+    else if (n <= 2) run(NVR<C::NVD, RpwOf<C::NVD>::value>{}, std::integral_constant<int, 2>{});
+    else run(NVR<C::NVD, RpwOf<C::NVD>::value>{}, std::integral_constant<int, 4>{});
     __syncthreads();
     for (int i = threadIdx.x; i < nr * n; i += NT) {
       const int r = i / n, j = i - r * n;
@@ -624,15 +669,15 @@ __device__ __forceinline__ void task_up(KA& a, const int32_t* w, int t, Lds& S) 
   signal(a, w[W_SIG], w[W_SIGN]);
 }
 
+template <class C>
 __device__ __forceinline__ void task_down(KA& a, const int32_t* w, int t, Lds& S) {
   const int l = w[W_LAYER], s = w[W_A], r0 = w[W_R0], r1 = w[W_R1];
   const int d = a.d, F = a.F, nr = r1 - r0;
   wait_deps(a, w, 0, 1, t);  // routing is known: this expert's weights can stream before its hidden state exists
-  compute_routing(a, l, S);
-  if (slot_info(a, s, S)) {
+  if (load_slot(a, l, s, S)) {
     const int e = S.slot_e, n = S.slot_n;
     const uint16_t* W = a.layers[l].w_down + ((int64_t)e * d + r0) * F;
-    gemv_task_k(
+    gemv_task<C::NVF>(
         a, w, t, Rows1{W, F}, nr, F, n, 1, N_WAITS,
         [&] {
           for (int i = threadIdx.x; i < n * F; i += NT) S.xs[i] = a.h[(int64_t)s * a.B * F + i];
@@ -645,6 +690,7 @@ __device__ __forceinline__ void task_down(KA& a, const int32_t* w, int t, Lds& S
   signal(a, w[W_SIG], w[W_SIGN]);
 }
 
+template <class C>
 __device__ __forceinline__ void task_lmhead(KA& a, const int32_t* w, int t, Lds& S) {
   const int r0 = w[W_R0], r1 = w[W_R1], tile = w[W_A];
   const int d = a.d, B = a.B, nr = r1 - r0;
@@ -655,7 +701,7 @@ __device__ __forceinline__ void task_lmhead(KA& a, const int32_t* w, int t, Lds&
     S.besti[threadIdx.x] = 0x7fffffff;
   }
   // each wave keeps its own running best per token (rows are visited in increasing order per wave)
-  gemv_task_k(
+  gemv_task<C::NVD>(
       a, w, t, Rows1{W, d}, nr, d, B, 0, N_WAITS, [&] { stage_norm(a, a.final_norm, B, nullptr, S); },
       [&](int r, int b, float v) {
         a.logits[(int64_t)b * a.V + r0 + r] = v;
@@ -710,18 +756,20 @@ __device__ __forceinline__ void task_lmhead(KA& a, const int32_t* w, int t, Lds&
 }
 
 // ------------------------------------------------------------------------------------------ attention
-// Split s of (sequence b, KV group g): positions [j0, j1) of the sequence's 0..len window (len = its
-// prior length; position len is the new token, taken from this step's projections, RoPE'd, rounded to
-// BF16 and written to the cache by the split that holds it).  Chunks of 64 positions: for the scores,
-// each thread owns one 8-dim slice of one position (16 B of K from HBM, queries of all heads of the
-// group in registers); for P*V, each thread owns (head, dim) outputs and reads the chunk's V from LDS.
+// Split s of (sequence b, KV group g) covers positions [j0, j1) of the sequence's 0..len window (len =
+// its prior length; position len is the new token, taken from this step's projections, RoPE'd, rounded
+// to BF16 and written to the cache by the split that holds it).  The split's page list and its first
+// chunk of K and V (256 positions) are loaded BEFORE the task waits for this step's queries.  Each thread
+// owns one 8-dim slice of NP positions of a chunk: it forms the scores of every head of the group for
+// its positions (queries in registers, slice sums by DPP), and after the chunk's softmax it accumulates
+// p * V for its slice and positions.  The per-thread partial outputs are reduced once per split.
 template <int DH, int GRP>
 __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& S) {
-  constexpr int SL = DH / 8;        // slices per position
-  constexpr int PPP = NT / SL;      // positions per pass
-  constexpr int CH = 64;            // positions per chunk
-  constexpr int NPASS = CH / PPP;   // 2 (DH=128) or 1 (DH=64)
-  constexpr int NO = (GRP * DH + NT - 1) / NT;  // (head, dim) outputs per thread
+  constexpr int DPT = 4;            // dims per thread slice
+  constexpr int SL = DH / DPT;      // slices per position (32 or 16)
+  constexpr int PPP = NT / SL;      // positions per pass (16 or 32)
+  constexpr int CH = 128;           // positions per chunk
+  constexpr int NP = CH / PPP;      // positions per thread per chunk (8 or 4)
   const int l = w[W_LAYER], b = w[W_A], g = w[W_B], s = w[W_C], nsplit = w[W_D];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sl = tid % SL, pp = tid / SL;
@@ -734,32 +782,45 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
   const int npos = len + 1;
   int chunk = (npos + nsplit - 1) / nsplit;
   chunk = (chunk + CH - 1) / CH * CH;
-  const int j0 = s * chunk, j1 = min(j0 + chunk, npos);
+  if (chunk > ATTN_MAX_SPLIT_PAGES * 16) {  // lengths grew far beyond the planned split count
+    if (tid == 0) raise_error(a, ERRC_SEQLEN, t);
+    chunk = ATTN_MAX_SPLIT_PAGES * 16;
+  }
+  const int j0 = min(s * chunk, npos), j1 = min(j0 + chunk, npos);
   const int jc1 = min(j1, len);  // cached positions end
   const bool has_new = (j0 <= len && len < j1);
   const int32_t* ptab = a.page_tables + (int64_t)b * a.max_pages;
   uint16_t* kvl = a.kv + (int64_t)l * a.n_pages * 2 * Hkv * 16 * DH;
-  uint16_t* vs = reinterpret_cast<uint16_t*>(S.xs);  // V of the chunk, [CH][DH] BF16
+  const int64_t vstride = (int64_t)Hkv * 16 * DH;
 
-  auto load_kv = [&](int c0, int pass, u4& kk, u4& vv) {
-    const int pos = c0 + pass * PPP + pp;
-    kk = vv = u4{0, 0, 0, 0};
-    if (pos < jc1) {
-      const int ph = ptab[pos >> 4];
-      if (ph < 0 || ph >= a.n_pages) {
-        raise_error(a, ERRC_PAGE, t);
-        return;
+  // page list of the split
+  const int np0 = j0 >> 4, npg = jc1 > j0 ? ((jc1 - 1) >> 4) - np0 + 1 : 0;
+  for (int i = tid; i < npg; i += NT) {
+    int ph = ptab[np0 + i];
+    if (ph < 0 || ph >= a.n_pages) {
+      raise_error(a, ERRC_PAGE, t);
+      ph = -1;
+    }
+    S.pages[i] = ph;
+  }
+  __syncthreads();
+  auto load_chunk = [&](int c0, u2 (&kk)[NP], u2 (&vv)[NP]) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int pos = c0 + pp + PPP * i;
+      kk[i] = vv[i] = u2{0, 0};
+      if (pos < jc1) {
+        const int ph = S.pages[(pos >> 4) - np0];
+        if (ph >= 0) {
+          const int64_t base = (((int64_t)ph * 2) * Hkv + g) * 16 * DH + (pos & 15) * DH + sl * DPT;
+          kk[i] = __builtin_nontemporal_load(as_global2(kvl + base));
+          vv[i] = __builtin_nontemporal_load(as_global2(kvl + base + vstride));
+        }
       }
-      const int64_t base = (((int64_t)ph * 2) * Hkv + g) * 16 * DH + (pos & 15) * DH + sl * 8;
-      kk = __builtin_nontemporal_load(as_global(kvl + base));
-      vv = __builtin_nontemporal_load(as_global(kvl + base + (int64_t)Hkv * 16 * DH));
     }
   };
-
-  // prefetch the first chunk of cached K/V before waiting for this step's projections
-  u4 kc[NPASS], vc[NPASS];
-#pragma unroll
-  for (int p = 0; p < NPASS; ++p) load_kv(j0, p, kc[p], vc[p]);
+  u2 kc[NP], vc[NP];
+  load_chunk(j0, kc, vc);  // old K/V stream while this step's projections are produced
 
   wait_deps(a, w, 0, N_WAITS, t);
 
@@ -794,41 +855,40 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
       const int64_t base = (((int64_t)ph * 2) * Hkv + g) * 16 * DH + (len & 15) * DH;
       for (int j = tid; j < DH; j += NT) {
         kvl[base + j] = f2bf(S.kn[j]);
-        kvl[base + (int64_t)Hkv * 16 * DH + j] = f2bf(S.vn[j]);
+        kvl[base + vstride + j] = f2bf(S.vn[j]);
       }
     } else if (tid == 0) {
       raise_error(a, ERRC_PAGE, t);
     }
   }
-  float qr[GRP][8];
+  mark(a, t, 0);
+  float qr[GRP][DPT];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) {
+    const f4 q0 = *reinterpret_cast<const f4*>(S.q + h * DH + sl * DPT);
+    qr[h][0] = q0.x; qr[h][1] = q0.y; qr[h][2] = q0.z; qr[h][3] = q0.w;
+  }
+  float o[GRP][DPT];
 #pragma unroll
   for (int h = 0; h < GRP; ++h)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qr[h][i] = S.q[h * DH + sl * 8 + i];
-  float o[NO];
-#pragma unroll
-  for (int i = 0; i < NO; ++i) o[i] = 0.f;
+    for (int i = 0; i < DPT; ++i) o[h][i] = 0.f;
 
   for (int c0 = j0; c0 < jc1; c0 += CH) {
-    u4 kn_[NPASS], vn_[NPASS];
-    const bool more = c0 + CH < jc1;
+    // scores of this thread's positions, summed over the SL lanes of each position
 #pragma unroll
-    for (int p = 0; p < NPASS; ++p)
-      if (more) load_kv(c0 + CH, p, kn_[p], vn_[p]);
-    // scores: partial over this thread's slice, summed over the SL lanes of the position
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-      const int pl = p * PPP + pp;
+    for (int i = 0; i < NP; ++i) {
+      const int pl = pp + PPP * i;
       const int pos = c0 + pl;
-      *reinterpret_cast<u4*>(vs + pl * DH + sl * 8) = vc[p];
-      const float kf[8] = {bf_lo(kc[p].x), bf_hi(kc[p].x), bf_lo(kc[p].y), bf_hi(kc[p].y),
-                           bf_lo(kc[p].z), bf_hi(kc[p].z), bf_lo(kc[p].w), bf_hi(kc[p].w)};
+      const u2 k2 = kc[i];
+      const float kf[DPT] = {bf_lo(k2.x), bf_hi(k2.x), bf_lo(k2.y), bf_hi(k2.y)};
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
         float sc = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sc = fmaf(qr[h][i], kf[i], sc);
-        sc = SL == 16 ? row16_sum(sc) : row8_sum(sc);
+        for (int e = 0; e < DPT; ++e) sc = fmaf(qr[h][e], kf[e], sc);
+        sc = row16_sum(sc);
+        if (SL == 32) sc += swz_xor16(sc);
         if (sl == h) S.sc[h * CH + pl] = pos < jc1 ? sc : -INFINITY;
       }
     }
@@ -836,12 +896,24 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
     // online softmax update, one wave per head
     if (wave < GRP) {
       const int h = wave;
-      const float v = S.sc[h * CH + lane];
+      constexpr int R = CH / 64;
+      float v[R];
+      float vm = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        v[r] = S.sc[h * CH + lane + 64 * r];
+        vm = fmaxf(vm, v[r]);
+      }
       const float mold = S.hm[h];
-      const float mnew = fmaxf(mold, wave_max(v));
-      const float pr = v == -INFINITY ? 0.f : expf(v - mnew);
-      const float psum = wave_sum(pr);
-      S.sc[h * CH + lane] = pr;
+      const float mnew = fmaxf(mold, wave_max(vm));
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float pr = v[r] == -INFINITY ? 0.f : expf(v[r] - mnew);
+        S.pt[(lane + 64 * r) * 8 + h] = pr;
+        ps += pr;
+      }
+      const float psum = wave_sum(ps);
       if (lane == 0) {
         const float sc = mold == -INFINITY ? 0.f : expf(mold - mnew);
         S.hscale[h] = sc;
@@ -850,26 +922,30 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
       }
     }
     __syncthreads();
-    // P * V for this thread's (head, dim) outputs
-    const int nvalid = min(CH, jc1 - c0);
 #pragma unroll
-    for (int i = 0; i < NO; ++i) {
-      const int pr = tid + i * NT;
-      if (pr < GRP * DH) {
-        const int h = pr / DH, dd = pr - h * DH;
-        float acc = o[i] * S.hscale[h];
-        const float* ph = S.sc + h * CH;
-        for (int j = 0; j < nvalid; ++j) acc = fmaf(ph[j], bf2f(vs[j * DH + dd]), acc);
-        o[i] = acc;
-      }
+    for (int h = 0; h < GRP; ++h) {
+      const float sc = S.hscale[h];
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) o[h][e] *= sc;
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int pl = pp + PPP * i;
+      const u2 v2 = vc[i];
+      const float vf[DPT] = {bf_lo(v2.x), bf_hi(v2.x), bf_lo(v2.y), bf_hi(v2.y)};
+      float pr[8];
+      const f4 p0 = *reinterpret_cast<const f4*>(S.pt + pl * 8);
+      const f4 p1 = *reinterpret_cast<const f4*>(S.pt + pl * 8 + 4);
+      pr[0] = p0.x; pr[1] = p0.y; pr[2] = p0.z; pr[3] = p0.w; pr[4] = p1.x; pr[5] = p1.y; pr[6] = p1.z; pr[7] = p1.w;
+#pragma unroll
+      for (int h = 0; h < GRP; ++h)
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) o[h][e] = fmaf(pr[h], vf[e], o[h][e]);
     }
     __syncthreads();
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-      kc[p] = kn_[p];
-      vc[p] = vn_[p];
-    }
+    if (c0 + CH < jc1) load_chunk(c0 + CH, kc, vc);
   }
+  mark(a, t, 1);
   // the new token
   if (has_new) {
     if (wave < GRP) {
@@ -889,97 +965,137 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < NO; ++i) {
-      const int pr = tid + i * NT;
-      if (pr < GRP * DH) {
-        const int h = pr / DH, dd = pr - h * DH;
-        o[i] = fmaf(S.pnew[h], S.vn[dd], o[i] * S.hscale[h]);
+    for (int h = 0; h < GRP; ++h) {
+      const float sc = S.hscale[h];
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) o[h][e] *= sc;
+      if (pp == 0) {
+        const float pn = S.pnew[h];
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) o[h][e] = fmaf(pn, S.vn[sl * DPT + e], o[h][e]);
       }
     }
   }
-  // partial (o, m, l) of this split
-  float* part = a.apart + ((((int64_t)b * Hkv + g) * ATTN_MAX_SPLITS + s) * GRP) * (DH + 2);
+  // reduce the per-thread partial outputs over positions: lanes of one slice within the wave, then the
+  // waves in order through LDS
 #pragma unroll
-  for (int i = 0; i < NO; ++i) {
-    const int pr = tid + i * NT;
-    if (pr < GRP * DH) {
-      const int h = pr / DH, dd = pr - h * DH;
-      pub(part + h * (DH + 2) + dd, o[i]);
+  for (int h = 0; h < GRP; ++h)
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) {
+      float v = o[h][e];
+      if (SL == 16) v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      o[h][e] = v;
     }
+  float* red = S.xs;  // [NW][GRP][DH]
+  if (lane < SL) {
+#pragma unroll
+    for (int h = 0; h < GRP; ++h)
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) red[(wave * GRP + h) * DH + sl * DPT + e] = o[h][e];
+  }
+  __syncthreads();
+  float* part = a.apart + ((((int64_t)b * Hkv + g) * ATTN_MAX_SPLITS + s) * GRP) * (DH + 2);
+  for (int i = tid; i < GRP * DH; i += NT) {
+    const int h = i / DH, dd = i - h * DH;
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) v += red[(q * GRP + h) * DH + dd];
+    pub(part + h * (DH + 2) + dd, v);
   }
   if (tid < GRP) {
     pub(part + tid * (DH + 2) + DH, S.hm[tid]);
     pub(part + tid * (DH + 2) + DH + 1, S.hl[tid]);
   }
+  mark(a, t, 2);
   // the last split of (b, g) to finish merges all splits (log-sum-exp) and publishes the group's output
   if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) {
+    mark(a, t, 3);
     const float* p0 = a.apart + (((int64_t)b * Hkv + g) * ATTN_MAX_SPLITS) * GRP * (DH + 2);
+    float* wsc = S.xs;                        // [GRP][nsplit] weights exp(m_s - M)
+    float* lsum = S.xs + GRP * ATTN_MAX_SPLITS;  // [GRP]
+    for (int i = tid; i < GRP * nsplit; i += NT) {
+      const int h = i / nsplit, q = i - h * nsplit;
+      wsc[i] = p0[((int64_t)q * GRP + h) * (DH + 2) + DH];
+    }
+    __syncthreads();
+    if (wave < GRP) {
+      const int h = wave;
+      float M = -INFINITY;
+      for (int q = lane; q < nsplit; q += 64) M = fmaxf(M, wsc[h * nsplit + q]);
+      M = wave_max(M);
+      float Ls = 0.f;
+      for (int q = lane; q < nsplit; q += 64) {
+        const float mq = wsc[h * nsplit + q];
+        const float wq = mq == -INFINITY ? 0.f : expf(mq - M);
+        wsc[h * nsplit + q] = wq;
+        Ls = fmaf(p0[((int64_t)q * GRP + h) * (DH + 2) + DH + 1], wq, Ls);
+      }
+      Ls = wave_sum(Ls);
+      if (lane == 0) lsum[h] = Ls;
+    }
+    __syncthreads();
     for (int i = tid; i < GRP * DH; i += NT) {
       const int h = i / DH, dd = i - h * DH;
-      float M = -INFINITY;
-      for (int q = 0; q < nsplit; ++q) M = fmaxf(M, p0[((int64_t)q * GRP + h) * (DH + 2) + DH]);
-      float Lsum = 0.f, ov = 0.f;
-      for (int q = 0; q < nsplit; ++q) {
-        const float* pq = p0 + ((int64_t)q * GRP + h) * (DH + 2);
-        const float mq = pq[DH];
-        const float wq = mq == -INFINITY ? 0.f : expf(mq - M);
-        Lsum = fmaf(pq[DH + 1], wq, Lsum);
-        ov = fmaf(pq[dd], wq, ov);
+      float ov = 0.f;
+      int q = 0;
+      for (; q + 8 <= nsplit; q += 8) {
+        float vv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) vv[u] = p0[((int64_t)(q + u) * GRP + h) * (DH + 2) + dd];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ov = fmaf(vv[u], wsc[h * nsplit + q + u], ov);
       }
-      pub(a.attn_o + (int64_t)b * a.Hq * DH + ((int64_t)g * GRP + h) * DH + dd, ov / Lsum);
+      for (; q < nsplit; ++q) ov = fmaf(p0[((int64_t)q * GRP + h) * (DH + 2) + dd], wsc[h * nsplit + q], ov);
+      pub(a.attn_o + (int64_t)b * a.Hq * DH + ((int64_t)g * GRP + h) * DH + dd, ov / lsum[h]);
     }
     signal(a, w[W_SIG], w[W_SIGN]);
   }
 }
 
+template <class C>
 __device__ __forceinline__ void task_attn(KA& a, const int32_t* w, int t, Lds& S) {
-  const int grp = a.Hq / a.Hkv;
-  if (a.dh == 128) {
-    if (grp == 8) attn_split<128, 8>(a, w, t, S);
-    else if (grp == 4) attn_split<128, 4>(a, w, t, S);
-    else attn_split<128, 2>(a, w, t, S);
-  } else {
-    if (grp == 8) attn_split<64, 8>(a, w, t, S);
-    else if (grp == 4) attn_split<64, 4>(a, w, t, S);
-    else attn_split<64, 2>(a, w, t, S);
-  }
+  attn_split<C::DH, C::GRP>(a, w, t, S);
 }
 
 // ------------------------------------------------------------------------------------------ the kernel
 
-__global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
-  KA& a = *(KA*)(__builtin_amdgcn_kernarg_segment_ptr());
-  (void)args;
-  __shared__ Lds S;
+// One task.  The argument block is re-derived from an opaque copy of its address on every task so
+// that no field is hoisted out of the task loop (that would pin dozens of registers for the kernel's
+// whole life).
+template <class C>
+__device__ __forceinline__ void run_task(KA* a0, const int32_t* w, int t, uint32_t& nxt, Lds& S) {
+  KA* ap = a0;
+  __asm__ volatile("" : "+s"(ap));
+  KA& a = *ap;
   const int tid = threadIdx.x;
-  if (tid == 0) S.next = (int)__hip_atomic_fetch_add(&a.ctr[a.c_ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  for (;;) {
-    const int t = S.next;
-    __syncthreads();
-    if (t >= a.n_tasks) break;
-    // claim the next task now; its ticket returns while this one runs
-    uint32_t nxt = 0;
-    if (tid == 0) nxt = __hip_atomic_fetch_add(&a.ctr[a.c_ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int32_t* w = a.tasks + (int64_t)t * DESC_WORDS;
-    switch (w[W_OP]) {
-      case OP_EMBED: task_embed(a, w, t, S); break;
-      case OP_ROUTER: task_router(a, w, t, S); break;
-      case OP_QKV: task_qkv(a, w, t, S); break;
-      case OP_ATTN: task_attn(a, w, t, S); break;
-      case OP_UP: task_up(a, w, t, S); break;
-      case OP_OPROJ: task_oproj(a, w, t, S); break;
-      case OP_DOWN: task_down(a, w, t, S); break;
-      case OP_RESID: task_resid(a, w, t, S); break;
-      case OP_LMHEAD: task_lmhead(a, w, t, S); break;
-      default:
-        if (tid == 0) raise_error(a, ERRC_OPCODE, t);
-    }
-    if (a.task_done && tid == 0) atomicAdd(&a.task_done[t], 1u);
-    if (tid == 0) S.next = (int)nxt;
-    __syncthreads();
+  if (a.ts && tid == 0) {
+    a.ts[(int64_t)t * 8 + 0] = wall_clock64();
+    a.ts[(int64_t)t * 8 + 1] = 0;
+    // hardware id: XCC id in the high word, the wave's HW_ID register in the low word
+    a.ts[(int64_t)t * 8 + 3] = ((uint64_t)__builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11)) << 32) |
+                               (uint64_t)__builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));
   }
-  // the last workgroup out resets the counters for the next step (stream order makes it visible)
+  switch (w[W_OP]) {
+    case OP_EMBED: task_embed(a, w, t, S); break;
+    case OP_ROUTER: task_router<C>(a, w, t, S); break;
+    case OP_QKV: task_qkv<C>(a, w, t, S); break;
+    case OP_ATTN: task_attn<C>(a, w, t, S); break;
+    case OP_UP: task_up<C>(a, w, t, S); break;
+    case OP_OPROJ: task_oproj<C>(a, w, t, S); break;
+    case OP_DOWN: task_down<C>(a, w, t, S); break;
+    case OP_RESID: task_resid(a, w, t, S); break;
+    case OP_LMHEAD: task_lmhead<C>(a, w, t, S); break;
+    default:
+      if (tid == 0) raise_error(a, ERRC_OPCODE, t);
+  }
+  if (a.task_done && tid == 0) atomicAdd(&a.task_done[t], 1u);
+  if (a.ts && tid == 0) a.ts[(int64_t)t * 8 + 2] = wall_clock64();
+}
+
+// The last workgroup out resets the counters for the next step (stream order makes it visible).
+__device__ __forceinline__ void exit_step(KA& a, Lds& S) {
+  const int tid = threadIdx.x;
   __syncthreads();
   if (tid == 0) {
     const uint32_t old = __hip_atomic_fetch_add(&a.ctr[a.c_done], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -994,9 +1110,44 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
   }
 }
 
-}  // namespace mk
+template <class C>
+__global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
+  KA* const a0 = (KA*)(__builtin_amdgcn_kernarg_segment_ptr());
+  (void)args;
+  __shared__ Lds S;
+  const int tid = threadIdx.x;
+  KA& a = *a0;
+  if (tid == 0) S.next = (int)__hip_atomic_fetch_add(&a.ctr[a.c_ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  for (;;) {
+    const int t = S.next;
+    __syncthreads();
+    if (t >= a.n_tasks) break;
+    // claim the next task now; its ticket returns while this one runs
+    uint32_t nxt = 0;
+    if (tid == 0) nxt = __hip_atomic_fetch_add(&a.ctr[a.c_ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int32_t* w = a.tasks + (int64_t)t * DESC_WORDS;
+    run_task<C>(a0, w, t, nxt, S);
+    if (tid == 0) S.next = (int)nxt;
+    __syncthreads();
+  }
+  exit_step(a, S);
+}
 
-extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(mk::mk_persistent, dim3(grid), dim3(mk::NT), 0, stream, *a);
+}  // namespace mk
+// Compiled shape classes: (d_head, group, d_model bound, d_ffn bound, group*d_head bound).
+using CfgFull = mk::Cfg<128, 8, 4, 2, 2>;  // d_head 128, group 8, d_model <= 2048, d_ffn <= 1024, group*d_head = 1024
+using CfgTiny = mk::Cfg<64, 2, 1, 1, 1>;   // d_head 64, group 2, d_model <= 512, d_ffn <= 512, group*d_head = 128
+
+extern "C" int mk_kernel_class(int d_head, int group, int d_model, int d_ffn) {
+  if (d_head == 128 && group == 8 && d_model <= 64 * 8 * CfgFull::NVD && d_ffn <= 64 * 8 * CfgFull::NVF) return 1;
+  if (d_head == 64 && group == 2 && d_model <= 64 * 8 * CfgTiny::NVD && d_ffn <= 64 * 8 * CfgTiny::NVF) return 2;
+  return 0;
+}
+
+extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int kclass, int grid, hipStream_t stream) {
+  if (kclass == 1) hipLaunchKernelGGL(mk::mk_persistent<CfgFull>, dim3(grid), dim3(mk::NT), 0, stream, *a);
+  else if (kclass == 2) hipLaunchKernelGGL(mk::mk_persistent<CfgTiny>, dim3(grid), dim3(mk::NT), 0, stream, *a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -85,7 +85,7 @@ Tiling choose_tiling(const mk_model_desc* d) {
   t.n_qkv_per_group = (d->n_q_heads / d->n_kv_heads + 2) * d->d_head / t.qkv_rows;
   t.router_rows = std::min(d->n_experts, 16);
   t.n_router = (d->n_experts + t.router_rows - 1) / t.router_rows;
-  t.up_rows = 32;
+  t.up_rows = 16;
   t.n_up = d->d_ffn / t.up_rows;
   t.lm_rows = 128;
   t.n_lm = (d->vocab + t.lm_rows - 1) / t.lm_rows;
@@ -167,7 +167,9 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
       w[W_R0] = i * t.router_rows;
       w[W_R1] = std::min(E, (i + 1) * t.router_rows);
       set_wait(w, 0, cl.xready + l, t.n_rt);
-      set_sig(w, cl.router_done + l);
+      set_sig(w, cl.router_done + l);  // issued only by the tile that arrives last, after it routed the layer
+      w[W_ARR] = cl.router_arrive + l;
+      w[W_ARRN] = t.n_router;
     }
     for (int g = 0; g < Hkv; ++g)
       for (int i = 0; i < t.n_qkv_per_group; ++i) {
@@ -197,7 +199,7 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
         w[W_A] = s;
         w[W_R0] = i * t.up_rows;
         w[W_R1] = (i + 1) * t.up_rows;
-        set_wait(w, 0, cl.router_done + l, t.n_router);
+        set_wait(w, 0, cl.router_done + l, 1);
         set_sig(w, cl.up_done + l * P->n_slots + s);
       }
     for (int g = 0; g < Hkv; ++g)
@@ -215,7 +217,7 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
         w[W_A] = s;
         w[W_R0] = r * t.rt;
         w[W_R1] = (r + 1) * t.rt;
-        set_wait(w, 0, cl.router_done + l, t.n_router);             // routing known: expert weights can stream
+        set_wait(w, 0, cl.router_done + l, 1);                      // routing known: expert weights can stream
         set_wait(w, 1, cl.up_done + l * P->n_slots + s, t.n_up);    // this expert's hidden state is complete
         set_sig(w, cl.resid_in + l * t.n_rt + r);
       }

@@ -23,7 +23,7 @@ def step_bytes(shape, ctx_lens, unique_experts_per_layer, n_unique_tokens):
     per_layer_fixed = s.layer_attn_bytes() + s.router_bytes() + 2 * s.d_model
     w = sum(per_layer_fixed + u * s.expert_bytes() for u in unique_experts_per_layer)
     w += 2 * s.vocab * s.d_model + 2 * s.d_model + 2 * s.d_model * n_unique_tokens
-    kv = sum((c + 1) * s.kv_bytes_per_pos_layer() * s.n_layers for c in ctx_lens)
+    kv = sum((int(c) + 1) * s.kv_bytes_per_pos_layer() * s.n_layers for c in ctx_lens)
     return w + kv
 
 

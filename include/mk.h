@@ -128,14 +128,17 @@ int mk_next_tokens(mk_model* m, int32_t** dev_ptr);
 int mk_status(mk_model* m, void* stream);
 
 /* Debug switches (bit flags, MK_DBG_*) and read-back of the handle's debug buffers. */
-enum { MK_DBG_DUMP_N = 1 };
+enum { MK_DBG_DUMP_N = 1, MK_DBG_TIMESTAMPS = 2 };
 enum {
   MK_DBGK_ROUTE_SEL = 1,     /* int32 [n_layers][batch][top_k]: last step's expert selection (always recorded) */
   MK_DBGK_ROUTE_GATE = 2,    /* fp32  [n_layers][batch][top_k]: its gates (always recorded) */
   MK_DBGK_ROUTER_LOGITS = 3, /* fp32  [n_layers][batch][n_experts] (always recorded) */
   MK_DBGK_NORM_IN = 4,       /* fp32  [n_layers][batch][d_model]: each layer's RMSNorm output (MK_DBG_DUMP_N) */
   MK_DBGK_COUNTERS = 5,      /* uint32 [n_counters] as left by the last step (all zero after a clean step) */
-  MK_DBGK_TASK_DONE = 6      /* uint32 [n_tasks]: completions per task in the last step (must be 1 each) */
+  MK_DBGK_TASK_DONE = 6,     /* uint32 [n_tasks]: completions per task in the last step (must be 1 each) */
+  MK_DBGK_TIMESTAMPS = 7     /* uint64 [n_tasks][8]: claim, dependencies met, end (100 MHz wall clock), hardware id
+                                (XCC id << 32 | HW_ID register), then up to 4 task-specific sub-phase marks (0 = unset);
+                                MK_DBG_TIMESTAMPS */
 };
 int mk_debug_set(mk_model* m, uint32_t flags);
 /* Copies `bytes` of debug buffer `kind` to host memory; synchronises the device first.
