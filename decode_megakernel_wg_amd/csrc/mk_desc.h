@@ -9,14 +9,14 @@
 namespace mk {
 
 enum Op : int32_t {
-  OP_EMBED = 1,   // x[b][rows] = embed[token_b][rows]; partial sum of squares            -> XREADY[0]
+  OP_EMBED = 1,   // x[b][rows] = embed[token_b][rows]; partial sum of squares; last tile publishes n_0 -> XREADY[0]
   OP_ROUTER = 2,  // router logits for experts [r0, r1) (fp64 accumulation); the last tile routes -> ROUTER_DONE[l]
   OP_QKV = 3,     // rows [r0, r1) of KV group g's fused [q heads; k; v] projection     -> QKV_DONE[l][g]
   OP_ATTN = 4,    // split s of (sequence b, KV group g): partial softmax(qK^T)V; last arriver combines -> ATTN_DONE[l][g]
   OP_UP = 5,      // gate+up rows [r0, r1) of expert slot s, SwiGLU                      -> UP_DONE[l][s]
-  OP_OPROJ = 6,   // rows [r0, r1) of Wo restricted to group g's columns                -> RESID_IN[l][tile]
-  OP_DOWN = 7,    // rows [r0, r1) of expert slot s's down projection, times the gate   -> RESID_IN[l][tile]
-  OP_RESID = 8,   // x += sum of branch partials on rows [r0, r1); partial sum of squares -> XREADY[l+1]
+  OP_OPROJ = 6,   // rows [r0, r1) of Wo restricted to group g's columns; residual epilogue (see below)
+  OP_DOWN = 7,    // rows [r0, r1) of expert slot s's down projection, times the gate; residual epilogue
+  OP_RESID = 8,   // (reserved: the residual add is the epilogue of the last O-proj / down task of a row tile)
   OP_LMHEAD = 9,  // logits for vocab rows [r0, r1); tile argmax; last arriver picks the next tokens
   OP_COUNT = 10
 };
@@ -36,6 +36,9 @@ enum Word : int {
   W_SIGN = 17,  // increment
   W_ARR = 18,   // arrival counter for the last-arriver epilogue (-1 = none)
   W_ARRN = 19,  // arrivals expected
+  W_ARR2 = 20,  // second-level arrival counter (-1 = none): row tiles of the residual stream
+  W_ARRN2 = 21, // arrivals expected there
+  W_RT = 22,    // residual row tile of OPROJ / DOWN / EMBED tasks
   W_SEQ = 31    // task index (debug)
 };
 constexpr int N_WAITS = 4;
@@ -49,7 +52,8 @@ constexpr int SLOT_WORDS = 32;  // routing table entry per expert slot: expert, 
 
 // Counter index layout for a model/batch; computed identically by planner and host launcher.
 struct CounterLayout {
-  int32_t ticket, done, xready, qkv_done, router_arrive, router_done, attn_arrive, attn_done, up_done, resid_in, lm_arrive, total;
+  int32_t ticket, done, xready, qkv_done, router_arrive, router_done, attn_arrive, attn_done, up_done, resid_arrive, norm_arrive,
+      lm_arrive, total;
   int32_t n_layers, n_kv, n_slots, n_row_tiles, batch;
   void build(int L, int Hkv, int B, int slots, int nrt) {
     n_layers = L;
@@ -67,7 +71,8 @@ struct CounterLayout {
     attn_arrive = o; o += L * B * Hkv;
     attn_done = o; o += L * Hkv;
     up_done = o; o += L * slots;
-    resid_in = o; o += L * nrt;
+    resid_arrive = o; o += L * nrt;
+    norm_arrive = o; o += L + 1;
     lm_arrive = o; o += 1;
     total = (o + 31) & ~31;
   }

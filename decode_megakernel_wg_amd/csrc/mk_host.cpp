@@ -59,6 +59,8 @@ struct mk_model {
   int32_t* tasks = nullptr;
   uint32_t* ctr = nullptr;
   uint32_t* err = nullptr;
+  uint32_t* nhl = nullptr;
+  float *nbuf = nullptr;
   float *x = nullptr, *ssq = nullptr, *rope_cs = nullptr, *qkv = nullptr, *apart = nullptr, *attn_o = nullptr, *opart = nullptr;
   float *rlogits = nullptr, *route_gate = nullptr, *h = nullptr, *ypart = nullptr, *lmbest_v = nullptr, *dump_n = nullptr;
   int32_t *route_sel = nullptr, *lmbest_i = nullptr, *next_tok = nullptr, *slots = nullptr;
@@ -176,7 +178,8 @@ int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out
       (rc = m->alloc(&m->ypart, (size_t)maxB * k * d)) || (rc = m->alloc(&m->lmbest_v, (size_t)maxB * t.n_lm)) ||
       (rc = m->alloc(&m->lmbest_i, (size_t)maxB * t.n_lm)) || (rc = m->alloc(&m->next_tok, maxB)) ||
       (rc = m->alloc(&m->ctr_snapshot, m->max_counters)) ||
-      (rc = m->alloc(&m->slots, (size_t)L * m->max_slots * mk::SLOT_WORDS)))
+      (rc = m->alloc(&m->slots, (size_t)L * m->max_slots * mk::SLOT_WORDS)) ||
+      (rc = m->alloc(&m->nbuf, (size_t)maxB * d)) || (rc = m->alloc(&m->nhl, (size_t)maxB * d)))
     return cleanup(rc);
   if (hipHostMalloc((void**)&m->staging, (size_t)m->max_tasks * mk::DESC_WORDS * sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
     m->staging = nullptr;
@@ -265,6 +268,8 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   a.err = m->err;
   a.x = m->x;
   a.ssq = m->ssq;
+  a.nbuf = m->nbuf;
+  a.nhl = m->nhl;
   a.rope_cs = m->rope_cs;
   a.qkv = m->qkv;
   a.apart = m->apart;

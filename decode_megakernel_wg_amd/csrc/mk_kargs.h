@@ -47,6 +47,8 @@ struct KArgs {
   uint32_t* err;
   float* x;          // [B][d] residual stream
   float* ssq;        // [B][n_rt] partial sums of squares of x per row tile
+  float* nbuf;       // [B][d] normalised input of the current layer (fp32)
+  uint32_t* nhl;     // [2][B][d/2] the same split into BF16 hi (first half) and lo parts, two values per word
   float* rope_cs;    // [B][dh/2][2] cos, sin of the new position
   float* qkv;        // [B][Hkv][(grp+2)*dh] projections (q heads of the group, then k, then v)
   float* apart;      // [B][Hkv][ATTN_MAX_SPLITS][grp][dh+2] attention split partials (o, m, l)

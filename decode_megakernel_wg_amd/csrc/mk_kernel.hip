@@ -29,20 +29,18 @@ namespace mk {
 
 constexpr int NT = 512;          // threads per workgroup
 constexpr int NW = NT / 64;      // waves per workgroup
-constexpr int XS_FLOATS = 32768; // 128 KB LDS staging area
+constexpr int XS_FLOATS = 16384; // 64 KB LDS staging area (fp32 activations, attention scratch)
+constexpr int XBP = 2048 + 8;     // bf16 row pitch of the split activations (the 16-byte skew spreads rows over banks)
+constexpr int NKP = 16;           // MFMA k-steps (32 K values each) per pass and wave
 constexpr uint32_t SPIN_LIMIT = 1u << 21;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 template <int N, int R>
 struct NVR {
   static constexpr int nv = N, rpw = R;
-};
-// Rows per wave per GEMV pass for NV 16-byte vectors per row and lane (passes hold 4-8 vectors per lane).
-template <int NV>
-struct RpwOf {
-  static constexpr int value = NV == 1 ? 4 : NV == 2 ? 4 : NV == 4 ? 2 : 1;
 };
 // A compiled shape class of the kernel: head dim, GQA group, and the 16-byte-vector counts per lane of
 // the three GEMV reduction lengths (d_model, d_ffn, group * d_head).  One kernel is instantiated per
@@ -65,8 +63,9 @@ typedef const __attribute__((address_space(4))) KArgs KA;
 
 struct Lds {
   float xs[XS_FLOATS];   // activation staging (GEMV inputs), attention reduction scratch
+  uint16_t xb[16 * XBP]; // GEMV inputs split into BF16 hi (rows 0..7) and lo (rows 8..15) parts
   float q[8 * 128];      // attention: RoPE'd, scaled queries of one KV group
-  float sc[8 * 256];     // attention: scores of one chunk [head][position]
+  float sc[8 * 128];     // attention: scores of one chunk [head][position]; LM head: tile logits [row][token]
   float pt[256 * 8];     // attention: probabilities of one chunk [position][head]
   int pages[ATTN_MAX_SPLIT_PAGES];  // attention: physical pages of the split
   float kn[128], vn[128];// attention: the new token's K and V (BF16-rounded)
@@ -74,8 +73,6 @@ struct Lds {
   float inv[8];          // per-token RMSNorm scale
   float ssqv[8 * 32];    // per-token partial sums of squares (row tiles)
   float gu[2 * 32 * 8];  // UP: gate/up values [row][token]
-  float bestv[8 * NW];
-  int besti[8 * NW];
   // routing of the current layer
   int sel[8 * 8];
   float gate[8 * 8];
@@ -303,60 +300,221 @@ __device__ __forceinline__ double dot8d(u4 w, const f4& x0, const f4& x1, double
   return acc;
 }
 
-// Computes one pass and hands every (row, b) sum to out(row, b, value) on lane 0 of the owning wave.
-template <int NV, int RPW, int NB, class Out>
-__device__ __forceinline__ void gemv_compute(const WBuf<NV, RPW>& buf, const float* xs, int xp, int nb, int nrows, int K8, int pass,
-                                             Out& out, int b0) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row0 = pass * NW * RPW + wave * RPW;
-  float acc[RPW][NB];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int c8 = lane + 64 * i;
-    if (c8 < K8) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const f4 x0 = *reinterpret_cast<const f4*>(xs + (b0 + b) * xp + c8 * 8);
-        const f4 x1 = *reinterpret_cast<const f4*>(xs + (b0 + b) * xp + c8 * 8 + 4);
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) acc[r][b] = dot8(buf.v[r][i], x0, x1, acc[r][b]);
-      }
-    }
+// The layer's normalised input, as published once per layer (see publish_norm): fp32 rows into S.xs
+// (pitch d) or BF16 hi/lo rows straight into S.xb, for staging rows j < nb from tokens tok[j].
+__device__ __forceinline__ void stage_n32(KA& a, int nb, const int* tok, Lds& S) {
+  const int d = a.d;
+  for (int i = threadIdx.x; i < nb * d; i += NT) {
+    const int j = i / d, c = i - j * d;
+    S.xs[i] = a.nbuf[(tok ? tok[j] : j) * d + c];
   }
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int row = row0 + r;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float s = wave_sum(acc[r][b]);
-      if (row < nrows && b0 + b < nb && lane == 0) out(row, b0 + b, s);
+  __syncthreads();
+}
+__device__ __forceinline__ void stage_nhl(KA& a, int nb, const int* tok, Lds& S) {
+  const int d2 = a.d >> 1;
+  const uint32_t* lo = a.nhl + (int64_t)a.B * d2;
+  for (int i = threadIdx.x; i < nb * d2; i += NT) {
+    const int j = i / d2, c = i - j * d2;
+    const int b = tok ? tok[j] : j;
+    *reinterpret_cast<uint32_t*>(S.xb + j * XBP + 2 * c) = a.nhl[b * d2 + c];
+    *reinterpret_cast<uint32_t*>(S.xb + (8 + j) * XBP + 2 * c) = lo[b * d2 + c];
+  }
+  __syncthreads();
+}
+
+// Residual rows [r0, r1): x += sum over KV groups of the O-projection partials + sum over the k selections
+// of the gated expert outputs (fixed order); partial sum of squares of the new rows into ssq[b][rt].
+__device__ __forceinline__ void resid_rows(KA& a, int r0, int r1, int rt) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int d = a.d, B = a.B;
+  if (wave < B) {
+    const int b = wave;
+    float acc = 0.f;
+    for (int r = r0 + lane; r < r1; r += 64) {
+      float v = a.x[b * d + r];
+      for (int g = 0; g < a.Hkv; ++g) v += a.opart[((int64_t)g * B + b) * d + r];
+      for (int j = 0; j < a.k; ++j) v += a.ypart[((int64_t)b * a.k + j) * d + r];
+      pub(&a.x[b * d + r], v);
+      acc = fmaf(v, v, acc);
+    }
+    const float s = wave_sum(acc);
+    if (lane == 0) pub(&a.ssq[b * a.n_rt + rt], s);
+  }
+}
+
+// The next layer's RMSNorm over the complete residual stream: n = x * gamma / sqrt(mean(x^2) + eps), gamma
+// of layer lnext (the final norm after the last layer), published as fp32 and as BF16 hi + lo parts.
+__device__ __forceinline__ void publish_norm(KA& a, int lnext, Lds& S) {
+  const int d = a.d, B = a.B, nrt = a.n_rt, d2 = d >> 1;
+  const uint16_t* gamma = lnext < a.L ? a.layers[lnext].attn_norm : a.final_norm;
+  if (threadIdx.x < B) {
+    float ss = 0.f;
+    for (int r = 0; r < nrt; ++r) ss += a.ssq[threadIdx.x * nrt + r];
+    S.inv[threadIdx.x] = 1.0f / sqrtf(ss / (float)d + a.eps);
+  }
+  __syncthreads();
+  uint32_t* lo = a.nhl + (int64_t)B * d2;
+  float* dump = (a.dump_n && lnext < a.L) ? a.dump_n + (int64_t)lnext * B * d : nullptr;
+  for (int i = threadIdx.x; i < B * d2; i += NT) {
+    const int b = i / d2, c = 2 * (i - b * d2);
+    const float inv = S.inv[b];
+    const float n0 = a.x[b * d + c] * bf2f(gamma[c]) * inv;
+    const float n1 = a.x[b * d + c + 1] * bf2f(gamma[c + 1]) * inv;
+    pub(&a.nbuf[b * d + c], n0);
+    pub(&a.nbuf[b * d + c + 1], n1);
+    const uint16_t h0 = f2bf(n0), h1 = f2bf(n1);
+    pubi(reinterpret_cast<int32_t*>(&a.nhl[i]), (int32_t)(h0 | ((uint32_t)h1 << 16)));
+    pubi(reinterpret_cast<int32_t*>(&lo[i]), (int32_t)(f2bf(n0 - bf2f(h0)) | ((uint32_t)f2bf(n1 - bf2f(h1)) << 16)));
+    if (dump) {
+      dump[b * d + c] = n0;
+      dump[b * d + c + 1] = n1;
     }
   }
 }
 
-// Drive a whole tile: pass 0 is in buf0 and, when the tile has more passes, pass 1 is in buf1.
-template <int NV, int RPW, int NB, class RowPtr, class Out>
-__device__ __forceinline__ void gemv_run2(WBuf<NV, RPW>& buf0, WBuf<NV, RPW>& buf1, const RowPtr& W, int nrows, int K, const float* xs,
-                                          int xp, int nb, Out& out) {
-  const int K8 = K >> 3;
-  const int np = (nrows + NW * RPW - 1) / (NW * RPW);
-  for (int p = 0; p < np; p += 2) {
-    for (int b0 = 0; b0 < nb; b0 += NB) gemv_compute<NV, RPW, NB>(buf0, xs, xp, nb, nrows, K8, p, out, b0);
-    if (p + 2 < np) gemv_load(buf0, W, nrows, K8, p + 2);
-    if (p + 1 >= np) break;
-    for (int b0 = 0; b0 < nb; b0 += NB) gemv_compute<NV, RPW, NB>(buf1, xs, xp, nb, nrows, K8, p + 1, out, b0);
-    if (p + 3 < np) gemv_load(buf1, W, nrows, K8, p + 3);
+// End of a task that produced rows of the residual stream: the last row tile of the layer publishes the
+// next layer's normalised input and signals that layer's consumers.
+__device__ __forceinline__ void norm_chain(KA& a, const int32_t* w, int lnext, Lds& S) {
+  if (arrive_last(a, w[W_ARR2], w[W_ARRN2], S)) {
+    publish_norm(a, lnext, S);
+    signal(a, w[W_SIG], w[W_SIGN]);
   }
 }
-template <int NV, int RPW, int NB, class RowPtr, class Out>
-__device__ __forceinline__ void gemv_run(WBuf<NV, RPW>& buf0, const RowPtr& W, int nrows, int K, const float* xs, int xp, int nb, Out& out) {
-  WBuf<NV, RPW> buf1;
-  if (nrows > NW * RPW) gemv_load(buf1, W, nrows, K >> 3, 1);
-  gemv_run2<NV, RPW, NB>(buf0, buf1, W, nrows, K, xs, xp, nb, out);
+// End of an O-proj / expert-down task: the last producer of the row tile adds the partials into x.
+__device__ __forceinline__ void resid_chain(KA& a, const int32_t* w, int l, Lds& S) {
+  if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) {
+    resid_rows(a, w[W_R0], w[W_R1], w[W_RT]);
+    norm_chain(a, w, l + 1, S);
+  }
+}
+
+// ------------------------------------------------------------------------------------------ MFMA GEMV core
+// A tile of nrows x K BF16 weights times nb <= 8 activation vectors, on v_mfma_f32_16x16x32_bf16: the
+// weights are the A operand as loaded (16 rows x 32 K per instruction, no conversion), the activations
+// the B operand with token j in column j, split into BF16 hi + lo parts (two MFMAs, ~16 mantissa bits,
+// fp32 accumulation).  The reduction over K happens inside the MFMA; wave w owns row block w / ks and
+// K-slice w % ks, and the ks partials of a row block are summed in a fixed order through LDS.
+// Operand layout (checked on gfx950): lane l holds A[l%16][8(l/16)+v], B[8(l/16)+v][l%16] and
+// D[4(l/16)+r][l%16].
+struct MGeo {
+  int nrows, K, rbn, ks, kw, nks, np;
+};
+__device__ __forceinline__ MGeo mgeo(int nrows, int K) {
+  MGeo g;
+  g.nrows = nrows;
+  g.K = K;
+  g.rbn = (nrows + 15) >> 4;  // row blocks (at most NW)
+  int ks = 1;
+  while (g.rbn * ks * 2 <= NW && K % (64 * ks) == 0) ks *= 2;
+  g.ks = ks;
+  g.kw = K / ks;
+  g.nks = g.kw >> 5;
+  g.np = (g.nks + NKP - 1) / NKP;
+  return g;
+}
+struct MBuf {
+  u4 v[NKP];
+};
+
+template <class RowPtr>
+__device__ __forceinline__ void mg_load(MBuf& buf, const RowPtr& W, const MGeo& g, int pass) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rb = wave / g.ks, kp = wave - rb * g.ks;
+  const int row = rb * 16 + (lane & 15);
+  const bool ok = rb < g.rbn && row < g.nrows;
+  gu4* rp = as_global(ok ? W(row) : W(0));
+  const int v0 = (kp * g.kw + 8 * (lane >> 4)) >> 3;
+#pragma unroll
+  for (int t = 0; t < NKP; ++t) {
+    const int s = pass * NKP + t;
+    buf.v[t] = (ok && s < g.nks) ? __builtin_nontemporal_load(rp + v0 + 4 * s) : u4{0, 0, 0, 0};
+  }
+}
+
+__device__ __forceinline__ void mg_compute(const MBuf& buf, f4& acc, const MGeo& g, int pass, int nb, Lds& S) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rb = wave / g.ks, kp = wave - rb * g.ks;
+  if (rb >= g.rbn) return;
+  const int j = lane & 15;
+  const bool live = j < nb;
+  const uint16_t* xh = S.xb + (live ? j : 0) * XBP;
+  const uint16_t* xl = S.xb + (live ? 8 + j : 8) * XBP;
+  const int k0 = kp * g.kw + 8 * (lane >> 4);
+#pragma unroll
+  for (int t = 0; t < NKP; ++t) {
+    const int s = pass * NKP + t;
+    if (s < g.nks) {
+      const int k = k0 + 32 * s;
+      u4 bh = *reinterpret_cast<const u4*>(xh + k);
+      u4 bl = *reinterpret_cast<const u4*>(xl + k);
+      if (!live) bh = bl = u4{0, 0, 0, 0};
+      const bf16x8 av = __builtin_bit_cast(bf16x8, buf.v[t]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bh), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl), acc, 0, 0, 0);
+    }
+  }
+}
+
+// Sum the K-slice partials of each row block (fixed order) and hand (row, token, value) to out().
+template <class Out>
+__device__ __forceinline__ void mg_finish(f4 acc, const MGeo& g, int nb, Out& out, Lds& S) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rb = wave / g.ks, kp = wave - rb * g.ks;
+  if (g.ks > 1) {
+    float* red = S.pt;  // [NW][64][4]
+    *reinterpret_cast<f4*>(red + (wave * 64 + lane) * 4) = acc;
+    __syncthreads();
+    if (kp == 0 && rb < g.rbn) {
+      f4 s4 = *reinterpret_cast<const f4*>(red + (wave * 64 + lane) * 4);
+      for (int p = 1; p < g.ks; ++p) s4 += *reinterpret_cast<const f4*>(red + ((wave + p) * 64 + lane) * 4);
+      acc = s4;
+    }
+  }
+  const int j = lane & 15, q = lane >> 4;
+  if (kp == 0 && rb < g.rbn && j < nb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = rb * 16 + 4 * q + r;
+      if (row < g.nrows) out(row, j, acc[r]);
+    }
+  }
+}
+
+// Split the staged fp32 inputs S.xs[nb][K] into BF16 hi and lo parts.
+__device__ __forceinline__ void split_x(int nb, int K, Lds& S) {
+  for (int i = threadIdx.x; i < nb * K; i += NT) {
+    const int j = i / K, c = i - j * K;
+    const float x = S.xs[i];
+    const uint16_t h = f2bf(x);
+    S.xb[j * XBP + c] = h;
+    S.xb[(8 + j) * XBP + c] = f2bf(x - bf2f(h));
+  }
+  __syncthreads();
+}
+
+// Prefetch, wait, stage, stream.  The first two passes of the tile (up to 2 x 16 KB per wave) are loaded
+// before the dependency wait [wait0, wait1), so weights stream while the inputs are still being produced.
+template <bool SPLIT, class RowPtr, class Stage, class Out>
+__device__ __forceinline__ void mgemv_task(KA& a, const int32_t* w, int t, const RowPtr& W, int nrows, int K, int nb, int wait0,
+                                           int wait1, Stage&& stage, Out&& out, Lds& S) {
+  const MGeo g = mgeo(nrows, K);
+  MBuf b0, b1;
+  mg_load(b0, W, g, 0);
+  if (g.np > 1) mg_load(b1, W, g, 1);
+  wait_deps(a, w, wait0, wait1, t);
+  stage();
+  if (SPLIT) split_x(nb, K, S);
+  mark(a, t, 0);
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < g.np; p += 2) {
+    mg_compute(b0, acc, g, p, nb, S);
+    if (p + 2 < g.np) mg_load(b0, W, g, p + 2);
+    if (p + 1 >= g.np) break;
+    mg_compute(b1, acc, g, p + 1, nb, S);
+    if (p + 3 < g.np) mg_load(b1, W, g, p + 3);
+  }
+  mg_finish(acc, g, nb, out, S);
+  mark(a, t, 1);
 }
 
 // fp64-accumulating variant for the router (products of BF16 and fp32 are exact in fp64).
@@ -409,15 +567,19 @@ __device__ __forceinline__ void route_layer(KA& a, int l, Lds& S) {
   }
   if (tid < 8) S.used[tid] = 0u;
   __syncthreads();
-  // rank of (b, e) among the token's logits
+  // rank of (b, e) among the token's logits (E is a multiple of 8: 4-wide LDS reads, unrolled)
   for (int i = tid; i < B * E; i += NT) {
     const int b = i / E, e = i - b * E;
     const float v = key[i];
     const float* kb = key + b * E;
     int rank = 0;
-    for (int q = 0; q < E; ++q) {
-      const float u = kb[q];
-      rank += (u > v) || (u == v && q < e);
+#pragma unroll 4
+    for (int q = 0; q < E; q += 4) {
+      const f4 u = *reinterpret_cast<const f4*>(kb + q);
+      rank += (u.x > v) || (u.x == v && q < e);
+      rank += (u.y > v) || (u.y == v && q + 1 < e);
+      rank += (u.z > v) || (u.z == v && q + 2 < e);
+      rank += (u.w > v) || (u.w == v && q + 3 < e);
     }
     if (rank < k) {
       S.sel[b * 8 + rank] = e;
@@ -517,55 +679,10 @@ __device__ __forceinline__ void task_embed(KA& a, const int32_t* w, int t, Lds& 
       pub(&a.rope_cs[(b * half + j) * 2 + 1], (float)sn);
     }
   }
-  signal(a, w[W_SIG], w[W_SIGN]);
-}
-
-__device__ __forceinline__ void task_resid(KA& a, const int32_t* w, int t, Lds& S) {
-  wait_deps(a, w, 0, N_WAITS, t);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r0 = w[W_R0], r1 = w[W_R1], rt = w[W_A];
-  const int d = a.d, B = a.B;
-  if (wave < B) {
-    const int b = wave;
-    float acc = 0.f;
-    for (int r = r0 + lane; r < r1; r += 64) {
-      float v = a.x[b * d + r];
-      for (int g = 0; g < a.Hkv; ++g) v += a.opart[((int64_t)g * B + b) * d + r];
-      for (int j = 0; j < a.k; ++j) v += a.ypart[((int64_t)b * a.k + j) * d + r];
-      pub(&a.x[b * d + r], v);
-      acc = fmaf(v, v, acc);
-    }
-    const float s = wave_sum(acc);
-    if (lane == 0) pub(&a.ssq[b * a.n_rt + rt], s);
-  }
-  signal(a, w[W_SIG], w[W_SIGN]);
+  norm_chain(a, w, 0, S);
 }
 
 
-// Generic "prefetch, wait, stage, stream" GEMV task.  Stage(): fills S.xs after the wait.  The first two
-// passes of the tile are loaded before the dependency wait (a one-token tile uses 16-vector passes, so up
-// to 256 KB per workgroup is in flight while its inputs are being produced).
-template <int NV>
-struct RpwBig {
-  static constexpr int value = NV == 1 ? 8 : NV == 2 ? 8 : NV == 4 ? 4 : 2;
-};
-template <int NV, int RPW, int NB, class RowPtr, class Stage, class Out>
-__device__ __forceinline__ void gemv_task_nb(KA& a, const int32_t* w, int t, const RowPtr& W, int nrows, int K, int nb, int wait0,
-                                             int wait1, Stage& stage, Out& out, Lds& S) {
-  WBuf<NV, RPW> buf0, buf1;
-  gemv_load(buf0, W, nrows, K >> 3, 0);
-  if (nrows > NW * RPW) gemv_load(buf1, W, nrows, K >> 3, 1);
-  wait_deps(a, w, wait0, wait1, t);
-  stage();
-  gemv_run2<NV, RPW, NB>(buf0, buf1, W, nrows, K, S.xs, K, nb, out);
-}
-template <int NV, class RowPtr, class Stage, class Out>
-__device__ __forceinline__ void gemv_task(KA& a, const int32_t* w, int t, const RowPtr& W, int nrows, int K, int nb, int wait0, int wait1,
-                                          Stage&& stage, Out&& out, Lds& S) {
-  if (nb <= 1) gemv_task_nb<NV, RpwBig<NV>::value, 1>(a, w, t, W, nrows, K, nb, wait0, wait1, stage, out, S);
-  else if (nb <= 2) gemv_task_nb<NV, RpwOf<NV>::value, 2>(a, w, t, W, nrows, K, nb, wait0, wait1, stage, out, S);
-  else gemv_task_nb<NV, RpwOf<NV>::value, 4>(a, w, t, W, nrows, K, nb, wait0, wait1, stage, out, S);  // 5..8 tokens: two groups
-}
 
 template <class C>
 __device__ __forceinline__ void task_qkv(KA& a, const int32_t* w, int t, Lds& S) {
@@ -579,8 +696,8 @@ __device__ __forceinline__ void task_qkv(KA& a, const int32_t* w, int t, Lds& S)
   const int rows = (grp + 2) * dh;
   float* out = a.qkv + (int64_t)g * rows + r0;
   const int64_t bstride = (int64_t)a.Hkv * rows;
-  gemv_task<C::NVD>(
-      a, w, t, Rows1{W, d}, r1 - r0, d, a.B, 0, N_WAITS, [&] { stage_norm(a, L.attn_norm, a.B, nullptr, S); },
+  mgemv_task<false>(
+      a, w, t, Rows1{W, d}, r1 - r0, d, a.B, 0, N_WAITS, [&] { stage_nhl(a, a.B, nullptr, S); },
       [&](int r, int b, float v) { pub(out + b * bstride + r, v); }, S);
   signal(a, w[W_SIG], w[W_SIGN]);
 }
@@ -598,9 +715,7 @@ __device__ __forceinline__ void task_router(KA& a, const int32_t* w, int t, Lds&
     WBuf<NV, RPW> buf0;
     gemv_load(buf0, Rows1{W, d}, nrows, K8, 0);
     wait_deps(a, w, 0, N_WAITS, t);
-    stage_norm(a, L.attn_norm, a.B, nullptr, S);
-    if (a.dump_n && r0 == 0)
-      for (int i = threadIdx.x; i < a.B * d; i += NT) a.dump_n[(int64_t)l * a.B * d + i] = S.xs[i];
+    stage_n32(a, a.B, nullptr, S);
     const int nb = a.B;
     if (nb <= 1) gemv_run_f64<NV, RPW, 1>(buf0, nrows, d, S.xs, d, nb, out);
     else if (nb <= 2) gemv_run_f64<NV, RPW, 2>(buf0, nrows, d, S.xs, d, nb, out);
@@ -621,7 +736,7 @@ __device__ __forceinline__ void task_oproj(KA& a, const int32_t* w, int t, Lds& 
   const int grp = a.Hq / a.Hkv, K = grp * a.dh, ldo = a.Hq * a.dh, B = a.B, d = a.d;
   const uint16_t* W = a.layers[l].wo + (int64_t)r0 * ldo + (int64_t)g * K;
   float* out = a.opart + (int64_t)g * B * d + r0;
-  gemv_task<C::NVO>(
+  mgemv_task<true>(
       a, w, t, Rows1{W, ldo}, r1 - r0, K, B, 0, N_WAITS,
       [&] {
         for (int i = threadIdx.x; i < B * K; i += NT) {
@@ -631,7 +746,7 @@ __device__ __forceinline__ void task_oproj(KA& a, const int32_t* w, int t, Lds& 
         __syncthreads();
       },
       [&](int r, int b, float v) { pub(out + (int64_t)b * d + r, v); }, S);
-  signal(a, w[W_SIG], w[W_SIGN]);
+  resid_chain(a, w, l, S);
 }
 
 template <class C>
@@ -645,19 +760,11 @@ __device__ __forceinline__ void task_up(KA& a, const int32_t* w, int t, Lds& S) 
     // gate rows then up rows of this tile, as one 2*nr-row tile (two bases)
     const uint16_t* Wg = L.w_gate + ((int64_t)e * F + r0) * d;
     const uint16_t* Wu = L.w_up + ((int64_t)e * F + r0) * d;
-    const Rows2 rows{Wg, Wu, d, nr};
-    auto out = [&](int r, int b, float v) { S.gu[r * 8 + b] = v; };
-    auto run = [&](auto nvr, auto nbc) {
-      constexpr int NV = decltype(nvr)::nv, RPW = decltype(nvr)::rpw, NB = decltype(nbc)::value;
-      WBuf<NV, RPW> b0, b1;
-      gemv_load(b0, rows, 2 * nr, d >> 3, 0);  // the expert's weights stream while its inputs are staged
-      if (2 * nr > NW * RPW) gemv_load(b1, rows, 2 * nr, d >> 3, 1);
-      stage_norm(a, L.attn_norm, n, S.slot_b, S);
-      gemv_run2<NV, RPW, NB>(b0, b1, rows, 2 * nr, d, S.xs, d, n, out);
-    };
-    if (n <= 1) run(NVR<C::NVD, RpwBig<C::NVD>::value>{}, std::integral_constant<int, 1>{});
-    else if (n <= 2) run(NVR<C::NVD, RpwOf<C::NVD>::value>{}, std::integral_constant<int, 2>{});
-    else run(NVR<C::NVD, RpwOf<C::NVD>::value>{}, std::integral_constant<int, 4>{});
+    // gate rows then up rows of this tile, one 2*nr-row tile over two bases; the expert is known only now,
+    // so its weights stream while the slot's inputs are staged
+    mgemv_task<false>(
+        a, w, t, Rows2{Wg, Wu, d, nr}, 2 * nr, d, n, 0, 0, [&] { stage_nhl(a, n, S.slot_b, S); },
+        [&](int r, int b, float v) { S.gu[r * 8 + b] = v; }, S);
     __syncthreads();
     for (int i = threadIdx.x; i < nr * n; i += NT) {
       const int r = i / n, j = i - r * n;
@@ -677,7 +784,7 @@ __device__ __forceinline__ void task_down(KA& a, const int32_t* w, int t, Lds& S
   if (load_slot(a, l, s, S)) {
     const int e = S.slot_e, n = S.slot_n;
     const uint16_t* W = a.layers[l].w_down + ((int64_t)e * d + r0) * F;
-    gemv_task<C::NVF>(
+    mgemv_task<true>(
         a, w, t, Rows1{W, F}, nr, F, n, 1, N_WAITS,
         [&] {
           for (int i = threadIdx.x; i < n * F; i += NT) S.xs[i] = a.h[(int64_t)s * a.B * F + i];
@@ -687,7 +794,7 @@ __device__ __forceinline__ void task_down(KA& a, const int32_t* w, int t, Lds& S
   } else {
     wait_deps(a, w, 1, N_WAITS, t);
   }
-  signal(a, w[W_SIG], w[W_SIGN]);
+  resid_chain(a, w, l, S);
 }
 
 template <class C>
@@ -696,38 +803,38 @@ __device__ __forceinline__ void task_lmhead(KA& a, const int32_t* w, int t, Lds&
   const int d = a.d, B = a.B, nr = r1 - r0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint16_t* W = a.lm_head + (int64_t)r0 * d;
-  if (threadIdx.x < 8 * NW) {
-    S.bestv[threadIdx.x] = -INFINITY;
-    S.besti[threadIdx.x] = 0x7fffffff;
-  }
-  // each wave keeps its own running best per token (rows are visited in increasing order per wave)
-  gemv_task<C::NVD>(
-      a, w, t, Rows1{W, d}, nr, d, B, 0, N_WAITS, [&] { stage_norm(a, a.final_norm, B, nullptr, S); },
+  float* tl = S.sc;  // this tile's logits [row][token], row < 128
+  mgemv_task<false>(
+      a, w, t, Rows1{W, d}, nr, d, B, 0, N_WAITS, [&] { stage_nhl(a, B, nullptr, S); },
       [&](int r, int b, float v) {
         a.logits[(int64_t)b * a.V + r0 + r] = v;
-        float& bv = S.bestv[b * NW + wave];
-        int& bi = S.besti[b * NW + wave];
-        if (v > bv || (v == bv && r0 + r < bi)) {
-          bv = v;
-          bi = r0 + r;
-        }
+        tl[r * 8 + b] = v;
       },
       S);
   __syncthreads();
-  if (threadIdx.x < B) {
-    const int b = threadIdx.x;
+  if (wave < B) {  // tile maximum per token, lowest index among equals
+    const int b = wave;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int q = 0; q < NW; ++q) {
-      const float v = S.bestv[b * NW + q];
-      const int i = S.besti[b * NW + q];
-      if (v > bv || (v == bv && i < bi)) {
+    for (int r = lane; r < nr; r += 64) {
+      const float v = tl[r * 8 + b];
+      if (v > bv) {
         bv = v;
-        bi = i;
+        bi = r0 + r;
       }
     }
-    pub(&a.lmbest_v[b * a.n_lm + tile], bv);
-    pubi(&a.lmbest_i[b * a.n_lm + tile], bi);
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) {
+      pub(&a.lmbest_v[b * a.n_lm + tile], bv);
+      pubi(&a.lmbest_i[b * a.n_lm + tile], bi);
+    }
   }
   if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) {
     if (wave < B) {
@@ -765,11 +872,13 @@ __device__ __forceinline__ void task_lmhead(KA& a, const int32_t* w, int t, Lds&
 // p * V for its slice and positions.  The per-thread partial outputs are reduced once per split.
 template <int DH, int GRP>
 __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& S) {
-  constexpr int DPT = 4;            // dims per thread slice
+  constexpr int DPT = 4;            // V / output dims per thread slice
   constexpr int SL = DH / DPT;      // slices per position (32 or 16)
-  constexpr int PPP = NT / SL;      // positions per pass (16 or 32)
-  constexpr int CH = 128;           // positions per chunk
-  constexpr int NP = CH / PPP;      // positions per thread per chunk (8 or 4)
+  constexpr int PPP = NT / SL;      // positions per V pass (16 or 32)
+  constexpr int CH = 128;           // positions per chunk: 8 waves x 16-position MFMA blocks
+  constexpr int NP = CH / PPP;      // V positions per thread per chunk (8 or 4)
+  constexpr int NKK = DH / 32;      // MFMA k-steps over the head dim
+  static_assert(CH == NW * 16, "one 16-position score block per wave");
   const int l = w[W_LAYER], b = w[W_A], g = w[W_B], s = w[W_C], nsplit = w[W_D];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sl = tid % SL, pp = tid / SL;
@@ -804,36 +913,56 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
     S.pages[i] = ph;
   }
   __syncthreads();
-  auto load_chunk = [&](int c0, u2 (&kk)[NP], u2 (&vv)[NP]) {
+  auto kv_base = [&](int pos) -> int64_t {
+    const int ph = S.pages[(pos >> 4) - np0];
+    return ph < 0 ? -1 : (((int64_t)ph * 2) * Hkv + g) * 16 * DH + (pos & 15) * DH;
+  };
+  // K in the MFMA A-operand layout (16 positions per wave, 8 dims per lane and k-step); V in 4-dim slices
+  auto load_chunk = [&](int c0, u4 (&kk)[NKK], u2 (&vv)[NP]) {
+    {
+      const int pos = c0 + 16 * wave + (lane & 15);
+      int64_t base = pos < jc1 ? kv_base(pos) : -1;
+#pragma unroll
+      for (int q = 0; q < NKK; ++q)
+        kk[q] = base >= 0 ? __builtin_nontemporal_load(as_global(kvl + base + 8 * (lane >> 4) + 32 * q)) : u4{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int pos = c0 + pp + PPP * i;
-      kk[i] = vv[i] = u2{0, 0};
-      if (pos < jc1) {
-        const int ph = S.pages[(pos >> 4) - np0];
-        if (ph >= 0) {
-          const int64_t base = (((int64_t)ph * 2) * Hkv + g) * 16 * DH + (pos & 15) * DH + sl * DPT;
-          kk[i] = __builtin_nontemporal_load(as_global2(kvl + base));
-          vv[i] = __builtin_nontemporal_load(as_global2(kvl + base + vstride));
-        }
-      }
+      const int64_t base = pos < jc1 ? kv_base(pos) : -1;
+      vv[i] = base >= 0 ? __builtin_nontemporal_load(as_global2(kvl + base + vstride + sl * DPT)) : u2{0, 0};
     }
   };
-  u2 kc[NP], vc[NP];
+  u4 kc[NKK];
+  u2 vc[NP];
   load_chunk(j0, kc, vc);  // old K/V stream while this step's projections are produced
 
   wait_deps(a, w, 0, N_WAITS, t);
 
-  // queries of the group: RoPE at position len, times 1/sqrt(dh)
+  // queries of the group: RoPE at position len, times 1/sqrt(dh); fp32 copy for the new token's score and
+  // BF16 hi/lo copies (heads as MFMA columns, zero columns beyond the group) for the cached positions
   const float* qsrc = a.qkv + ((int64_t)b * Hkv + g) * (GRP + 2) * DH;
   const float* cs = a.rope_cs + (int64_t)b * (DH / 2) * 2;
   const float qscale = 1.0f / sqrtf((float)DH);
+  uint16_t* qb = S.xb;  // [2][16][DH]: hi then lo
+  for (int i = tid; i < 16 * DH; i += NT) {
+    if (i >= GRP * DH) {
+      qb[i] = 0;
+      qb[16 * DH + i] = 0;
+    }
+  }
   for (int i = tid; i < GRP * DH / 2; i += NT) {
     const int h = i / (DH / 2), j = i - h * (DH / 2);
     const float c = cs[2 * j], sn = cs[2 * j + 1];
     const float x0 = qsrc[h * DH + j], x1 = qsrc[h * DH + j + DH / 2];
-    S.q[h * DH + j] = (x0 * c - x1 * sn) * qscale;
-    S.q[h * DH + j + DH / 2] = (x0 * sn + x1 * c) * qscale;
+    const float y0 = (x0 * c - x1 * sn) * qscale, y1 = (x0 * sn + x1 * c) * qscale;
+    S.q[h * DH + j] = y0;
+    S.q[h * DH + j + DH / 2] = y1;
+    const uint16_t h0 = f2bf(y0), h1 = f2bf(y1);
+    qb[h * DH + j] = h0;
+    qb[h * DH + j + DH / 2] = h1;
+    qb[16 * DH + h * DH + j] = f2bf(y0 - bf2f(h0));
+    qb[16 * DH + h * DH + j + DH / 2] = f2bf(y1 - bf2f(h1));
   }
   if (has_new) {
     for (int j = tid; j < DH / 2; j += NT) {
@@ -862,11 +991,11 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
     }
   }
   mark(a, t, 0);
-  float qr[GRP][DPT];
+  u4 qh[NKK], ql[NKK];
 #pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    const f4 q0 = *reinterpret_cast<const f4*>(S.q + h * DH + sl * DPT);
-    qr[h][0] = q0.x; qr[h][1] = q0.y; qr[h][2] = q0.z; qr[h][3] = q0.w;
+  for (int q = 0; q < NKK; ++q) {
+    qh[q] = *reinterpret_cast<const u4*>(qb + (lane & 15) * DH + 8 * (lane >> 4) + 32 * q);
+    ql[q] = *reinterpret_cast<const u4*>(qb + 16 * DH + (lane & 15) * DH + 8 * (lane >> 4) + 32 * q);
   }
   float o[GRP][DPT];
 #pragma unroll
@@ -875,21 +1004,24 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
     for (int i = 0; i < DPT; ++i) o[h][i] = 0.f;
 
   for (int c0 = j0; c0 < jc1; c0 += CH) {
-    // scores of this thread's positions, summed over the SL lanes of each position
+    u4 kn_[NKK];
+    u2 vn_[NP];
+    const bool more = c0 + CH < jc1;
+    if (more) load_chunk(c0 + CH, kn_, vn_);  // next chunk in flight while this one is processed
+    // scores on MFMA: D[position][head] = K (16 positions x 32 dims) times q^T (32 dims x heads), hi + lo
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int pl = pp + PPP * i;
-      const int pos = c0 + pl;
-      const u2 k2 = kc[i];
-      const float kf[DPT] = {bf_lo(k2.x), bf_hi(k2.x), bf_lo(k2.y), bf_hi(k2.y)};
+    for (int q = 0; q < NKK; ++q) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, kc[q]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, qh[q]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, ql[q]), acc, 0, 0, 0);
+    }
+    if ((lane & 15) < GRP) {
+      const int h = lane & 15;
 #pragma unroll
-      for (int h = 0; h < GRP; ++h) {
-        float sc = 0.f;
-#pragma unroll
-        for (int e = 0; e < DPT; ++e) sc = fmaf(qr[h][e], kf[e], sc);
-        sc = row16_sum(sc);
-        if (SL == 32) sc += swz_xor16(sc);
-        if (sl == h) S.sc[h * CH + pl] = pos < jc1 ? sc : -INFINITY;
+      for (int r = 0; r < 4; ++r) {
+        const int pl = 16 * wave + 4 * (lane >> 4) + r;
+        S.sc[h * CH + pl] = c0 + pl < jc1 ? acc[r] : -INFINITY;
       }
     }
     __syncthreads();
@@ -943,7 +1075,12 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
         for (int e = 0; e < DPT; ++e) o[h][e] = fmaf(pr[h], vf[e], o[h][e]);
     }
     __syncthreads();
-    if (c0 + CH < jc1) load_chunk(c0 + CH, kc, vc);
+    if (more) {
+#pragma unroll
+      for (int q = 0; q < NKK; ++q) kc[q] = kn_[q];
+#pragma unroll
+      for (int i = 0; i < NP; ++i) vc[i] = vn_[i];
+    }
   }
   mark(a, t, 1);
   // the new token
@@ -1084,7 +1221,6 @@ __device__ __forceinline__ void run_task(KA* a0, const int32_t* w, int t, uint32
     case OP_UP: task_up<C>(a, w, t, S); break;
     case OP_OPROJ: task_oproj<C>(a, w, t, S); break;
     case OP_DOWN: task_down<C>(a, w, t, S); break;
-    case OP_RESID: task_resid(a, w, t, S); break;
     case OP_LMHEAD: task_lmhead<C>(a, w, t, S); break;
     default:
       if (tid == 0) raise_error(a, ERRC_OPCODE, t);

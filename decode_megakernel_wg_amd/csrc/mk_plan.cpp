@@ -62,8 +62,8 @@ int validate_desc(const mk_model_desc* d, std::string* msg) {
     *msg = "n_q_heads * d_head above 8192";
     return MK_E_UNSUPPORTED;
   }
-  if (d->n_experts > 256 || d->top_k > 8 || d->top_k > d->n_experts) {
-    *msg = "n_experts <= 256 and top_k <= min(8, n_experts) required";
+  if (d->n_experts > 256 || d->n_experts % 8 || d->top_k > 8 || d->top_k > d->n_experts) {
+    *msg = "n_experts a multiple of 8, at most 256, and top_k <= min(8, n_experts) required";
     return MK_E_UNSUPPORTED;
   }
   if (d->vocab % 64) {
@@ -107,6 +107,7 @@ struct Emitter {
     }
     w[W_SIG] = -1;
     w[W_ARR] = -1;
+    w[W_ARR2] = -1;
     w[W_SEQ] = (int32_t)(o / DESC_WORDS);
     return w;
   }
@@ -118,6 +119,17 @@ void set_wait(int32_t* w, int i, int32_t c, int32_t target) {
 void set_sig(int32_t* w, int32_t c, int32_t n = 1) {
   w[W_SIG] = c;
   w[W_SIGN] = n;
+}
+// O-proj and expert-down tasks of row tile r of layer l: the last of the tile's producers adds the branch
+// partials into the residual stream (fixed order), and the last row tile of the layer publishes the next
+// layer's normalised input and signals XREADY[l+1].
+void resid_epilogue(int32_t* w, const CounterLayout& cl, const Tiling& t, int l, int r, int producers) {
+  w[W_RT] = r;
+  w[W_ARR] = cl.resid_arrive + l * t.n_rt + r;
+  w[W_ARRN] = producers;
+  w[W_ARR2] = cl.norm_arrive + l + 1;
+  w[W_ARRN2] = t.n_rt;
+  set_sig(w, cl.xready + l + 1);
 }
 }  // namespace
 
@@ -159,6 +171,9 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
     w[W_A] = r;
     w[W_R0] = r * t.rt;
     w[W_R1] = (r + 1) * t.rt;
+    w[W_RT] = r;
+    w[W_ARR2] = cl.norm_arrive + 0;  // the last embedding tile publishes the layer-0 normalised input
+    w[W_ARRN2] = t.n_rt;
     set_sig(w, cl.xready + 0);
   }
   for (int l = 0; l < L; ++l) {
@@ -166,7 +181,7 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
       int32_t* w = em.add(OP_ROUTER, l);
       w[W_R0] = i * t.router_rows;
       w[W_R1] = std::min(E, (i + 1) * t.router_rows);
-      set_wait(w, 0, cl.xready + l, t.n_rt);
+      set_wait(w, 0, cl.xready + l, 1);
       set_sig(w, cl.router_done + l);  // issued only by the tile that arrives last, after it routed the layer
       w[W_ARR] = cl.router_arrive + l;
       w[W_ARRN] = t.n_router;
@@ -177,7 +192,7 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
         w[W_A] = g;
         w[W_R0] = i * t.qkv_rows;
         w[W_R1] = (i + 1) * t.qkv_rows;
-        set_wait(w, 0, cl.xready + l, t.n_rt);
+        set_wait(w, 0, cl.xready + l, 1);
         set_sig(w, cl.qkv_done + l * Hkv + g);
       }
     for (int g = 0; g < Hkv; ++g)
@@ -209,7 +224,7 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
         w[W_R0] = r * t.rt;
         w[W_R1] = (r + 1) * t.rt;
         set_wait(w, 0, cl.attn_done + l * Hkv + g, B);
-        set_sig(w, cl.resid_in + l * t.n_rt + r);
+        resid_epilogue(w, cl, t, l, r, Hkv + P->n_slots);
       }
     for (int s = 0; s < P->n_slots; ++s)
       for (int r = 0; r < t.n_rt; ++r) {
@@ -219,23 +234,15 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
         w[W_R1] = (r + 1) * t.rt;
         set_wait(w, 0, cl.router_done + l, 1);                      // routing known: expert weights can stream
         set_wait(w, 1, cl.up_done + l * P->n_slots + s, t.n_up);    // this expert's hidden state is complete
-        set_sig(w, cl.resid_in + l * t.n_rt + r);
+        resid_epilogue(w, cl, t, l, r, Hkv + P->n_slots);
       }
-    for (int r = 0; r < t.n_rt; ++r) {
-      int32_t* w = em.add(OP_RESID, l);
-      w[W_A] = r;
-      w[W_R0] = r * t.rt;
-      w[W_R1] = (r + 1) * t.rt;
-      set_wait(w, 0, cl.resid_in + l * t.n_rt + r, Hkv + P->n_slots);
-      set_sig(w, cl.xready + l + 1);
-    }
   }
   for (int i = 0; i < t.n_lm; ++i) {
     int32_t* w = em.add(OP_LMHEAD, L);
     w[W_A] = i;
     w[W_R0] = i * t.lm_rows;
     w[W_R1] = std::min(d->vocab, (i + 1) * t.lm_rows);
-    set_wait(w, 0, cl.xready + L, t.n_rt);
+    set_wait(w, 0, cl.xready + L, 1);
     w[W_ARR] = cl.lm_arrive;
     w[W_ARRN] = t.n_lm;
   }

@@ -76,11 +76,14 @@ def test_tiny_16_steps():
     w = W.make("tiny")
     sess, orc, worst = run_parity(w, w.steps)
     print(f"tiny: worst logits rel L2 {worst:.2e}, routing near-ties {orc.near_ties}/{orc.route_checked}")
-    # KV written by the kernel equals the oracle's cache (BF16 of each new K/V; at most one BF16 step apart)
+    # KV written by the kernel equals the oracle's cache: the new K/V are BF16 roundings of fp32 values that
+    # agree to ~1e-6, so a rounding may land one step apart (more steps only for values near zero)
+    from oracle import oracle as O
+
     kv_gpu = sess.kvc.kv.view(torch.int16).cpu().numpy().view(np.uint16)
-    diff = np.abs(kv_gpu.astype(np.int32) - orc.kv.astype(np.int32))
-    assert diff.max() <= 1, f"KV cache differs by {diff.max()} BF16 steps"
-    assert (diff == 0).mean() > 0.99
+    g32, o32 = O.bf16_to_f32(kv_gpu), O.bf16_to_f32(orc.kv)
+    assert np.allclose(g32, o32, rtol=2 ** -7, atol=1e-4), f"KV cache differs: max abs {np.abs(g32 - o32).max():.3g}"
+    assert (kv_gpu == orc.kv).mean() > 0.99
 
 
 def test_tiny_ragged_batch_shuffled_pages():
