@@ -31,6 +31,36 @@ WORKLOAD_TEXT = {
 }
 
 
+def kernel_source_hash():
+    """sha256 (first 16 hex) over the persistent kernel's sources, names included, in name order."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "decode_megakernel_wg_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload):
+    """Calibrated HBM bytes per launch of the persistent kernel from the committed counter summary of this
+    workload, or None when there is none or it was taken on other kernel sources."""
+    import re
+
+    path = os.path.join(ROOT, "profiles", f"mk_persistent_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        text = fh.read()
+    h = re.search(r"Kernel source hash[^`]*`([0-9a-f]+)`", text)
+    t = re.search(r"\| traffic_bytes_per_launch \| (\d+) \|", text)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return int(t.group(1))
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -89,9 +119,10 @@ def run_gpu(workload, steps, warmup, model=None):
                 tok_s=steps * w.B / (total_ms * 1e-3), kernel_ms=sum(per) / steps)
 
 
-def cpu_baseline(workload):
-    """The CPU oracle, timed on one decode step of the same workload (all layers and the LM head), with each
-    layer's synthetic weights generated before its timed call."""
+def cpu_baseline(workload, min_seconds=10.0, max_steps=16):
+    """The CPU oracle timed on consecutive greedy decode steps of the same workload (all layers and the LM head
+    per step), until at least `min_seconds` of timed work or `max_steps` steps.  Each layer's synthetic weights
+    are generated on the host before its timed call (generation is not timed)."""
     import numpy as np
 
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -99,34 +130,39 @@ def cpu_baseline(workload):
     from oracle_runner import OracleRun
     from synth import workloads as W
 
-    w = W.make(workload, steps=1)
+    w = W.make(workload, steps=max_steps)
     pt, n_pages = W.page_tables(w)
     t0 = time.time()
     orc = OracleRun(w, pt, n_pages, keep_all=False)
     log(f"oracle setup (KV + LM head generation) {time.time() - t0:.1f} s")
     s = w.shape
-    x = O.embed(orc.D, W.host_embed_rows(s, w.tokens), np.arange(w.B, dtype=np.int32))
-    timed = 0.0
-    for l in range(s.n_layers):
-        hl = orc.layer_weights(l, [])
-        n = np.stack([O.rmsnorm(x[b], hl.arrs[0]) for b in range(w.B)])
-        need = set()
-        for b in range(w.B):
-            sel, _, _ = O.router(n[b], hl.arrs[5], s.top_k, w.router_bias)
-            need.update(int(e) for e in sel)
-        Wl = orc.layer_weights(l, sorted(need))
+    tokens = np.array(w.tokens, np.int32)
+    pos = np.array(w.ctx, np.int64)
+    timed, steps = 0.0, 0
+    while steps < max_steps and timed < min_seconds:
+        x = O.embed(orc.D, W.host_embed_rows(s, tokens), np.arange(w.B, dtype=np.int32))
+        for l in range(s.n_layers):
+            hl = orc.layer_weights(l, [])
+            n = np.stack([O.rmsnorm(x[b], hl.arrs[0]) for b in range(w.B)])
+            need = set()
+            for b in range(w.B):
+                sel, _, _ = O.router(n[b], hl.arrs[5], s.top_k, w.router_bias)
+                need.update(int(e) for e in sel)
+            Wl = orc.layer_weights(l, sorted(need))
+            t1 = time.perf_counter()
+            x, _ = O.layer(orc.D, Wl, pos, pt, orc.kv[l], x)
+            timed += time.perf_counter() - t1
         t1 = time.perf_counter()
-        x, _ = O.layer(orc.D, Wl, np.array(w.ctx, np.int64), pt, orc.kv[l], x)
+        _, nxt = O.head(orc.D, x, orc.final_norm, orc.lm_head)
         timed += time.perf_counter() - t1
-        if l % 12 == 11:
-            log(f"oracle layer {l + 1}/{s.n_layers}, timed {timed:.2f} s")
-    t1 = time.perf_counter()
-    O.head(orc.D, x, orc.final_norm, orc.lm_head)
-    timed += time.perf_counter() - t1
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(w.B / timed, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": f"one decode step of {workload} (all {s.n_layers} layers + LM head, batch {w.B}); fp64-accumulating C oracle; "
-                      f"{timed:.2f} s of timed CPU work; weight generation excluded"}
+        tokens = np.asarray(nxt, np.int32)
+        pos = pos + 1
+        steps += 1
+        log(f"oracle step {steps}: timed {timed:.2f} s")
+    cores = O.num_threads()
+    return {"value": round(steps * w.B / timed, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"{steps} consecutive greedy decode steps of {workload} (all {s.n_layers} layers + LM head, batch {w.B}); "
+                      f"fp64-accumulating C oracle with OpenMP; {timed:.2f} s of timed CPU work; host weight generation excluded"}
 
 
 def main():
@@ -171,7 +207,7 @@ def main():
         "sol_bytes_per_step": int(r["avg_bytes"]),
         "unique_experts_per_layer": int(round(sum(r["uniq"]) / len(r["uniq"]))),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
-                     "frac": round(achieved / 8000.0, 4), "traffic": None},
+                     "frac": round(achieved / 8000.0, 4), "traffic": counter_traffic(args.workload)},
     }
     if not args.no_cpu_baseline:
         del r

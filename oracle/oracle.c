@@ -29,6 +29,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 float or_bf16_to_f32(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
@@ -299,4 +302,12 @@ int or_decode_step(const or_dims* D, const or_layer_w* layers, const uint16_t* e
   if (rc == 0) or_head(D, x, B, final_norm, lm_head, logits, next);
   free(x);
   return rc;
+}
+
+int or_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }

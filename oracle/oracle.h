@@ -103,6 +103,9 @@ int or_decode_step(const or_dims* D, const or_layer_w* layers, const uint16_t* e
                    int64_t n_pages, float* logits, int32_t* next, int32_t* sel_out, float* gate_out, float* n_out);
 
 /* BF16 helpers (round to nearest even; NaN kept quiet). */
+/* Threads the OpenMP loops of this library run on (omp_get_max_threads), for reporting. */
+int or_num_threads(void);
+
 uint16_t or_f32_to_bf16(float f);
 float or_bf16_to_f32(uint16_t b);
 

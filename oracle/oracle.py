@@ -45,6 +45,11 @@ class OrLayerW(C.Structure):
 _lib = None
 
 
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().or_num_threads())
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -66,6 +71,8 @@ def lib():
         L.or_head.argtypes = [vp, vp, C.c_int, vp, vp, vp, vp]
         L.or_decode_step.argtypes = [vp, vp, vp, vp, vp, C.c_int, vp, vp, vp, i64, vp, i64, vp, vp, vp, vp, vp]
         L.or_decode_step.restype = C.c_int
+        L.or_num_threads.argtypes = []
+        L.or_num_threads.restype = C.c_int
         L.or_f32_to_bf16.argtypes = [C.c_float]
         L.or_f32_to_bf16.restype = C.c_uint16
         L.or_bf16_to_f32.argtypes = [C.c_uint16]
