@@ -9,11 +9,11 @@
 namespace mk {
 
 enum Op : int32_t {
-  OP_EMBED = 1,   // x[b][rows] = embed[token_b][rows]; partial sum of squares; last tile publishes n_0 -> XREADY[0]
-  OP_ROUTER = 2,  // router logits for experts [r0, r1) (fp64 accumulation); the last tile routes -> ROUTER_DONE[l]
+  OP_EMBED = 1,   // x[b][rows] = embed[token_b][rows]; partial sum of squares of the rows  -> XREADY[0]
+  OP_ROUTER = 2,  // router logits for experts [r0, r1) (fp64 accumulation); the last tile routes -> SLOT_READY[l][*]
   OP_QKV = 3,     // rows [r0, r1) of KV group g's fused [q heads; k; v] projection     -> QKV_DONE[l][g]
   OP_ATTN = 4,    // split s of (sequence b, KV group g): partial softmax(qK^T)V; last arriver combines -> ATTN_DONE[l][g]
-  OP_UP = 5,      // gate+up rows [r0, r1) of expert slot s, SwiGLU                      -> UP_DONE[l][s]
+  OP_UP = 5,      // gate+up rows [r0, r1) of expert slot s, SwiGLU (waits SLOT_READY)     -> UP_DONE[l][s]
   OP_OPROJ = 6,   // rows [r0, r1) of Wo restricted to group g's columns; residual epilogue (see below)
   OP_DOWN = 7,    // rows [r0, r1) of expert slot s's down projection, times the gate; residual epilogue
   OP_RESID = 8,   // (reserved: the residual add is the epilogue of the last O-proj / down task of a row tile)
@@ -36,12 +36,18 @@ enum Word : int {
   W_SIGN = 17,  // increment
   W_ARR = 18,   // arrival counter for the last-arriver epilogue (-1 = none)
   W_ARRN = 19,  // arrivals expected
-  W_ARR2 = 20,  // second-level arrival counter (-1 = none): row tiles of the residual stream
-  W_ARRN2 = 21, // arrivals expected there
+  W_SIGR = 20,  // counters signalled: [W_SIG, W_SIG + W_SIGR) (router: one per expert slot, the value
+                // written there is the slot's routing, at least 1)
   W_RT = 22,    // residual row tile of OPROJ / DOWN / EMBED tasks
+  W_Q = 23,     // claim queue: Q_ATTN, Q_MOE, or Q_ANY (placed by the launcher)
   W_SEQ = 31    // task index (debug)
 };
 constexpr int N_WAITS = 4;
+// Claim queues.  The workgroups are split into two groups, each claiming from its own in-order queue:
+// the attention branch (embedding, router, QKV, attention, O-projection) and the expert branch (expert
+// up / down projections).  Each queue is a subsequence of the list's topological order, so the earliest
+// unfinished task of the list is always at the head of its queue with every producer finished.
+enum Queue : int32_t { Q_ATTN = 0, Q_MOE = 1, Q_ANY = 2 };
 constexpr int DESC_WORDS = 32;
 
 // Tile sizes chosen by the planner (rows per task); the kernel reads r0/r1 from the descriptor.
@@ -52,8 +58,8 @@ constexpr int SLOT_WORDS = 32;  // routing table entry per expert slot: expert, 
 
 // Counter index layout for a model/batch; computed identically by planner and host launcher.
 struct CounterLayout {
-  int32_t ticket, done, xready, qkv_done, router_arrive, router_done, attn_arrive, attn_done, up_done, resid_arrive, norm_arrive,
-      lm_arrive, total;
+  int32_t ticket, ticket2, done, xready, qkv_done, router_arrive, slot_ready, attn_arrive, attn_done, up_done, resid_arrive, lm_arrive,
+      total;
   int32_t n_layers, n_kv, n_slots, n_row_tiles, batch;
   void build(int L, int Hkv, int B, int slots, int nrt) {
     n_layers = L;
@@ -62,17 +68,17 @@ struct CounterLayout {
     n_row_tiles = nrt;
     batch = B;
     int32_t o = 0;
-    ticket = o; o += 32;     // own cache line
+    ticket = o; o += 32;     // own cache line (queue Q_ATTN)
+    ticket2 = o; o += 32;    // queue Q_MOE
     done = o; o += 32;
     xready = o; o += L + 1;
     qkv_done = o; o += L * Hkv;
     router_arrive = o; o += L;
-    router_done = o; o += L;
+    slot_ready = o; o += L * slots;
     attn_arrive = o; o += L * B * Hkv;
     attn_done = o; o += L * Hkv;
     up_done = o; o += L * slots;
     resid_arrive = o; o += L * nrt;
-    norm_arrive = o; o += L + 1;
     lm_arrive = o; o += 1;
     total = (o + 31) & ~31;
   }

@@ -59,8 +59,6 @@ struct mk_model {
   int32_t* tasks = nullptr;
   uint32_t* ctr = nullptr;
   uint32_t* err = nullptr;
-  uint32_t* nhl = nullptr;
-  float *nbuf = nullptr;
   float *x = nullptr, *ssq = nullptr, *rope_cs = nullptr, *qkv = nullptr, *apart = nullptr, *attn_o = nullptr, *opart = nullptr;
   float *rlogits = nullptr, *route_gate = nullptr, *h = nullptr, *ypart = nullptr, *lmbest_v = nullptr, *dump_n = nullptr;
   int32_t *route_sel = nullptr, *lmbest_i = nullptr, *next_tok = nullptr, *slots = nullptr;
@@ -69,6 +67,9 @@ struct mk_model {
   // task list
   mk::Plan plan;
   bool have_plan = false, dirty = false;
+  int uploaded_grid = -1;    // grid the device task array was laid out for
+  int32_t n_first = 0;       // tasks of the first claim queue in the device array
+  int32_t first_group = 0;   // workgroups claiming from the first queue
   int32_t* staging = nullptr;  // pinned host copy of the task list
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
@@ -178,8 +179,7 @@ int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out
       (rc = m->alloc(&m->ypart, (size_t)maxB * k * d)) || (rc = m->alloc(&m->lmbest_v, (size_t)maxB * t.n_lm)) ||
       (rc = m->alloc(&m->lmbest_i, (size_t)maxB * t.n_lm)) || (rc = m->alloc(&m->next_tok, maxB)) ||
       (rc = m->alloc(&m->ctr_snapshot, m->max_counters)) ||
-      (rc = m->alloc(&m->slots, (size_t)L * m->max_slots * mk::SLOT_WORDS)) ||
-      (rc = m->alloc(&m->nbuf, (size_t)maxB * d)) || (rc = m->alloc(&m->nhl, (size_t)maxB * d)))
+      (rc = m->alloc(&m->slots, (size_t)L * m->max_slots * mk::SLOT_WORDS)))
     return cleanup(rc);
   if (hipHostMalloc((void**)&m->staging, (size_t)m->max_tasks * mk::DESC_WORDS * sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
     m->staging = nullptr;
@@ -213,6 +213,43 @@ int mk_build_tasks(mk_model* m, const mk_batch* batch, int32_t* tasks_out, int64
   return MK_OK;
 }
 
+// Lay the task list out in the pinned staging buffer for the current grid.  With two or more workgroups,
+// the attention-branch queue comes first and the expert-branch queue second, each in list order, and the
+// workgroups are split between them in proportion to the queues' estimated HBM bytes; vocabulary tiles of
+// the LM head go to both queues in that same proportion.  With one workgroup the list stays one queue.
+static void lay_out_queues(mk_model* m) {
+  const mk::Plan& P = m->plan;
+  const int64_t n = P.n_tasks();
+  const int32_t* src = P.desc.data();
+  int32_t* dst = m->staging;
+  if (m->grid < 2) {
+    std::memcpy(dst, src, P.desc.size() * sizeof(int32_t));
+    m->n_first = (int32_t)n;
+    m->first_group = m->grid;
+  } else {
+    const double tot = P.bytes_attn + P.bytes_moe;
+    const double fa = tot > 0 ? P.bytes_attn / tot : 0.5;
+    int ga = (int)(fa * m->grid + 0.5);
+    ga = std::max(1, std::min(m->grid - 1, ga));
+    const int64_t lm_first = (int64_t)((double)P.t.n_lm * ga / m->grid + 0.5);
+    int64_t o = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+      int64_t lm_seen = 0;
+      for (int64_t i = 0; i < n; ++i) {
+        const int32_t* w = src + i * mk::DESC_WORDS;
+        int q = w[mk::W_Q];
+        if (q == mk::Q_ANY) q = (lm_seen++ < lm_first) ? mk::Q_ATTN : mk::Q_MOE;
+        if (q != pass) continue;
+        std::memcpy(dst + o * mk::DESC_WORDS, w, mk::DESC_WORDS * sizeof(int32_t));
+        ++o;
+      }
+      if (pass == 0) m->n_first = (int32_t)o;
+    }
+    m->first_group = ga;
+  }
+  m->uploaded_grid = m->grid;
+}
+
 int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* page_tables, void* kv_pages,
                    float* logits_out, void* stream) {
   if (!m) return fail(MK_E_INVAL, "null handle");
@@ -220,9 +257,9 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   if (!tokens || !seq_lens || !page_tables || !kv_pages || !logits_out) return fail(MK_E_INVAL, "null step pointer");
   hipStream_t s = (hipStream_t)stream;
   const mk::Plan& P = m->plan;
-  if (m->dirty) {
+  if (m->dirty || m->uploaded_grid != m->grid) {
     if (m->upload_pending) HIPCHK(hipEventSynchronize(m->upload_done));  // staging may still feed the previous copy
-    std::memcpy(m->staging, P.desc.data(), P.desc.size() * sizeof(int32_t));
+    lay_out_queues(m);
     HIPCHK(hipMemcpyAsync(m->tasks, m->staging, P.desc.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
     HIPCHK(hipEventRecord(m->upload_done, s));
     m->upload_pending = true;
@@ -251,6 +288,9 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   a.n_tasks = (int32_t)P.n_tasks();
   a.n_counters = P.cl.total;
   a.c_ticket = P.cl.ticket;
+  a.c_ticket2 = P.cl.ticket2;
+  a.n_first = m->n_first;
+  a.first_group = m->first_group;
   a.c_done = P.cl.done;
   a.layers = m->layers;
   a.embed = m->embed;
@@ -268,8 +308,6 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   a.err = m->err;
   a.x = m->x;
   a.ssq = m->ssq;
-  a.nbuf = m->nbuf;
-  a.nhl = m->nhl;
   a.rope_cs = m->rope_cs;
   a.qkv = m->qkv;
   a.apart = m->apart;

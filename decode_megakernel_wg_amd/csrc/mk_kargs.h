@@ -27,7 +27,9 @@ struct KArgs {
   int32_t B, n_slots, max_pages, n_rt, n_lm;
   int64_t n_pages;
   float eps;
-  int32_t n_tasks, n_counters, c_ticket, c_done;
+  int32_t n_tasks, n_counters, c_ticket, c_ticket2, c_done;
+  int32_t n_first;      // tasks [0, n_first) form the first claim queue, [n_first, n_tasks) the second
+  int32_t first_group;  // workgroups [0, first_group) claim from the first queue, the rest from the second
   // model (device)
   const LayerW* layers;
   const uint16_t* embed;
@@ -47,8 +49,6 @@ struct KArgs {
   uint32_t* err;
   float* x;          // [B][d] residual stream
   float* ssq;        // [B][n_rt] partial sums of squares of x per row tile
-  float* nbuf;       // [B][d] normalised input of the current layer (fp32)
-  uint32_t* nhl;     // [2][B][d/2] the same split into BF16 hi (first half) and lo parts, two values per word
   float* rope_cs;    // [B][dh/2][2] cos, sin of the new position
   float* qkv;        // [B][Hkv][(grp+2)*dh] projections (q heads of the group, then k, then v)
   float* apart;      // [B][Hkv][ATTN_MAX_SPLITS][grp][dh+2] attention split partials (o, m, l)

@@ -5,7 +5,8 @@
 // 1.58x vLLM on H100", section "One persistent kernel for the whole decode step"):
 //  * one 512-thread workgroup per compute unit stays resident for the whole step and claims tasks
 //    (one operation on one tile) from a task list in global memory, in list order, through an atomic
-//    ticket; the next ticket is claimed while the current task runs;
+//    ticket; two tickets are claimed ahead and the next task's descriptor is copied into LDS while the
+//    current task runs, so a task starts without a round trip to memory;
 //  * dependencies are global counters: a finished task increments its counter, a task that needs an
 //    input spins on the producer's counter (no grid barrier, no kernel boundary);
 //  * weight tiles (immutable) and old KV pages are loaded into registers BEFORE the task waits for its
@@ -80,10 +81,27 @@ struct Lds {
   int slot_e, slot_n, slot_b[8], slot_j[8];
   float slot_g[8];
   int slotw[SLOT_WORDS];
-  int task, next, flag;
+  int32_t desc[2][DESC_WORDS];  // current and next task descriptor
+  uint32_t wval;                // value a wait observed (expert slot words)
+  int next1, flag;
+};
+
+// A task descriptor staged in LDS; every word is read as a wave-uniform (scalar) value.
+struct Desc {
+  const int32_t* p;
+  __device__ __forceinline__ int32_t operator[](int i) const { return __builtin_amdgcn_readfirstlane(p[i]); }
 };
 
 // ------------------------------------------------------------------------------------------ helpers
+
+// The thread index as an opaque value: each use goes through an empty volatile asm, so the compiler cannot
+// hoist values derived from it out of the persistent task loop (where they would stay live, and be spilled,
+// across every task body).
+__device__ __forceinline__ int tidx() {
+  int t = (int)__builtin_amdgcn_workitem_id_x();
+  __asm__ volatile("" : "+v"(t));
+  return t;
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -142,30 +160,32 @@ __device__ __forceinline__ void raise_error(KA& a, uint32_t code, int task) {
   __hip_atomic_store(&a.err[ERR_ABORT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0 spins until counter c reaches target (or the step is aborted).
-__device__ __forceinline__ void spin_ge(KA& a, int32_t c, int32_t target, int task) {
-  if (c < 0) return;
-  uint32_t n = 0;
-  while (__hip_atomic_load(&a.ctr[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)target) {
+// Thread 0 spins until counter c reaches target (or the step is aborted); returns the value it saw.
+__device__ __forceinline__ uint32_t spin_ge(KA& a, int32_t c, int32_t target, int task) {
+  if (c < 0) return 0u;
+  uint32_t n = 0, v;
+  while ((v = __hip_atomic_load(&a.ctr[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < (uint32_t)target) {
     if ((++n & 63) == 0) {
-      if (__hip_atomic_load(&a.err[ERR_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
+      if (__hip_atomic_load(&a.err[ERR_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return 0u;
       if (n > SPIN_LIMIT) {
         raise_error(a, ERRC_TIMEOUT, task);
-        return;
+        return 0u;
       }
     }
     __builtin_amdgcn_s_sleep(1);
   }
+  return v;
 }
 
 // Debug trace: sub-phase mark k (0..3) of task t.
 __device__ __forceinline__ void mark(KA& a, int t, int k) {
-  if (a.ts && threadIdx.x == 0) a.ts[(int64_t)t * 8 + 4 + k] = wall_clock64();
+  if (a.ts && tidx() == 0) a.ts[(int64_t)t * 8 + 4 + k] = wall_clock64();
 }
 
 // Wait for descriptor waits [i0, i1), then make the producers' data visible to the whole workgroup.
-__device__ __forceinline__ void wait_deps(KA& a, const int32_t* w, int i0, int i1, int task) {
-  if (threadIdx.x == 0) {
+__device__ __forceinline__ void wait_deps(KA& a, Desc w, int i0, int i1, int task) {
+  if (i0 >= i1) return;
+  if (tidx() == 0) {
     for (int i = i0; i < i1; ++i) spin_ge(a, w[W_WAIT0 + 2 * i], w[W_WAIT0 + 2 * i + 1], task);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (a.ts) a.ts[(int64_t)task * 8 + 1] = wall_clock64();
@@ -173,18 +193,30 @@ __device__ __forceinline__ void wait_deps(KA& a, const int32_t* w, int i0, int i
   __syncthreads();
 }
 
+// Wait i of the descriptor, returning the counter value it observed (to every thread).  Expert-slot
+// counters carry the routing of their slot in that value.
+__device__ __forceinline__ uint32_t wait_value(KA& a, Desc w, int i, int task, Lds& S) {
+  if (tidx() == 0) {
+    S.wval = spin_ge(a, w[W_WAIT0 + 2 * i], w[W_WAIT0 + 2 * i + 1], task);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (a.ts) a.ts[(int64_t)task * 8 + 1] = wall_clock64();
+  }
+  __syncthreads();
+  return S.wval;
+}
+
 // Every thread has issued its published stores: drain them, then count the task as complete.
 __device__ __forceinline__ void signal(KA& a, int32_t c, int32_t n) {
   drain_stores();
   __syncthreads();
-  if (threadIdx.x == 0 && c >= 0) __hip_atomic_fetch_add(&a.ctr[c], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tidx() == 0 && c >= 0) __hip_atomic_fetch_add(&a.ctr[c], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Arrive on a last-arriver counter; returns true (to every thread) in the workgroup that arrives last.
 __device__ __forceinline__ bool arrive_last(KA& a, int32_t c, int32_t n, Lds& S) {
   drain_stores();
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tidx() == 0) {
     uint32_t old = __hip_atomic_fetch_add(&a.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     S.flag = (old == (uint32_t)(n - 1));
     if (S.flag) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -193,40 +225,66 @@ __device__ __forceinline__ bool arrive_last(KA& a, int32_t c, int32_t n, Lds& S)
   return S.flag != 0;
 }
 
-// RMSNorm of the residual stream into LDS: xs[b][i] = x[b][i] * gamma[i] * inv_rms[b], for b < nb
-// (token list tok[] maps staging row -> batch row; null = identity).
-__device__ __forceinline__ void stage_norm(KA& a, const uint16_t* gamma, int nb, const int* tok, Lds& S) {
+// Copy n16 16-byte chunks from global memory (contiguous) to LDS (contiguous) with direct global->LDS
+// loads, spread over the workgroup's waves: no registers are held, and every chunk is in flight at once.
+// Completion is tracked by vmcnt: the caller drains (vmcnt(0)) and synchronises before reading dst.
+__device__ __forceinline__ void lds_copy(const void* src, void* dst, int n16) {
+  const int wave = tidx() >> 6, lane = tidx() & 63;
+  for (int c0 = wave * 64; c0 < n16; c0 += NT) {
+    if (c0 + lane < n16)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const char*)src + (int64_t)(c0 + lane) * 16),
+                                       (__attribute__((address_space(3))) void*)((char*)dst + (int64_t)c0 * 16), 16, 0, 0);
+  }
+}
+
+// The RMSNorm gain of one consumer, loaded (two elements per word) before the consumer waits for its
+// input: gains are weights, immutable during the step.
+constexpr int NORM_PAIRS = 4096 / 2 / NT;  // gain pairs per thread (d_model <= 4096)
+struct NormGain {
+  uint32_t g[NORM_PAIRS];
+};
+__device__ __forceinline__ NormGain norm_gain(const uint16_t* gamma, int d) {
+  NormGain n;
+  const uint32_t* g2 = reinterpret_cast<const uint32_t*>(gamma);
+#pragma unroll
+  for (int e = 0; e < NORM_PAIRS; ++e) {
+    const int p = tidx() + e * NT;
+    n.g[e] = 2 * p < d ? g2[p] : 0u;
+  }
+  return n;
+}
+
+// RMSNorm of the residual stream into LDS: xs[j][i] = x[b][i] * (gamma[i] * inv_rms[b]) for staging rows
+// j < nb of tokens b = tok[j] (null = identity).  inv_rms[b] = 1 / sqrt(sum of the row tiles' partial sums
+// of squares (tile order) / d + eps).  One round trip: the rows and the partial sums load together.
+__device__ __forceinline__ void stage_norm(KA& a, const NormGain& gn, int nb, const int* tok, Lds& S) {
   const int d = a.d, nrt = a.n_rt;
-  // one round trip: raw x rows, the partial sums of squares and the gain are loaded together
-  constexpr int MAXE = 4096 / NT;  // gain elements per thread (d_model <= 4096)
-  float gv[MAXE];
-#pragma unroll
-  for (int e = 0; e < MAXE; ++e) {
-    const int c = threadIdx.x + e * NT;
-    gv[e] = c < d ? bf2f(gamma[c]) : 0.f;
-  }
-  for (int i = threadIdx.x; i < nb * d; i += NT) {
-    const int j = i / d, c = i - j * d;
+  for (int j = 0; j < nb; ++j) lds_copy(a.x + (tok ? tok[j] : j) * d, S.xs + j * d, d / 4);
+  if (tidx() < nb * nrt) {
+    const int j = tidx() / nrt, r = tidx() - j * nrt;
     const int b = tok ? tok[j] : j;
-    S.xs[i] = a.x[b * d + c];
+    S.ssqv[tidx()] = a.ssq[b * nrt + r];
   }
-  if (threadIdx.x < nb * nrt) {
-    const int j = threadIdx.x / nrt, r = threadIdx.x - j * nrt;
-    const int b = tok ? tok[j] : j;
-    S.ssqv[threadIdx.x] = a.ssq[b * nrt + r];
-  }
+  drain_stores();
   __syncthreads();
-  if (threadIdx.x < nb) {
+  if (tidx() < nb) {
     float ss = 0.f;
-    for (int r = 0; r < nrt; ++r) ss += S.ssqv[threadIdx.x * nrt + r];
-    S.inv[threadIdx.x] = 1.0f / sqrtf(ss / (float)d + a.eps);
+    for (int r = 0; r < nrt; ++r) ss += S.ssqv[tidx() * nrt + r];
+    S.inv[tidx()] = 1.0f / sqrtf(ss / (float)d + a.eps);
   }
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < MAXE; ++e) {
-    const int c = threadIdx.x + e * NT;
-    if (c < d)
-      for (int j = 0; j < nb; ++j) S.xs[j * d + c] *= gv[e] * S.inv[j];
+  for (int e = 0; e < NORM_PAIRS; ++e) {
+    const int p = tidx() + e * NT;
+    if (2 * p < d) {
+      const float g0 = bf_lo(gn.g[e]), g1 = bf_hi(gn.g[e]);
+      for (int j = 0; j < nb; ++j) {
+        const float inv = S.inv[j];
+        float* xr = S.xs + j * d + 2 * p;
+        xr[0] *= g0 * inv;
+        xr[1] *= g1 * inv;
+      }
+    }
   }
   __syncthreads();
 }
@@ -260,7 +318,7 @@ struct Rows2 {
 
 template <int NV, int RPW, class RowPtr>
 __device__ __forceinline__ void gemv_load(WBuf<NV, RPW>& buf, const RowPtr& W, int nrows, int K8, int pass) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tidx() >> 6, lane = tidx() & 63;
   const int row0 = pass * NW * RPW + wave * RPW;
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
@@ -300,91 +358,49 @@ __device__ __forceinline__ double dot8d(u4 w, const f4& x0, const f4& x1, double
   return acc;
 }
 
-// The layer's normalised input, as published once per layer (see publish_norm): fp32 rows into S.xs
-// (pitch d) or BF16 hi/lo rows straight into S.xb, for staging rows j < nb from tokens tok[j].
-__device__ __forceinline__ void stage_n32(KA& a, int nb, const int* tok, Lds& S) {
-  const int d = a.d;
-  for (int i = threadIdx.x; i < nb * d; i += NT) {
-    const int j = i / d, c = i - j * d;
-    S.xs[i] = a.nbuf[(tok ? tok[j] : j) * d + c];
-  }
-  __syncthreads();
-}
-__device__ __forceinline__ void stage_nhl(KA& a, int nb, const int* tok, Lds& S) {
-  const int d2 = a.d >> 1;
-  const uint32_t* lo = a.nhl + (int64_t)a.B * d2;
-  for (int i = threadIdx.x; i < nb * d2; i += NT) {
-    const int j = i / d2, c = i - j * d2;
-    const int b = tok ? tok[j] : j;
-    *reinterpret_cast<uint32_t*>(S.xb + j * XBP + 2 * c) = a.nhl[b * d2 + c];
-    *reinterpret_cast<uint32_t*>(S.xb + (8 + j) * XBP + 2 * c) = lo[b * d2 + c];
-  }
-  __syncthreads();
-}
-
 // Residual rows [r0, r1): x += sum over KV groups of the O-projection partials + sum over the k selections
-// of the gated expert outputs (fixed order); partial sum of squares of the new rows into ssq[b][rt].
-__device__ __forceinline__ void resid_rows(KA& a, int r0, int r1, int rt) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int d = a.d, B = a.B;
+// of the gated expert outputs (fixed order: groups ascending, then selections ascending); the partial sum
+// of squares of each token's new rows goes to ssq[b][rt].  Every partial of a row is loaded before any is
+// added, so the whole update costs one round trip to memory.
+__device__ __forceinline__ void resid_rows(KA& a, int r0, int r1, int rt, Lds& S) {
+  const int wave = tidx() >> 6, lane = tidx() & 63;
+  const int d = a.d, B = a.B, n = r1 - r0, Hkv = a.Hkv, k = a.k;
+  float* sq = S.xs;  // [B][n] squares of the new rows
+  for (int i = tidx(); i < B * n; i += NT) {
+    const int b = i / n, r = r0 + (i - b * n);
+    const float xv = a.x[b * d + r];
+    float op[8], yp[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) op[g] = g < Hkv ? a.opart[((int64_t)g * B + b) * d + r] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) yp[j] = j < k ? a.ypart[((int64_t)b * k + j) * d + r] : 0.f;
+    float v = xv;
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      if (g < Hkv) v += op[g];
+    for (int g = 8; g < Hkv; ++g) v += a.opart[((int64_t)g * B + b) * d + r];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) v += yp[j];
+    pub(&a.x[b * d + r], v);
+    sq[i] = v * v;
+  }
+  __syncthreads();
   if (wave < B) {
     const int b = wave;
     float acc = 0.f;
-    for (int r = r0 + lane; r < r1; r += 64) {
-      float v = a.x[b * d + r];
-      for (int g = 0; g < a.Hkv; ++g) v += a.opart[((int64_t)g * B + b) * d + r];
-      for (int j = 0; j < a.k; ++j) v += a.ypart[((int64_t)b * a.k + j) * d + r];
-      pub(&a.x[b * d + r], v);
-      acc = fmaf(v, v, acc);
-    }
+    for (int r = lane; r < n; r += 64) acc += sq[b * n + r];
     const float s = wave_sum(acc);
     if (lane == 0) pub(&a.ssq[b * a.n_rt + rt], s);
   }
 }
 
-// The next layer's RMSNorm over the complete residual stream: n = x * gamma / sqrt(mean(x^2) + eps), gamma
-// of layer lnext (the final norm after the last layer), published as fp32 and as BF16 hi + lo parts.
-__device__ __forceinline__ void publish_norm(KA& a, int lnext, Lds& S) {
-  const int d = a.d, B = a.B, nrt = a.n_rt, d2 = d >> 1;
-  const uint16_t* gamma = lnext < a.L ? a.layers[lnext].attn_norm : a.final_norm;
-  if (threadIdx.x < B) {
-    float ss = 0.f;
-    for (int r = 0; r < nrt; ++r) ss += a.ssq[threadIdx.x * nrt + r];
-    S.inv[threadIdx.x] = 1.0f / sqrtf(ss / (float)d + a.eps);
-  }
-  __syncthreads();
-  uint32_t* lo = a.nhl + (int64_t)B * d2;
-  float* dump = (a.dump_n && lnext < a.L) ? a.dump_n + (int64_t)lnext * B * d : nullptr;
-  for (int i = threadIdx.x; i < B * d2; i += NT) {
-    const int b = i / d2, c = 2 * (i - b * d2);
-    const float inv = S.inv[b];
-    const float n0 = a.x[b * d + c] * bf2f(gamma[c]) * inv;
-    const float n1 = a.x[b * d + c + 1] * bf2f(gamma[c + 1]) * inv;
-    pub(&a.nbuf[b * d + c], n0);
-    pub(&a.nbuf[b * d + c + 1], n1);
-    const uint16_t h0 = f2bf(n0), h1 = f2bf(n1);
-    pubi(reinterpret_cast<int32_t*>(&a.nhl[i]), (int32_t)(h0 | ((uint32_t)h1 << 16)));
-    pubi(reinterpret_cast<int32_t*>(&lo[i]), (int32_t)(f2bf(n0 - bf2f(h0)) | ((uint32_t)f2bf(n1 - bf2f(h1)) << 16)));
-    if (dump) {
-      dump[b * d + c] = n0;
-      dump[b * d + c + 1] = n1;
-    }
-  }
-}
-
-// End of a task that produced rows of the residual stream: the last row tile of the layer publishes the
-// next layer's normalised input and signals that layer's consumers.
-__device__ __forceinline__ void norm_chain(KA& a, const int32_t* w, int lnext, Lds& S) {
-  if (arrive_last(a, w[W_ARR2], w[W_ARRN2], S)) {
-    publish_norm(a, lnext, S);
-    signal(a, w[W_SIG], w[W_SIGN]);
-  }
-}
-// End of an O-proj / expert-down task: the last producer of the row tile adds the partials into x.
-__device__ __forceinline__ void resid_chain(KA& a, const int32_t* w, int l, Lds& S) {
+// End of an O-proj / expert-down task: the last producer of the row tile adds the partials into x and
+// signals the next layer's readiness counter (which waits for every row tile).
+__device__ __forceinline__ void resid_chain(KA& a, Desc w, Lds& S) {
   if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) {
-    resid_rows(a, w[W_R0], w[W_R1], w[W_RT]);
-    norm_chain(a, w, l + 1, S);
+    resid_rows(a, w[W_R0], w[W_R1], w[W_RT], S);
+    signal(a, w[W_SIG], w[W_SIGN]);
   }
 }
 
@@ -418,7 +434,7 @@ struct MBuf {
 
 template <class RowPtr>
 __device__ __forceinline__ void mg_load(MBuf& buf, const RowPtr& W, const MGeo& g, int pass) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tidx() >> 6, lane = tidx() & 63;
   const int rb = wave / g.ks, kp = wave - rb * g.ks;
   const int row = rb * 16 + (lane & 15);
   const bool ok = rb < g.rbn && row < g.nrows;
@@ -432,7 +448,7 @@ __device__ __forceinline__ void mg_load(MBuf& buf, const RowPtr& W, const MGeo& 
 }
 
 __device__ __forceinline__ void mg_compute(const MBuf& buf, f4& acc, const MGeo& g, int pass, int nb, Lds& S) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tidx() >> 6, lane = tidx() & 63;
   const int rb = wave / g.ks, kp = wave - rb * g.ks;
   if (rb >= g.rbn) return;
   const int j = lane & 15;
@@ -458,7 +474,7 @@ __device__ __forceinline__ void mg_compute(const MBuf& buf, f4& acc, const MGeo&
 // Sum the K-slice partials of each row block (fixed order) and hand (row, token, value) to out().
 template <class Out>
 __device__ __forceinline__ void mg_finish(f4 acc, const MGeo& g, int nb, Out& out, Lds& S) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tidx() >> 6, lane = tidx() & 63;
   const int rb = wave / g.ks, kp = wave - rb * g.ks;
   if (g.ks > 1) {
     float* red = S.pt;  // [NW][64][4]
@@ -482,7 +498,7 @@ __device__ __forceinline__ void mg_finish(f4 acc, const MGeo& g, int nb, Out& ou
 
 // Split the staged fp32 inputs S.xs[nb][K] into BF16 hi and lo parts.
 __device__ __forceinline__ void split_x(int nb, int K, Lds& S) {
-  for (int i = threadIdx.x; i < nb * K; i += NT) {
+  for (int i = tidx(); i < nb * K; i += NT) {
     const int j = i / K, c = i - j * K;
     const float x = S.xs[i];
     const uint16_t h = f2bf(x);
@@ -495,7 +511,7 @@ __device__ __forceinline__ void split_x(int nb, int K, Lds& S) {
 // Prefetch, wait, stage, stream.  The first two passes of the tile (up to 2 x 16 KB per wave) are loaded
 // before the dependency wait [wait0, wait1), so weights stream while the inputs are still being produced.
 template <bool SPLIT, class RowPtr, class Stage, class Out>
-__device__ __forceinline__ void mgemv_task(KA& a, const int32_t* w, int t, const RowPtr& W, int nrows, int K, int nb, int wait0,
+__device__ __forceinline__ void mgemv_task(KA& a, Desc w, int t, const RowPtr& W, int nrows, int K, int nb, int wait0,
                                            int wait1, Stage&& stage, Out&& out, Lds& S) {
   const MGeo g = mgeo(nrows, K);
   MBuf b0, b1;
@@ -521,7 +537,7 @@ __device__ __forceinline__ void mgemv_task(KA& a, const int32_t* w, int t, const
 template <int NV, int RPW, int NB, class Out>
 __device__ __forceinline__ void gemv_run_f64(WBuf<NV, RPW>& buf0, int nrows, int K, const float* xs, int xp, int nb, Out& out) {
   const int K8 = K >> 3;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tidx() >> 6, lane = tidx() & 63;
   // router tiles hold at most NW*RPW rows: one pass
   double acc[RPW][NB];
 #pragma unroll
@@ -556,9 +572,11 @@ __device__ __forceinline__ void gemv_run_f64(WBuf<NV, RPW>& buf0, int nrows, int
 // Done once per layer by the router tile that finishes last: top-k of each token's router logits (logit
 // descending, lower index first on ties; a NaN ranks lowest), gates = softmax of the selected logits,
 // and the table of expert slots (slot s = the s-th distinct selected expert in ascending id, with the
-// tokens that chose it, their selection rank and gate).  Expert tasks read their slot's entry.
-__device__ __forceinline__ void route_layer(KA& a, int l, Lds& S) {
-  const int E = a.E, k = a.k, B = a.B, tid = threadIdx.x;
+// tokens that chose it, their selection rank and gate).  Each slot's readiness counter (ctr[slot0 + s])
+// then receives the slot's expert and token mask (see slot_routing), so expert tasks learn their expert
+// from the wait itself.
+__device__ __forceinline__ void route_layer(KA& a, int l, int32_t slot0, Lds& S) {
+  const int E = a.E, k = a.k, B = a.B, tid = tidx();
   const float* lg = a.rlogits + (int64_t)l * B * E;
   float* key = S.xs;  // [B][E] logits with NaN replaced by -inf
   for (int i = tid; i < B * E; i += NT) {
@@ -600,7 +618,8 @@ __device__ __forceinline__ void route_layer(KA& a, int l, Lds& S) {
     }
   }
   __syncthreads();
-  // slot table
+  // slot table (n_slots <= 64 < NT: thread s builds slot s and keeps its counter value)
+  uint32_t sv = 0;
   for (int s = tid; s < a.n_slots; s += NT) {
     int e = -1, cnt = 0;
     for (int wd = 0; wd < 8 && e < 0; ++wd) {
@@ -615,6 +634,7 @@ __device__ __forceinline__ void route_layer(KA& a, int l, Lds& S) {
     }
     int32_t* ent = a.slots + ((int64_t)l * a.n_slots + s) * SLOT_WORDS;
     int n = 0;
+    uint32_t mask = 0;
     if (e >= 0)
       for (int b = 0; b < B; ++b)
         for (int j = 0; j < k; ++j)
@@ -622,34 +642,23 @@ __device__ __forceinline__ void route_layer(KA& a, int l, Lds& S) {
             pubi(ent + 2 + 3 * n, b);
             pubi(ent + 3 + 3 * n, j);
             pubi(ent + 4 + 3 * n, __float_as_int(S.gate[b * 8 + j]));
+            mask |= 1u << b;
             ++n;
           }
     pubi(ent + 0, e);
     pubi(ent + 1, n);
+    sv = e >= 0 ? (mask << 16) | (uint32_t)(e + 1) : 0x80000000u;
   }
-}
-
-// Load slot s's routing entry into LDS (valid after the layer's routing was published); false if unused.
-__device__ __forceinline__ bool load_slot(KA& a, int l, int s, Lds& S) {
-  if (threadIdx.x < SLOT_WORDS) S.slotw[threadIdx.x] = a.slots[((int64_t)l * a.n_slots + s) * SLOT_WORDS + threadIdx.x];
+  // publish the entries, then release the slots (one counter each, value = routing)
+  drain_stores();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    S.slot_e = S.slotw[0];
-    S.slot_n = S.slot_e >= 0 ? min(S.slotw[1], 8) : 0;
-    for (int i = 0; i < S.slot_n; ++i) {
-      S.slot_b[i] = S.slotw[2 + 3 * i];
-      S.slot_j[i] = S.slotw[3 + 3 * i];
-      S.slot_g[i] = __int_as_float(S.slotw[4 + 3 * i]);
-    }
-  }
-  __syncthreads();
-  return S.slot_e >= 0 && S.slot_e < a.E;
+  if (tid < a.n_slots && slot0 >= 0) __hip_atomic_store(&a.ctr[slot0 + tid], sv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------------------------------ task bodies
 
-__device__ __forceinline__ void task_embed(KA& a, const int32_t* w, int t, Lds& S) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ __forceinline__ void task_embed(KA& a, Desc w, int t, Lds& S) {
+  const int wave = tidx() >> 6, lane = tidx() & 63;
   const int r0 = w[W_R0], r1 = w[W_R1], rt = w[W_A];
   if (wave < a.B) {
     const int b = wave;
@@ -670,7 +679,7 @@ __device__ __forceinline__ void task_embed(KA& a, const int32_t* w, int t, Lds& 
   // RoPE angles of each sequence's new position (fp64 angle, then cos/sin), once per step
   if (rt == 0) {
     const int half = a.dh / 2;
-    for (int i = threadIdx.x; i < a.B * half; i += NT) {
+    for (int i = tidx(); i < a.B * half; i += NT) {
       const int b = i / half, j = i - b * half;
       const double th = (double)a.seq_lens[b] * a.inv_freq[j];
       double sn, cs;
@@ -679,13 +688,13 @@ __device__ __forceinline__ void task_embed(KA& a, const int32_t* w, int t, Lds& 
       pub(&a.rope_cs[(b * half + j) * 2 + 1], (float)sn);
     }
   }
-  norm_chain(a, w, 0, S);
+  signal(a, w[W_SIG], w[W_SIGN]);
 }
 
 
 
 template <class C>
-__device__ __forceinline__ void task_qkv(KA& a, const int32_t* w, int t, Lds& S) {
+__device__ __forceinline__ void task_qkv(KA& a, Desc w, int t, Lds& S) {
   const int l = w[W_LAYER], g = w[W_A], r0 = w[W_R0], r1 = w[W_R1];
   const int grp = a.Hq / a.Hkv, dh = a.dh, d = a.d;
   const LayerW& L = a.layers[l];
@@ -696,26 +705,30 @@ __device__ __forceinline__ void task_qkv(KA& a, const int32_t* w, int t, Lds& S)
   const int rows = (grp + 2) * dh;
   float* out = a.qkv + (int64_t)g * rows + r0;
   const int64_t bstride = (int64_t)a.Hkv * rows;
-  mgemv_task<false>(
-      a, w, t, Rows1{W, d}, r1 - r0, d, a.B, 0, N_WAITS, [&] { stage_nhl(a, a.B, nullptr, S); },
+  const NormGain gn = norm_gain(L.attn_norm, d);
+  mgemv_task<true>(
+      a, w, t, Rows1{W, d}, r1 - r0, d, a.B, 0, N_WAITS, [&] { stage_norm(a, gn, a.B, nullptr, S); },
       [&](int r, int b, float v) { pub(out + b * bstride + r, v); }, S);
   signal(a, w[W_SIG], w[W_SIGN]);
 }
 
 template <class C>
-__device__ __forceinline__ void task_router(KA& a, const int32_t* w, int t, Lds& S) {
+__device__ __forceinline__ void task_router(KA& a, Desc w, int t, Lds& S) {
   const int l = w[W_LAYER], r0 = w[W_R0], r1 = w[W_R1];
   const LayerW& L = a.layers[l];
   const int d = a.d, nrows = r1 - r0, K8 = d >> 3;
   const uint16_t* W = L.w_router + (int64_t)r0 * d;
   float* lg = a.rlogits + (int64_t)l * a.B * a.E;
   auto out = [&](int r, int b, double v) { pub(lg + b * a.E + r0 + r, (float)v + a.router_bias[r0 + r]); };
+  const NormGain gn = norm_gain(L.attn_norm, d);
   auto go = [&](auto nvr) {
     constexpr int NV = decltype(nvr)::nv, RPW = decltype(nvr)::rpw;
     WBuf<NV, RPW> buf0;
     gemv_load(buf0, Rows1{W, d}, nrows, K8, 0);
     wait_deps(a, w, 0, N_WAITS, t);
-    stage_n32(a, a.B, nullptr, S);
+    stage_norm(a, gn, a.B, nullptr, S);
+    if (a.dump_n && r0 == 0)  // debug: the normalised input this layer routed on
+      for (int i = tidx(); i < a.B * d; i += NT) a.dump_n[(int64_t)l * a.B * d + i] = S.xs[i];
     const int nb = a.B;
     if (nb <= 1) gemv_run_f64<NV, RPW, 1>(buf0, nrows, d, S.xs, d, nb, out);
     else if (nb <= 2) gemv_run_f64<NV, RPW, 2>(buf0, nrows, d, S.xs, d, nb, out);
@@ -724,14 +737,11 @@ __device__ __forceinline__ void task_router(KA& a, const int32_t* w, int t, Lds&
   };
   (void)K8;
   go(NVR<C::NVD, 2>{});
-  if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) {
-    route_layer(a, l, S);
-    signal(a, w[W_SIG], w[W_SIGN]);
-  }
+  if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) route_layer(a, l, w[W_SIG], S);
 }
 
 template <class C>
-__device__ __forceinline__ void task_oproj(KA& a, const int32_t* w, int t, Lds& S) {
+__device__ __forceinline__ void task_oproj(KA& a, Desc w, int t, Lds& S) {
   const int l = w[W_LAYER], g = w[W_A], r0 = w[W_R0], r1 = w[W_R1];
   const int grp = a.Hq / a.Hkv, K = grp * a.dh, ldo = a.Hq * a.dh, B = a.B, d = a.d;
   const uint16_t* W = a.layers[l].wo + (int64_t)r0 * ldo + (int64_t)g * K;
@@ -739,34 +749,51 @@ __device__ __forceinline__ void task_oproj(KA& a, const int32_t* w, int t, Lds& 
   mgemv_task<true>(
       a, w, t, Rows1{W, ldo}, r1 - r0, K, B, 0, N_WAITS,
       [&] {
-        for (int i = threadIdx.x; i < B * K; i += NT) {
+        for (int i = tidx(); i < B * K; i += NT) {
           const int b = i / K, c = i - b * K;
           S.xs[i] = a.attn_o[(int64_t)b * ldo + (int64_t)g * K + c];
         }
         __syncthreads();
       },
       [&](int r, int b, float v) { pub(out + (int64_t)b * d + r, v); }, S);
-  resid_chain(a, w, l, S);
+  resid_chain(a, w, S);
+}
+
+// Routing of an expert slot as its readiness counter carries it: bits 0..15 = expert + 1, bits 16..23 =
+// mask of the tokens that selected it; bit 31 alone = slot unused this step.  Tokens of the slot in
+// ascending order go to S.slot_b; returns the expert, or -1 for an unused slot.
+__device__ __forceinline__ int slot_routing(KA& a, uint32_t v, Lds& S) {
+  const int e = (int)(v & 0xffffu) - 1;
+  if ((v >> 31) || e < 0 || e >= a.E) return -1;
+  if (tidx() == 0) {
+    uint32_t m = (v >> 16) & 0xffu;
+    int n = 0;
+    for (int b = 0; b < a.B; ++b)
+      if (m & (1u << b)) S.slot_b[n++] = b;
+    S.slot_n = n;
+  }
+  __syncthreads();
+  return S.slot_n > 0 ? e : -1;
 }
 
 template <class C>
-__device__ __forceinline__ void task_up(KA& a, const int32_t* w, int t, Lds& S) {
+__device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
   const int l = w[W_LAYER], s = w[W_A], r0 = w[W_R0], r1 = w[W_R1];
   const int d = a.d, F = a.F, nr = r1 - r0;
-  wait_deps(a, w, 0, N_WAITS, t);
-  if (load_slot(a, l, s, S)) {
-    const int e = S.slot_e, n = S.slot_n;
-    const LayerW& L = a.layers[l];
-    // gate rows then up rows of this tile, as one 2*nr-row tile (two bases)
+  const LayerW& L = a.layers[l];
+  const NormGain gn = norm_gain(L.attn_norm, d);
+  const int e = slot_routing(a, wait_value(a, w, 0, t, S), S);
+  if (e >= 0) {
+    const int n = S.slot_n;
+    // gate rows then up rows of this tile, as one 2*nr-row tile over two bases; the expert is known only
+    // now, so its weights stream while the slot's inputs are normalised into LDS
     const uint16_t* Wg = L.w_gate + ((int64_t)e * F + r0) * d;
     const uint16_t* Wu = L.w_up + ((int64_t)e * F + r0) * d;
-    // gate rows then up rows of this tile, one 2*nr-row tile over two bases; the expert is known only now,
-    // so its weights stream while the slot's inputs are staged
-    mgemv_task<false>(
-        a, w, t, Rows2{Wg, Wu, d, nr}, 2 * nr, d, n, 0, 0, [&] { stage_nhl(a, n, S.slot_b, S); },
+    mgemv_task<true>(
+        a, w, t, Rows2{Wg, Wu, d, nr}, 2 * nr, d, n, 0, 0, [&] { stage_norm(a, gn, n, S.slot_b, S); },
         [&](int r, int b, float v) { S.gu[r * 8 + b] = v; }, S);
     __syncthreads();
-    for (int i = threadIdx.x; i < nr * n; i += NT) {
+    for (int i = tidx(); i < nr * n; i += NT) {
       const int r = i / n, j = i - r * n;
       const float gv = S.gu[r * 8 + j], uv = S.gu[(nr + r) * 8 + j];
       const float h = gv / (1.0f + expf(-gv)) * uv;
@@ -777,35 +804,43 @@ __device__ __forceinline__ void task_up(KA& a, const int32_t* w, int t, Lds& S) 
 }
 
 template <class C>
-__device__ __forceinline__ void task_down(KA& a, const int32_t* w, int t, Lds& S) {
+__device__ __forceinline__ void task_down(KA& a, Desc w, int t, Lds& S) {
   const int l = w[W_LAYER], s = w[W_A], r0 = w[W_R0], r1 = w[W_R1];
   const int d = a.d, F = a.F, nr = r1 - r0;
-  wait_deps(a, w, 0, 1, t);  // routing is known: this expert's weights can stream before its hidden state exists
-  if (load_slot(a, l, s, S)) {
-    const int e = S.slot_e, n = S.slot_n;
+  // the slot's routing is known: this expert's weights stream before its hidden state exists
+  const int e = slot_routing(a, wait_value(a, w, 0, t, S), S);
+  if (e >= 0) {
+    const int n = S.slot_n;
     const uint16_t* W = a.layers[l].w_down + ((int64_t)e * d + r0) * F;
+    const int32_t* ent = a.slots + ((int64_t)l * a.n_slots + s) * SLOT_WORDS;
     mgemv_task<true>(
         a, w, t, Rows1{W, F}, nr, F, n, 1, N_WAITS,
         [&] {
-          for (int i = threadIdx.x; i < n * F; i += NT) S.xs[i] = a.h[(int64_t)s * a.B * F + i];
+          // hidden state of the slot's tokens, and their selection ranks and gates
+          if (tidx() < SLOT_WORDS) S.slotw[tidx()] = ent[tidx()];
+          for (int i = tidx(); i < n * F; i += NT) S.xs[i] = a.h[(int64_t)s * a.B * F + i];
+          __syncthreads();
+          if (tidx() < n) {
+            S.slot_j[tidx()] = S.slotw[3 + 3 * tidx()];
+            S.slot_g[tidx()] = __int_as_float(S.slotw[4 + 3 * tidx()]);
+          }
           __syncthreads();
         },
         [&](int r, int j, float v) { pub(a.ypart + ((int64_t)S.slot_b[j] * a.k + S.slot_j[j]) * d + r0 + r, S.slot_g[j] * v); }, S);
-  } else {
-    wait_deps(a, w, 1, N_WAITS, t);
   }
-  resid_chain(a, w, l, S);
+  resid_chain(a, w, S);
 }
 
 template <class C>
-__device__ __forceinline__ void task_lmhead(KA& a, const int32_t* w, int t, Lds& S) {
+__device__ __forceinline__ void task_lmhead(KA& a, Desc w, int t, Lds& S) {
   const int r0 = w[W_R0], r1 = w[W_R1], tile = w[W_A];
   const int d = a.d, B = a.B, nr = r1 - r0;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tidx() >> 6, lane = tidx() & 63;
   const uint16_t* W = a.lm_head + (int64_t)r0 * d;
   float* tl = S.sc;  // this tile's logits [row][token], row < 128
-  mgemv_task<false>(
-      a, w, t, Rows1{W, d}, nr, d, B, 0, N_WAITS, [&] { stage_nhl(a, B, nullptr, S); },
+  const NormGain gn = norm_gain(a.final_norm, d);
+  mgemv_task<true>(
+      a, w, t, Rows1{W, d}, nr, d, B, 0, N_WAITS, [&] { stage_norm(a, gn, B, nullptr, S); },
       [&](int r, int b, float v) {
         a.logits[(int64_t)b * a.V + r0 + r] = v;
         tl[r * 8 + b] = v;
@@ -866,12 +901,14 @@ __device__ __forceinline__ void task_lmhead(KA& a, const int32_t* w, int t, Lds&
 // Split s of (sequence b, KV group g) covers positions [j0, j1) of the sequence's 0..len window (len =
 // its prior length; position len is the new token, taken from this step's projections, RoPE'd, rounded
 // to BF16 and written to the cache by the split that holds it).  The split's page list and its first
-// chunk of K and V (256 positions) are loaded BEFORE the task waits for this step's queries.  Each thread
-// owns one 8-dim slice of NP positions of a chunk: it forms the scores of every head of the group for
-// its positions (queries in registers, slice sums by DPP), and after the chunk's softmax it accumulates
-// p * V for its slice and positions.  The per-thread partial outputs are reduced once per split.
+// chunk of K and V (128 positions) are loaded BEFORE the task waits for this step's queries.  Scores run
+// on MFMA: each wave takes 16 positions of a chunk with K as the A operand (as stored) and the group's
+// RoPE'd, scaled queries as BF16 hi + lo B operands held in registers for the whole split.  After the
+// chunk's online softmax (one wave per head), each thread accumulates p * V for a 4-dim slice of its
+// positions; the next chunk's K/V loads are in flight meanwhile.  The per-thread partial outputs are
+// reduced once per split, and the last split of (b, g) to finish merges all splits.
 template <int DH, int GRP>
-__device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& S) {
+__device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
   constexpr int DPT = 4;            // V / output dims per thread slice
   constexpr int SL = DH / DPT;      // slices per position (32 or 16)
   constexpr int PPP = NT / SL;      // positions per V pass (16 or 32)
@@ -880,7 +917,7 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
   constexpr int NKK = DH / 32;      // MFMA k-steps over the head dim
   static_assert(CH == NW * 16, "one 16-position score block per wave");
   const int l = w[W_LAYER], b = w[W_A], g = w[W_B], s = w[W_C], nsplit = w[W_D];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = tidx(), wave = tid >> 6, lane = tid & 63;
   const int sl = tid % SL, pp = tid / SL;
   const int Hkv = a.Hkv;
   int len = a.seq_lens[b];
@@ -933,9 +970,11 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
       vv[i] = base >= 0 ? __builtin_nontemporal_load(as_global2(kvl + base + vstride + sl * DPT)) : u2{0, 0};
     }
   };
-  u4 kc[NKK];
-  u2 vc[NP];
-  load_chunk(j0, kc, vc);  // old K/V stream while this step's projections are produced
+  u4 kc[NKK], kx[NKK];
+  u2 vc[NP], vx[NP];
+  // the split's first two chunks of old K/V stream while this step's projections are produced
+  load_chunk(j0, kc, vc);
+  load_chunk(j0 + CH, kx, vx);
 
   wait_deps(a, w, 0, N_WAITS, t);
 
@@ -1004,10 +1043,6 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
     for (int i = 0; i < DPT; ++i) o[h][i] = 0.f;
 
   for (int c0 = j0; c0 < jc1; c0 += CH) {
-    u4 kn_[NKK];
-    u2 vn_[NP];
-    const bool more = c0 + CH < jc1;
-    if (more) load_chunk(c0 + CH, kn_, vn_);  // next chunk in flight while this one is processed
     // scores on MFMA: D[position][head] = K (16 positions x 32 dims) times q^T (32 dims x heads), hi + lo
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1075,12 +1110,12 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
         for (int e = 0; e < DPT; ++e) o[h][e] = fmaf(pr[h], vf[e], o[h][e]);
     }
     __syncthreads();
-    if (more) {
+    // rotate: the next chunk is in flight or has landed; request the one after it
 #pragma unroll
-      for (int q = 0; q < NKK; ++q) kc[q] = kn_[q];
+    for (int q = 0; q < NKK; ++q) kc[q] = kx[q];
 #pragma unroll
-      for (int i = 0; i < NP; ++i) vc[i] = vn_[i];
-    }
+    for (int i = 0; i < NP; ++i) vc[i] = vx[i];
+    if (c0 + 2 * CH < jc1) load_chunk(c0 + 2 * CH, kx, vx);
   }
   mark(a, t, 1);
   // the new token
@@ -1191,7 +1226,7 @@ __device__ __forceinline__ void attn_split(KA& a, const int32_t* w, int t, Lds& 
 }
 
 template <class C>
-__device__ __forceinline__ void task_attn(KA& a, const int32_t* w, int t, Lds& S) {
+__device__ __forceinline__ void task_attn(KA& a, Desc w, int t, Lds& S) {
   attn_split<C::DH, C::GRP>(a, w, t, S);
 }
 
@@ -1201,11 +1236,11 @@ __device__ __forceinline__ void task_attn(KA& a, const int32_t* w, int t, Lds& S
 // that no field is hoisted out of the task loop (that would pin dozens of registers for the kernel's
 // whole life).
 template <class C>
-__device__ __forceinline__ void run_task(KA* a0, const int32_t* w, int t, uint32_t& nxt, Lds& S) {
+__device__ __forceinline__ void run_task(KA* a0, Desc w, int t, Lds& S) {
   KA* ap = a0;
   __asm__ volatile("" : "+s"(ap));
   KA& a = *ap;
-  const int tid = threadIdx.x;
+  const int tid = tidx();
   if (a.ts && tid == 0) {
     a.ts[(int64_t)t * 8 + 0] = wall_clock64();
     a.ts[(int64_t)t * 8 + 1] = 0;
@@ -1231,7 +1266,7 @@ __device__ __forceinline__ void run_task(KA* a0, const int32_t* w, int t, uint32
 
 // The last workgroup out resets the counters for the next step (stream order makes it visible).
 __device__ __forceinline__ void exit_step(KA& a, Lds& S) {
-  const int tid = threadIdx.x;
+  const int tid = tidx();
   __syncthreads();
   if (tid == 0) {
     const uint32_t old = __hip_atomic_fetch_add(&a.ctr[a.c_done], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1246,26 +1281,50 @@ __device__ __forceinline__ void exit_step(KA& a, Lds& S) {
   }
 }
 
+// Copy the descriptor at position pos of the task array into LDS: wave 0, lanes 0..7, 16 bytes each,
+// straight from global memory to LDS (no registers held while the copy is in flight; it completes under
+// vmcnt).
+__device__ __forceinline__ void fetch_desc(KA& a, int pos, int32_t* dst) {
+  const int lane = tidx() & 63;
+  if (tidx() < 64 && lane < DESC_WORDS / 4)
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.tasks + (int64_t)pos * DESC_WORDS + 4 * lane),
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
 template <class C>
 __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
   KA* const a0 = (KA*)(__builtin_amdgcn_kernarg_segment_ptr());
   (void)args;
   __shared__ Lds S;
-  const int tid = threadIdx.x;
+  const int tid = tidx();
   KA& a = *a0;
-  if (tid == 0) S.next = (int)__hip_atomic_fetch_add(&a.ctr[a.c_ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // this workgroup's claim queue: positions [base, base + count) of the task array, own ticket counter
+  const bool second = (int)blockIdx.x >= a.first_group;
+  const int base = second ? a.n_first : 0;
+  const int count = second ? a.n_tasks - a.n_first : a.n_first;
+  const int ticket = second ? a.c_ticket2 : a.c_ticket;
+  // first task: claim and fetch synchronously; then keep two claims and one descriptor ahead
+  if (tid == 0) S.next1 = (int)__hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  for (;;) {
-    const int t = S.next;
+  int i = S.next1;
+  if (i < count) fetch_desc(a, base + i, S.desc[0]);
+  if (tid == 0) S.next1 = (int)__hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  drain_stores();
+  __syncthreads();
+  int cur = 0;
+  while (i < count) {
+    const int i1 = S.next1;
     __syncthreads();
-    if (t >= a.n_tasks) break;
-    // claim the next task now; its ticket returns while this one runs
-    uint32_t nxt = 0;
-    if (tid == 0) nxt = __hip_atomic_fetch_add(&a.ctr[a.c_ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int32_t* w = a.tasks + (int64_t)t * DESC_WORDS;
-    run_task<C>(a0, w, t, nxt, S);
-    if (tid == 0) S.next = (int)nxt;
+    if (i1 < count) fetch_desc(a, base + i1, S.desc[cur ^ 1]);
+    uint32_t i2 = 0;
+    if (tid == 0) i2 = __hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const Desc w{S.desc[cur]};
+    run_task<C>(a0, w, w[W_SEQ], S);
+    drain_stores();  // the next descriptor has landed in LDS, the claim has returned
+    if (tid == 0) S.next1 = (int)i2;
     __syncthreads();
+    i = i1;
+    cur ^= 1;
   }
   exit_step(a, S);
 }

@@ -106,8 +106,8 @@ struct Emitter {
       w[W_WAIT0 + 2 * i + 1] = 0;
     }
     w[W_SIG] = -1;
+    w[W_SIGR] = 1;
     w[W_ARR] = -1;
-    w[W_ARR2] = -1;
     w[W_SEQ] = (int32_t)(o / DESC_WORDS);
     return w;
   }
@@ -121,14 +121,12 @@ void set_sig(int32_t* w, int32_t c, int32_t n = 1) {
   w[W_SIGN] = n;
 }
 // O-proj and expert-down tasks of row tile r of layer l: the last of the tile's producers adds the branch
-// partials into the residual stream (fixed order), and the last row tile of the layer publishes the next
-// layer's normalised input and signals XREADY[l+1].
+// partials into the residual stream (fixed order) and counts the row tile into XREADY[l+1]; the next
+// layer's consumers wait for all row tiles and normalise the residual stream themselves.
 void resid_epilogue(int32_t* w, const CounterLayout& cl, const Tiling& t, int l, int r, int producers) {
   w[W_RT] = r;
   w[W_ARR] = cl.resid_arrive + l * t.n_rt + r;
   w[W_ARRN] = producers;
-  w[W_ARR2] = cl.norm_arrive + l + 1;
-  w[W_ARRN2] = t.n_rt;
   set_sig(w, cl.xready + l + 1);
 }
 }  // namespace
@@ -172,8 +170,6 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
     w[W_R0] = r * t.rt;
     w[W_R1] = (r + 1) * t.rt;
     w[W_RT] = r;
-    w[W_ARR2] = cl.norm_arrive + 0;  // the last embedding tile publishes the layer-0 normalised input
-    w[W_ARRN2] = t.n_rt;
     set_sig(w, cl.xready + 0);
   }
   for (int l = 0; l < L; ++l) {
@@ -181,8 +177,10 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
       int32_t* w = em.add(OP_ROUTER, l);
       w[W_R0] = i * t.router_rows;
       w[W_R1] = std::min(E, (i + 1) * t.router_rows);
-      set_wait(w, 0, cl.xready + l, 1);
-      set_sig(w, cl.router_done + l);  // issued only by the tile that arrives last, after it routed the layer
+      set_wait(w, 0, cl.xready + l, t.n_rt);
+      // issued only by the tile that arrives last, after it routed the layer: one counter per expert slot
+      set_sig(w, cl.slot_ready + l * P->n_slots);
+      w[W_SIGR] = P->n_slots;
       w[W_ARR] = cl.router_arrive + l;
       w[W_ARRN] = t.n_router;
     }
@@ -192,7 +190,7 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
         w[W_A] = g;
         w[W_R0] = i * t.qkv_rows;
         w[W_R1] = (i + 1) * t.qkv_rows;
-        set_wait(w, 0, cl.xready + l, 1);
+        set_wait(w, 0, cl.xready + l, t.n_rt);
         set_sig(w, cl.qkv_done + l * Hkv + g);
       }
     for (int g = 0; g < Hkv; ++g)
@@ -211,10 +209,11 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
     for (int s = 0; s < P->n_slots; ++s)
       for (int i = 0; i < t.n_up; ++i) {
         int32_t* w = em.add(OP_UP, l);
+        w[W_Q] = Q_MOE;
         w[W_A] = s;
         w[W_R0] = i * t.up_rows;
         w[W_R1] = (i + 1) * t.up_rows;
-        set_wait(w, 0, cl.router_done + l, 1);
+        set_wait(w, 0, cl.slot_ready + l * P->n_slots + s, 1);  // the slot's routing (expert, tokens)
         set_sig(w, cl.up_done + l * P->n_slots + s);
       }
     for (int g = 0; g < Hkv; ++g)
@@ -229,24 +228,34 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
     for (int s = 0; s < P->n_slots; ++s)
       for (int r = 0; r < t.n_rt; ++r) {
         int32_t* w = em.add(OP_DOWN, l);
+        w[W_Q] = Q_MOE;
         w[W_A] = s;
         w[W_R0] = r * t.rt;
         w[W_R1] = (r + 1) * t.rt;
-        set_wait(w, 0, cl.router_done + l, 1);                      // routing known: expert weights can stream
+        set_wait(w, 0, cl.slot_ready + l * P->n_slots + s, 1);     // routing known: expert weights can stream
         set_wait(w, 1, cl.up_done + l * P->n_slots + s, t.n_up);    // this expert's hidden state is complete
         resid_epilogue(w, cl, t, l, r, Hkv + P->n_slots);
       }
   }
   for (int i = 0; i < t.n_lm; ++i) {
     int32_t* w = em.add(OP_LMHEAD, L);
+    w[W_Q] = Q_ANY;  // the launcher shares the vocabulary tiles between both workgroup groups
     w[W_A] = i;
     w[W_R0] = i * t.lm_rows;
     w[W_R1] = std::min(d->vocab, (i + 1) * t.lm_rows);
-    set_wait(w, 0, cl.xready + L, 1);
+    set_wait(w, 0, cl.xready + L, t.n_rt);
     w[W_ARR] = cl.lm_arrive;
     w[W_ARRN] = t.n_lm;
   }
   (void)grp;
+  // HBM bytes of each queue, to size the two workgroup groups: attention-branch weights, router and KV
+  // read, versus the weights of the distinct experts a step can select
+  const double dh = d->d_head, dm = d->d_model;
+  const double attn_w = 2.0 * dm * (2.0 * d->n_q_heads * dh + 2.0 * Hkv * dh) + 2.0 * E * dm + 2.0 * dm;
+  double kv = 0;
+  for (int b = 0; b < B; ++b) kv += ((double)batch->seq_lens[b] + 1) * 2.0 * Hkv * dh * 2.0;
+  P->bytes_attn = L * (attn_w + kv);
+  P->bytes_moe = (double)L * P->n_slots * 3.0 * d->d_ffn * dm * 2.0;
   return MK_OK;
 }
 
