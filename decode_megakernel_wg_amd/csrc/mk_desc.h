@@ -17,7 +17,7 @@ enum Op : int32_t {
   OP_OPROJ = 6,   // rows [r0, r1) of Wo restricted to group g's columns; residual epilogue (see below)
   OP_DOWN = 7,    // rows [r0, r1) of expert slot s's down projection, times the gate; residual epilogue
   OP_RESID = 8,   // (reserved: the residual add is the epilogue of the last O-proj / down task of a row tile)
-  OP_LMHEAD = 9,  // logits for vocab rows [r0, r1); tile argmax; last arriver picks the next tokens
+  OP_LMHEAD = 9,  // (reserved: the LM head runs as the kernel's closing phase over a shared chunk pool)
   OP_COUNT = 10
 };
 
@@ -54,12 +54,13 @@ constexpr int DESC_WORDS = 32;
 constexpr int ATTN_SPLIT_POS = 256;  // positions per attention split (before clamping)
 constexpr int ATTN_MAX_SPLIT_PAGES = 256;  // pages one split may cover (its page list is staged in LDS)
 constexpr int ATTN_MAX_SPLITS = 256;
-constexpr int SLOT_WORDS = 32;  // routing table entry per expert slot: expert, token count, (token, rank, gate) x 8
+constexpr int SLOT_WORDS = 32;
+constexpr int LM_MAX_WG = 1024;  // most workgroups a launch may have (stride of the LM head's per-workgroup bests)  // routing table entry per expert slot: expert, token count, (token, rank, gate) x 8
 
 // Counter index layout for a model/batch; computed identically by planner and host launcher.
 struct CounterLayout {
   int32_t ticket, ticket2, done, xready, qkv_done, router_arrive, slot_ready, attn_arrive, attn_done, up_done, resid_arrive, lm_arrive,
-      total;
+      lm_pool, total;
   int32_t n_layers, n_kv, n_slots, n_row_tiles, batch;
   void build(int L, int Hkv, int B, int slots, int nrt) {
     n_layers = L;
@@ -80,6 +81,7 @@ struct CounterLayout {
     up_done = o; o += L * slots;
     resid_arrive = o; o += L * nrt;
     lm_arrive = o; o += 1;
+    lm_pool = o; o += 1;     // next unclaimed 128-row vocabulary chunk of the LM head
     total = (o + 31) & ~31;
   }
 };

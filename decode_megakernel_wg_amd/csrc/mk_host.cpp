@@ -140,7 +140,7 @@ int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out
   m->desc.router_bias = nullptr;
   HIPCHK(hipGetDevice(&m->device));
   HIPCHK(hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, m->device));
-  m->grid = m->n_cu;
+  m->grid = std::min(m->n_cu, mk::LM_MAX_WG);
   m->tiling = mk::choose_tiling(desc);
   const mk::Tiling& t = m->tiling;
   const int d = desc->d_model, Hq = desc->n_q_heads, Hkv = desc->n_kv_heads, dh = desc->d_head, E = desc->n_experts;
@@ -176,8 +176,8 @@ int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out
       (rc = m->alloc(&m->attn_o, (size_t)maxB * Hq * dh)) || (rc = m->alloc(&m->opart, (size_t)Hkv * maxB * d)) ||
       (rc = m->alloc(&m->rlogits, (size_t)L * maxB * E)) || (rc = m->alloc(&m->route_sel, (size_t)L * maxB * k)) ||
       (rc = m->alloc(&m->route_gate, (size_t)L * maxB * k)) || (rc = m->alloc(&m->h, (size_t)m->max_slots * maxB * F)) ||
-      (rc = m->alloc(&m->ypart, (size_t)maxB * k * d)) || (rc = m->alloc(&m->lmbest_v, (size_t)maxB * t.n_lm)) ||
-      (rc = m->alloc(&m->lmbest_i, (size_t)maxB * t.n_lm)) || (rc = m->alloc(&m->next_tok, maxB)) ||
+      (rc = m->alloc(&m->ypart, (size_t)maxB * k * d)) || (rc = m->alloc(&m->lmbest_v, (size_t)maxB * mk::LM_MAX_WG)) ||
+      (rc = m->alloc(&m->lmbest_i, (size_t)maxB * mk::LM_MAX_WG)) || (rc = m->alloc(&m->next_tok, maxB)) ||
       (rc = m->alloc(&m->ctr_snapshot, m->max_counters)) ||
       (rc = m->alloc(&m->slots, (size_t)L * m->max_slots * mk::SLOT_WORDS)))
     return cleanup(rc);
@@ -231,7 +231,9 @@ static void lay_out_queues(mk_model* m) {
     const double fa = tot > 0 ? P.bytes_attn / tot : 0.5;
     int ga = (int)(fa * m->grid + 0.5);
     ga = std::max(1, std::min(m->grid - 1, ga));
-    const int64_t lm_first = (int64_t)((double)P.t.n_lm * ga / m->grid + 0.5);
+    int64_t n_any = 0;
+    for (int64_t i = 0; i < n; ++i) n_any += src[i * mk::DESC_WORDS + mk::W_Q] == mk::Q_ANY;
+    const int64_t lm_first = (int64_t)((double)n_any * ga / m->grid + 0.5);
     int64_t o = 0;
     for (int pass = 0; pass < 2; ++pass) {
       int64_t lm_seen = 0;
@@ -282,7 +284,9 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   a.n_slots = P.n_slots;
   a.max_pages = D.max_pages_per_seq;
   a.n_rt = P.t.n_rt;
-  a.n_lm = P.t.n_lm;
+  a.c_lm_pool = P.cl.lm_pool;
+  a.c_lm_arrive = P.cl.lm_arrive;
+  a.c_xfinal = P.cl.xready + D.n_layers;
   a.n_pages = D.n_pages;
   a.eps = D.rms_eps;
   a.n_tasks = (int32_t)P.n_tasks();
@@ -406,8 +410,8 @@ int mk_debug_read(mk_model* m, int kind, void* host_dst, int64_t bytes) {
 }
 
 int mk_set_grid(mk_model* m, int32_t n_workgroups) {
-  if (!m || n_workgroups < 0) return fail(MK_E_INVAL, "bad argument");
-  m->grid = n_workgroups == 0 ? m->n_cu : n_workgroups;
+  if (!m || n_workgroups < 0 || n_workgroups > mk::LM_MAX_WG) return fail(MK_E_INVAL, "n_workgroups outside 0..1024");
+  m->grid = n_workgroups == 0 ? std::min(m->n_cu, mk::LM_MAX_WG) : n_workgroups;
   return MK_OK;
 }
 

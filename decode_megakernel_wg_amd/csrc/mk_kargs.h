@@ -24,10 +24,11 @@ enum { ERRC_TIMEOUT = 1, ERRC_TOKEN = 2, ERRC_PAGE = 3, ERRC_SEQLEN = 4, ERRC_OP
 struct KArgs {
   // shape of the model and of this step
   int32_t L, d, Hq, Hkv, dh, E, k, F, V;
-  int32_t B, n_slots, max_pages, n_rt, n_lm;
+  int32_t B, n_slots, max_pages, n_rt;
   int64_t n_pages;
   float eps;
   int32_t n_tasks, n_counters, c_ticket, c_ticket2, c_done;
+  int32_t c_lm_pool, c_lm_arrive, c_xfinal;  // LM head: chunk pool, arrivals, readiness of the final residual stream
   int32_t n_first;      // tasks [0, n_first) form the first claim queue, [n_first, n_tasks) the second
   int32_t first_group;  // workgroups [0, first_group) claim from the first queue, the rest from the second
   // model (device)
@@ -60,8 +61,8 @@ struct KArgs {
   float* route_gate; // [L][B][k]
   float* h;          // [n_slots][B][F] SwiGLU hidden state per expert slot and token of the slot
   float* ypart;      // [B][k][d] gated expert outputs
-  float* lmbest_v;   // [B][n_lm] per-tile maximum logit
-  int32_t* lmbest_i; // [B][n_lm] its index
+  float* lmbest_v;   // [B][LM_MAX_WG] best logit per token found by each workgroup
+  int32_t* lmbest_i; // [B][LM_MAX_WG] its index
   int32_t* next_tok; // [max_batch]
   float* dump_n;     // [L][B][d] or null
   uint32_t* task_done;     // [n_tasks] or null

@@ -73,7 +73,7 @@ struct Lds {
   float hm[8], hl[8], hscale[8], pnew[8];
   float inv[8];          // per-token RMSNorm scale
   float ssqv[8 * 32];    // per-token partial sums of squares (row tiles)
-  float gu[2 * 32 * 8];  // UP: gate/up values [row][token]
+  float gu[2 * 64 * 8];  // UP: gate/up values [row][token] (up to 64 rows each)
   // routing of the current layer
   int sel[8 * 8];
   float gate[8 * 8];
@@ -82,6 +82,7 @@ struct Lds {
   float slot_g[8];
   int slotw[SLOT_WORDS];
   int32_t desc[2][DESC_WORDS];  // current and next task descriptor
+  int lmq[4];                   // LM head: ring of claimed vocabulary chunks
   uint32_t wval;                // value a wait observed (expert slot words)
   int next1, flag;
 };
@@ -508,18 +509,21 @@ __device__ __forceinline__ void split_x(int nb, int K, Lds& S) {
   __syncthreads();
 }
 
-// Prefetch, wait, stage, stream.  The first two passes of the tile (up to 2 x 16 KB per wave) are loaded
-// before the dependency wait [wait0, wait1), so weights stream while the inputs are still being produced.
-template <bool SPLIT, class RowPtr, class Stage, class Out>
+// Prefetch, wait, stage, stream.  The first AHEAD passes of the tile (16 KB per wave each) are requested
+// before the dependency wait [wait0, wait1), so weights stream while the inputs are still being produced;
+// afterwards pass p+1 is requested before pass p is computed.  A tile whose weights are known only at run
+// time (expert up-projection) requests one pass ahead, so that its inputs do not queue behind two passes.
+template <bool SPLIT, int AHEAD = 2, class RowPtr, class Stage, class Out>
 __device__ __forceinline__ void mgemv_task(KA& a, Desc w, int t, const RowPtr& W, int nrows, int K, int nb, int wait0,
                                            int wait1, Stage&& stage, Out&& out, Lds& S) {
   const MGeo g = mgeo(nrows, K);
   MBuf b0, b1;
   mg_load(b0, W, g, 0);
-  if (g.np > 1) mg_load(b1, W, g, 1);
+  if (AHEAD > 1 && g.np > 1) mg_load(b1, W, g, 1);
   wait_deps(a, w, wait0, wait1, t);
   stage();
   if (SPLIT) split_x(nb, K, S);
+  if (AHEAD == 1 && g.np > 1) mg_load(b1, W, g, 1);
   mark(a, t, 0);
   f4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int p = 0; p < g.np; p += 2) {
@@ -749,10 +753,8 @@ __device__ __forceinline__ void task_oproj(KA& a, Desc w, int t, Lds& S) {
   mgemv_task<true>(
       a, w, t, Rows1{W, ldo}, r1 - r0, K, B, 0, N_WAITS,
       [&] {
-        for (int i = tidx(); i < B * K; i += NT) {
-          const int b = i / K, c = i - b * K;
-          S.xs[i] = a.attn_o[(int64_t)b * ldo + (int64_t)g * K + c];
-        }
+        for (int b = 0; b < B; ++b) lds_copy(a.attn_o + (int64_t)b * ldo + (int64_t)g * K, S.xs + b * K, K / 4);
+        drain_stores();
         __syncthreads();
       },
       [&](int r, int b, float v) { pub(out + (int64_t)b * d + r, v); }, S);
@@ -782,15 +784,22 @@ __device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
   const int d = a.d, F = a.F, nr = r1 - r0;
   const LayerW& L = a.layers[l];
   const NormGain gn = norm_gain(L.attn_norm, d);
+  // the layer's expert tables are read before the wait, so the weight requests follow it immediately
+  const uint16_t* wg0 = L.w_gate;
+  const uint16_t* wu0 = L.w_up;
+  __asm__ volatile("" ::"s"(wg0), "s"(wu0));
   const int e = slot_routing(a, wait_value(a, w, 0, t, S), S);
   if (e >= 0) {
     const int n = S.slot_n;
     // gate rows then up rows of this tile, as one 2*nr-row tile over two bases; the expert is known only
     // now, so its weights stream while the slot's inputs are normalised into LDS
-    const uint16_t* Wg = L.w_gate + ((int64_t)e * F + r0) * d;
-    const uint16_t* Wu = L.w_up + ((int64_t)e * F + r0) * d;
-    mgemv_task<true>(
-        a, w, t, Rows2{Wg, Wu, d, nr}, 2 * nr, d, n, 0, 0, [&] { stage_norm(a, gn, n, S.slot_b, S); },
+    const uint16_t* Wg = wg0 + ((int64_t)e * F + r0) * d;
+    const uint16_t* Wu = wu0 + ((int64_t)e * F + r0) * d;
+    mgemv_task<true, 1>(
+        a, w, t, Rows2{Wg, Wu, d, nr}, 2 * nr, d, n, 0, 0, [&] {
+          mark(a, t, 2);  // weights requested
+          stage_norm(a, gn, n, S.slot_b, S);
+        },
         [&](int r, int b, float v) { S.gu[r * 8 + b] = v; }, S);
     __syncthreads();
     for (int i = tidx(); i < nr * n; i += NT) {
@@ -807,18 +816,21 @@ template <class C>
 __device__ __forceinline__ void task_down(KA& a, Desc w, int t, Lds& S) {
   const int l = w[W_LAYER], s = w[W_A], r0 = w[W_R0], r1 = w[W_R1];
   const int d = a.d, F = a.F, nr = r1 - r0;
+  const uint16_t* wd0 = a.layers[l].w_down;
+  __asm__ volatile("" ::"s"(wd0));
   // the slot's routing is known: this expert's weights stream before its hidden state exists
   const int e = slot_routing(a, wait_value(a, w, 0, t, S), S);
   if (e >= 0) {
     const int n = S.slot_n;
-    const uint16_t* W = a.layers[l].w_down + ((int64_t)e * d + r0) * F;
+    const uint16_t* W = wd0 + ((int64_t)e * d + r0) * F;
     const int32_t* ent = a.slots + ((int64_t)l * a.n_slots + s) * SLOT_WORDS;
     mgemv_task<true>(
         a, w, t, Rows1{W, F}, nr, F, n, 1, N_WAITS,
         [&] {
           // hidden state of the slot's tokens, and their selection ranks and gates
           if (tidx() < SLOT_WORDS) S.slotw[tidx()] = ent[tidx()];
-          for (int i = tidx(); i < n * F; i += NT) S.xs[i] = a.h[(int64_t)s * a.B * F + i];
+          lds_copy(a.h + (int64_t)s * a.B * F, S.xs, n * F / 4);
+          drain_stores();
           __syncthreads();
           if (tidx() < n) {
             S.slot_j[tidx()] = S.slotw[3 + 3 * tidx()];
@@ -831,68 +843,150 @@ __device__ __forceinline__ void task_down(KA& a, Desc w, int t, Lds& S) {
   resid_chain(a, w, S);
 }
 
-template <class C>
-__device__ __forceinline__ void task_lmhead(KA& a, Desc w, int t, Lds& S) {
-  const int r0 = w[W_R0], r1 = w[W_R1], tile = w[W_A];
-  const int d = a.d, B = a.B, nr = r1 - r0;
+// LM head, the kernel's closing phase (not a task): once a workgroup's claim queue is exhausted it takes
+// 128-row vocabulary chunks from a shared pool (one atomic per chunk, claimed ahead of use) and streams
+// them as 16 KB-per-wave passes, each requested two passes before its use, so every compute unit keeps
+// reading until the vocabulary is done, whatever its share of the layers was.  Its first chunk is
+// requested before it waits for the final residual stream.  Each workgroup publishes its best logit per
+// token (maximum, lowest index on ties: an order-independent choice); the last one to finish reduces them
+// to the next tokens.
+__device__ __forceinline__ void lm_phase(KA& a, Lds& S) {
+  constexpr int CHR = 128;  // rows per chunk: one 16-row block per wave, no K split
+  constexpr int LMQ = 4;    // ring of claimed chunk ids
+  const int d = a.d, B = a.B, V = a.V;
   const int wave = tidx() >> 6, lane = tidx() & 63;
-  const uint16_t* W = a.lm_head + (int64_t)r0 * d;
-  float* tl = S.sc;  // this tile's logits [row][token], row < 128
+  const MGeo g = mgeo(CHR, d);
+  const int np = g.np, nch = (V + CHR - 1) / CHR;
+  const int ahead = np >= 2 ? 2 : 3;  // chunks claimed ahead, so pass q + 2 always has its chunk id
   const NormGain gn = norm_gain(a.final_norm, d);
-  mgemv_task<true>(
-      a, w, t, Rows1{W, d}, nr, d, B, 0, N_WAITS, [&] { stage_norm(a, gn, B, nullptr, S); },
-      [&](int r, int b, float v) {
-        a.logits[(int64_t)b * a.V + r0 + r] = v;
-        tl[r * 8 + b] = v;
-      },
-      S);
+  if (tidx() == 0)
+    for (int k = 0; k < ahead; ++k)
+      S.lmq[k] = (int)__hip_atomic_fetch_add(&a.ctr[a.c_lm_pool], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (wave < B) {  // tile maximum per token, lowest index among equals
-    const int b = wave;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int r = lane; r < nr; r += 64) {
-      const float v = tl[r * 8 + b];
-      if (v > bv) {
-        bv = v;
-        bi = r0 + r;
+  auto load = [&](MBuf& buf, int q) {
+    const int k = q / np, p = q - k * np;
+    const int id = S.lmq[k % LMQ];
+    if (id >= nch) return;
+    MGeo gc = g;
+    gc.nrows = min(CHR, V - id * CHR);
+    mg_load(buf, Rows1{a.lm_head + (int64_t)id * CHR * d, d}, gc, p);
+  };
+  MBuf b0, b1;
+  const bool any = S.lmq[0] < nch;
+  if (any) {
+    load(b0, 0);
+    load(b1, 1);
+  }
+  if (tidx() == 0) {
+    spin_ge(a, a.c_xfinal, a.n_rt, -1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  float bv = -INFINITY;  // best of this lane's token so far
+  int bi = 0x7fffffff;
+  if (any) {
+    stage_norm(a, gn, B, nullptr, S);
+    split_x(B, d, S);
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    uint32_t pend = 0;
+    bool done = false;
+    // pass q: compute, then request pass q + 2 into the same buffer
+    auto comp = [&](MBuf& buf, int q) {
+      const int k = q / np, p = q - k * np;
+      if (p == 0) {
+        // chunk k starts: publish the claim made at the start of chunk k - 1, claim chunk k + ahead
+        if (k > 0) {
+          if (tidx() == 0) S.lmq[(k - 1 + ahead) % LMQ] = (int)pend;
+          __syncthreads();
+        }
+        if (tidx() == 0) pend = __hip_atomic_fetch_add(&a.ctr[a.c_lm_pool], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        acc = f4{0.f, 0.f, 0.f, 0.f};
       }
-    }
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
+      const int id = S.lmq[k % LMQ];
+      if (id >= nch) {
+        done = true;
+        return;
       }
-    }
-    if (lane == 0) {
-      pub(&a.lmbest_v[b * a.n_lm + tile], bv);
-      pubi(&a.lmbest_i[b * a.n_lm + tile], bi);
+      mg_compute(buf, acc, g, p, B, S);
+      if (p == np - 1) {
+        const int j = lane & 15, qd = lane >> 4;
+        if (j < B) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = id * CHR + wave * 16 + 4 * qd + r;
+            if (row < V) {
+              const float v = acc[r];
+              a.logits[(int64_t)j * V + row] = v;
+              if (v > bv || (v == bv && row < bi)) {
+                bv = v;
+                bi = row;
+              }
+            }
+          }
+        }
+      }
+      load(buf, q + 2);
+    };
+    for (int q = 0; !done; q += 2) {
+      comp(b0, q);
+      if (done) break;
+      comp(b1, q + 1);
     }
   }
-  if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) {
+  // this workgroup's best per token: the 4 lanes of a token in each wave, then the waves in order
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  float* wbv = S.sc;                                  // [NW][16]
+  int* wbi = reinterpret_cast<int*>(S.sc + NW * 16);  // [NW][16]
+  if (lane < 16) {
+    wbv[wave * 16 + lane] = bv;
+    wbi[wave * 16 + lane] = bi;
+  }
+  __syncthreads();
+  if (tidx() < B) {
+    const int b = tidx();
+    float v = -INFINITY;
+    int ix = 0x7fffffff;
+    for (int q = 0; q < NW; ++q) {
+      const float ov = wbv[q * 16 + b];
+      const int oi = wbi[q * 16 + b];
+      if (ov > v || (ov == v && oi < ix)) {
+        v = ov;
+        ix = oi;
+      }
+    }
+    pub(&a.lmbest_v[b * LM_MAX_WG + blockIdx.x], v);
+    pubi(&a.lmbest_i[b * LM_MAX_WG + blockIdx.x], ix);
+  }
+  if (arrive_last(a, a.c_lm_arrive, gridDim.x, S)) {
     if (wave < B) {
       const int b = wave;
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int q = lane; q < a.n_lm; q += 64) {
-        const float v = a.lmbest_v[b * a.n_lm + q];
-        const int i = a.lmbest_i[b * a.n_lm + q];
-        if (v > bv || (v == bv && i < bi)) {
-          bv = v;
-          bi = i;
+      float v = -INFINITY;
+      int ix = 0x7fffffff;
+      for (int q = lane; q < (int)gridDim.x; q += 64) {
+        const float ov = a.lmbest_v[b * LM_MAX_WG + q];
+        const int oi = a.lmbest_i[b * LM_MAX_WG + q];
+        if (ov > v || (ov == v && oi < ix)) {
+          v = ov;
+          ix = oi;
         }
       }
       for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
+        const float ov = __shfl_xor(v, o);
+        const int oi = __shfl_xor(ix, o);
+        if (ov > v || (ov == v && oi < ix)) {
+          v = ov;
+          ix = oi;
         }
       }
-      if (lane == 0) a.next_tok[b] = bi;
+      if (lane == 0) a.next_tok[b] = ix;
     }
   }
 }
@@ -1256,7 +1350,6 @@ __device__ __forceinline__ void run_task(KA* a0, Desc w, int t, Lds& S) {
     case OP_UP: task_up<C>(a, w, t, S); break;
     case OP_OPROJ: task_oproj<C>(a, w, t, S); break;
     case OP_DOWN: task_down<C>(a, w, t, S); break;
-    case OP_LMHEAD: task_lmhead<C>(a, w, t, S); break;
     default:
       if (tid == 0) raise_error(a, ERRC_OPCODE, t);
   }
@@ -1326,6 +1419,7 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
     i = i1;
     cur ^= 1;
   }
+  lm_phase(*(KA*)a0, S);
   exit_step(a, S);
 }
 

@@ -87,7 +87,7 @@ Tiling choose_tiling(const mk_model_desc* d) {
   t.n_router = (d->n_experts + t.router_rows - 1) / t.router_rows;
   t.up_rows = 16;
   t.n_up = d->d_ffn / t.up_rows;
-  t.lm_rows = 128;
+  t.lm_rows = 128;  // vocabulary chunk of the LM head's closing phase
   t.n_lm = (d->vocab + t.lm_rows - 1) / t.lm_rows;
   return t;
 }
@@ -236,16 +236,6 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
         set_wait(w, 1, cl.up_done + l * P->n_slots + s, t.n_up);    // this expert's hidden state is complete
         resid_epilogue(w, cl, t, l, r, Hkv + P->n_slots);
       }
-  }
-  for (int i = 0; i < t.n_lm; ++i) {
-    int32_t* w = em.add(OP_LMHEAD, L);
-    w[W_Q] = Q_ANY;  // the launcher shares the vocabulary tiles between both workgroup groups
-    w[W_A] = i;
-    w[W_R0] = i * t.lm_rows;
-    w[W_R1] = std::min(d->vocab, (i + 1) * t.lm_rows);
-    set_wait(w, 0, cl.xready + L, t.n_rt);
-    w[W_ARR] = cl.lm_arrive;
-    w[W_ARRN] = t.n_lm;
   }
   (void)grp;
   // HBM bytes of each queue, to size the two workgroup groups: attention-branch weights, router and KV

@@ -16,7 +16,7 @@ struct Tiling {
   int qkv_rows;     // rows per QKV task (divides d_head)
   int router_rows;  // experts per ROUTER task
   int up_rows;      // d_ffn rows (of gate and of up) per UP task
-  int lm_rows;      // vocab rows per LMHEAD task
+  int lm_rows;      // vocabulary rows per chunk of the LM head's closing phase
   int n_qkv_per_group, n_router, n_up, n_lm;
 };
 

@@ -186,5 +186,5 @@ def test_task_counts_full_model():
     d = desc_for(W.FULL, B=1, pages=600, n_pages=600)
     tasks, _ = mk.mk_plan_tasks(d, [8192])
     ops = np.bincount(tasks[:, W_OP], minlength=10)
-    assert ops[OP_LMHEAD] == 262144 // 128
+    assert ops[OP_LMHEAD] == 0   # the LM head is the kernel's closing phase, not tasks
     assert ops[OP_ATTN] == 48 * 4 * -(-(8192 + 1) // 256)
