@@ -10,7 +10,7 @@ namespace mk {
 
 enum Op : int32_t {
   OP_EMBED = 1,   // x[b][rows] = embed[token_b][rows]; partial sum of squares of the rows  -> XREADY[0]
-  OP_ROUTER = 2,  // router logits for experts [r0, r1) (fp64 accumulation); the last tile routes -> SLOT_READY[l][*]
+  OP_ROUTER = 2,  // (reserved: router logits are partials of the residual row tiles; the last tile routes)
   OP_QKV = 3,     // rows [r0, r1) of KV group g's fused [q heads; k; v] projection     -> QKV_DONE[l][g]
   OP_ATTN = 4,    // split s of (sequence b, KV group g): partial softmax(qK^T)V; last arriver combines -> ATTN_DONE[l][g]
   OP_UP = 5,      // gate+up rows [r0, r1) of expert slot s, SwiGLU (waits SLOT_READY)     -> UP_DONE[l][s]
@@ -40,6 +40,10 @@ enum Word : int {
                 // written there is the slot's routing, at least 1)
   W_RT = 22,    // residual row tile of OPROJ / DOWN / EMBED tasks
   W_Q = 23,     // claim queue: Q_ATTN, Q_MOE, or Q_ANY (placed by the launcher)
+  W_ARR2 = 24,  // row-tile tasks: arrival counter of the next layer's router partials (-1 = none: last layer)
+  W_ARRN2 = 25, // arrivals expected there (row tiles)
+  W_RSIG = 26,  // first expert-slot counter of the next layer, signalled by the tile that routes it
+  W_RSIGR = 27, // expert slots
   W_SEQ = 31    // task index (debug)
 };
 constexpr int N_WAITS = 4;

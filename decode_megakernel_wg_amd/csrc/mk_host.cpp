@@ -60,6 +60,7 @@ struct mk_model {
   uint32_t* ctr = nullptr;
   uint32_t* err = nullptr;
   float *x = nullptr, *ssq = nullptr, *rope_cs = nullptr, *qkv = nullptr, *apart = nullptr, *attn_o = nullptr, *opart = nullptr;
+  double* rpart = nullptr;
   float *rlogits = nullptr, *route_gate = nullptr, *h = nullptr, *ypart = nullptr, *lmbest_v = nullptr, *dump_n = nullptr;
   int32_t *route_sel = nullptr, *lmbest_i = nullptr, *next_tok = nullptr, *slots = nullptr;
   uint32_t *task_done = nullptr, *ctr_snapshot = nullptr;
@@ -174,7 +175,7 @@ int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out
       (rc = m->alloc(&m->rope_cs, (size_t)maxB * dh)) || (rc = m->alloc(&m->qkv, (size_t)maxB * Hkv * (grp + 2) * dh)) ||
       (rc = m->alloc(&m->apart, (size_t)maxB * Hkv * mk::ATTN_MAX_SPLITS * grp * (dh + 2))) ||
       (rc = m->alloc(&m->attn_o, (size_t)maxB * Hq * dh)) || (rc = m->alloc(&m->opart, (size_t)Hkv * maxB * d)) ||
-      (rc = m->alloc(&m->rlogits, (size_t)L * maxB * E)) || (rc = m->alloc(&m->route_sel, (size_t)L * maxB * k)) ||
+      (rc = m->alloc(&m->rlogits, (size_t)L * maxB * E)) || (rc = m->alloc(&m->rpart, (size_t)t.n_rt * maxB * E)) || (rc = m->alloc(&m->route_sel, (size_t)L * maxB * k)) ||
       (rc = m->alloc(&m->route_gate, (size_t)L * maxB * k)) || (rc = m->alloc(&m->h, (size_t)m->max_slots * maxB * F)) ||
       (rc = m->alloc(&m->ypart, (size_t)maxB * k * d)) || (rc = m->alloc(&m->lmbest_v, (size_t)maxB * mk::LM_MAX_WG)) ||
       (rc = m->alloc(&m->lmbest_i, (size_t)maxB * mk::LM_MAX_WG)) || (rc = m->alloc(&m->next_tok, maxB)) ||
@@ -318,6 +319,7 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   a.attn_o = m->attn_o;
   a.opart = m->opart;
   a.rlogits = m->rlogits;
+  a.rpart = m->rpart;
   a.route_sel = m->route_sel;
   a.slots = m->slots;
   a.route_gate = m->route_gate;

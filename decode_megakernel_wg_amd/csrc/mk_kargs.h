@@ -56,6 +56,7 @@ struct KArgs {
   float* attn_o;     // [B][Hq*dh] merged attention output
   float* opart;      // [Hkv][B][d] O-projection partial per KV group
   float* rlogits;    // [L][B][E] router logits
+  double* rpart;     // [n_rt][B][E] router partials of the row tiles (the layer being routed)
   int32_t* route_sel;
   int32_t* slots;    // [L][n_slots][SLOT_WORDS] routing table: expert, token count, (token, rank, gate bits) x 8
   float* route_gate; // [L][B][k]

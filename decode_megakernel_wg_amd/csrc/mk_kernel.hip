@@ -359,14 +359,99 @@ __device__ __forceinline__ double dot8d(u4 w, const f4& x0, const f4& x1, double
   return acc;
 }
 
+// ------------------------------------------------------------------------------------------ routing
+// Done once per layer by the workgroup that completes the layer's router logits: top-k of each token's
+// router logits (logit descending, lower index first on ties; a NaN ranks lowest), gates = softmax of the
+// selected logits,
+// and the table of expert slots (slot s = the s-th distinct selected expert in ascending id, with the
+// tokens that chose it, their selection rank and gate).  Each slot's readiness counter (ctr[slot0 + s])
+// then receives the slot's expert and token mask (see slot_routing), so expert tasks learn their expert
+// from the wait itself.
+__device__ __forceinline__ void route_select(KA& a, int l, int32_t slot0, Lds& S) {
+  const int E = a.E, k = a.k, B = a.B, tid = tidx();
+  float* key = S.xs;  // [B][E] router logits with NaN replaced by -inf (filled by the caller)
+  if (tid < 8) S.used[tid] = 0u;
+  __syncthreads();
+  // rank of (b, e) among the token's logits (E is a multiple of 8: 4-wide LDS reads, unrolled)
+  for (int i = tid; i < B * E; i += NT) {
+    const int b = i / E, e = i - b * E;
+    const float v = key[i];
+    const float* kb = key + b * E;
+    int rank = 0;
+#pragma unroll 4
+    for (int q = 0; q < E; q += 4) {
+      const f4 u = *reinterpret_cast<const f4*>(kb + q);
+      rank += (u.x > v) || (u.x == v && q < e);
+      rank += (u.y > v) || (u.y == v && q + 1 < e);
+      rank += (u.z > v) || (u.z == v && q + 2 < e);
+      rank += (u.w > v) || (u.w == v && q + 3 < e);
+    }
+    if (rank < k) {
+      S.sel[b * 8 + rank] = e;
+      atomicOr(&S.used[e >> 5], 1u << (e & 31));
+    }
+  }
+  __syncthreads();
+  if (tid < B) {
+    const int b = tid;
+    const float mx = key[b * E + S.sel[b * 8]];
+    float z = 0.f;
+    for (int j = 0; j < k; ++j) z += expf(key[b * E + S.sel[b * 8 + j]] - mx);
+    for (int j = 0; j < k; ++j) {
+      const float gt = expf(key[b * E + S.sel[b * 8 + j]] - mx) / z;
+      S.gate[b * 8 + j] = gt;
+      pubi(&a.route_sel[((int64_t)l * B + b) * k + j], S.sel[b * 8 + j]);
+      pub(&a.route_gate[((int64_t)l * B + b) * k + j], gt);
+    }
+  }
+  __syncthreads();
+  // slot table (n_slots <= 64 < NT: thread s builds slot s and keeps its counter value)
+  uint32_t sv = 0;
+  for (int s = tid; s < a.n_slots; s += NT) {
+    int e = -1, cnt = 0;
+    for (int wd = 0; wd < 8 && e < 0; ++wd) {
+      const uint32_t m = S.used[wd];
+      const int pc = __popc(m);
+      if (cnt + pc > s) {
+        uint32_t mm = m;
+        for (int q = 0; q < s - cnt; ++q) mm &= mm - 1;
+        e = wd * 32 + __ffs(mm) - 1;
+      }
+      cnt += pc;
+    }
+    int32_t* ent = a.slots + ((int64_t)l * a.n_slots + s) * SLOT_WORDS;
+    int n = 0;
+    uint32_t mask = 0;
+    if (e >= 0)
+      for (int b = 0; b < B; ++b)
+        for (int j = 0; j < k; ++j)
+          if (S.sel[b * 8 + j] == e && n < 8) {
+            pubi(ent + 2 + 3 * n, b);
+            pubi(ent + 3 + 3 * n, j);
+            pubi(ent + 4 + 3 * n, __float_as_int(S.gate[b * 8 + j]));
+            mask |= 1u << b;
+            ++n;
+          }
+    pubi(ent + 0, e);
+    pubi(ent + 1, n);
+    sv = e >= 0 ? (mask << 16) | (uint32_t)(e + 1) : 0x80000000u;
+  }
+  // publish the entries, then release the slots (one counter each, value = routing)
+  drain_stores();
+  __syncthreads();
+  if (tid < a.n_slots && slot0 >= 0) __hip_atomic_store(&a.ctr[slot0 + tid], sv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Residual rows [r0, r1): x += sum over KV groups of the O-projection partials + sum over the k selections
 // of the gated expert outputs (fixed order: groups ascending, then selections ascending); the partial sum
 // of squares of each token's new rows goes to ssq[b][rt].  Every partial of a row is loaded before any is
-// added, so the whole update costs one round trip to memory.
+// added, so the whole update costs one round trip to memory.  The new rows stay in LDS at xs[B*n ...] for
+// the next layer's router partial.
 __device__ __forceinline__ void resid_rows(KA& a, int r0, int r1, int rt, Lds& S) {
   const int wave = tidx() >> 6, lane = tidx() & 63;
   const int d = a.d, B = a.B, n = r1 - r0, Hkv = a.Hkv, k = a.k;
-  float* sq = S.xs;  // [B][n] squares of the new rows
+  float* sq = S.xs;           // [B][n] squares of the new rows
+  float* xr = S.xs + B * n;   // [B][n] the new rows
   for (int i = tidx(); i < B * n; i += NT) {
     const int b = i / n, r = r0 + (i - b * n);
     const float xv = a.x[b * d + r];
@@ -385,6 +470,7 @@ __device__ __forceinline__ void resid_rows(KA& a, int r0, int r1, int rt, Lds& S
       if (j < k) v += yp[j];
     pub(&a.x[b * d + r], v);
     sq[i] = v * v;
+    xr[i] = v;
   }
   __syncthreads();
   if (wave < B) {
@@ -396,12 +482,137 @@ __device__ __forceinline__ void resid_rows(KA& a, int r0, int r1, int rt, Lds& S
   }
 }
 
-// End of an O-proj / expert-down task: the last producer of the row tile adds the partials into x and
-// signals the next layer's readiness counter (which waits for every row tile).
+// Router partial of one residual row tile for layer l: u[b][e] = sum over the tile's rows i of
+// W_router[l][e][i] * x[b][i] * gamma_l[i], accumulated in fp64 (each product is exact in fp64), in column
+// order per thread and then in a fixed tree over the threads of an expert.  The layer's router logit is
+// then inv_rms[b] * (sum of the row tiles' partials in tile order) + bias[e]: the RMSNorm scale is the one
+// factor that needs the whole residual stream, so the router runs as soon as the last row tile is done.
+// The router and gain slices are requested (router_pre) before the tile's residual update, so their
+// round trip overlaps that of the residual partials.
+constexpr int RP_MAXV = 8;  // 16-byte vectors of router weights per thread (64 columns)
+struct RouterPre {
+  u4 wv[RP_MAXV], gv[RP_MAXV];
+  int tpe, cols;
+};
+__device__ __forceinline__ void router_pre(KA& a, int l, int r0, int r1, RouterPre& rp) {
+  const int E = a.E, n = r1 - r0, d = a.d, tid = tidx();
+  int tpe = NT / E;  // threads per expert: a power of two, at least 8 columns each
+  while (tpe > 1 && n / tpe < 8) tpe >>= 1;
+  while (n / tpe > 8 * RP_MAXV) tpe <<= 1;
+  rp.tpe = tpe;
+  rp.cols = n / tpe;
+  const LayerW& L = a.layers[l];
+  if (tid < E * tpe) {
+    const int e = tid / tpe, q = tid - e * tpe, c0 = q * rp.cols;
+    const uint16_t* wr = L.w_router + (int64_t)e * d + r0 + c0;
+    const uint16_t* gm = L.attn_norm + r0 + c0;
+#pragma unroll
+    for (int v = 0; v < RP_MAXV; ++v) {
+      if (8 * v < rp.cols) {
+        rp.wv[v] = *reinterpret_cast<const u4*>(wr + 8 * v);
+        rp.gv[v] = *reinterpret_cast<const u4*>(gm + 8 * v);
+      }
+    }
+  }
+}
+__device__ __forceinline__ void router_partial(KA& a, const RouterPre& rp, int r0, int r1, int rt, const float* xr) {
+  const int B = a.B, E = a.E, n = r1 - r0, tid = tidx(), tpe = rp.tpe, cols = rp.cols;
+  if (tid < E * tpe) {
+    const int e = tid / tpe, q = tid - e * tpe, c0 = q * cols;
+    double acc[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[b] = 0.0;
+#pragma unroll
+    for (int v = 0; v < RP_MAXV; ++v) {
+      if (8 * v < cols) {
+        const u4 wv = rp.wv[v], gv = rp.gv[v];
+        const float wf[8] = {bf_lo(wv.x), bf_hi(wv.x), bf_lo(wv.y), bf_hi(wv.y), bf_lo(wv.z), bf_hi(wv.z), bf_lo(wv.w), bf_hi(wv.w)};
+        const float gf[8] = {bf_lo(gv.x), bf_hi(gv.x), bf_lo(gv.y), bf_hi(gv.y), bf_lo(gv.z), bf_hi(gv.z), bf_lo(gv.w), bf_hi(gv.w)};
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          if (b < B) {
+            const float* xb = xr + b * n + c0 + 8 * v;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[b] = fma((double)wf[u], (double)xb[u] * (double)gf[u], acc[b]);
+          }
+        }
+      }
+    }
+    // fixed tree over the tpe threads of the expert (adjacent lanes)
+    for (int o = 1; o < tpe; o <<= 1)
+#pragma unroll
+      for (int b = 0; b < 8; ++b) acc[b] += __shfl_xor(acc[b], o);
+    if (q == 0)
+      for (int b = 0; b < B; ++b)
+        __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.rpart) + ((int64_t)rt * B + b) * E + e,
+                           (unsigned long long)__double_as_longlong(acc[b]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The workgroup that completes a layer's router partials: logits, then routing.  inv_rms[b] is formed from
+// the row tiles' partial sums of squares exactly as every consumer's RMSNorm forms it.
+__device__ __forceinline__ void route_from_partials(KA& a, int l, int32_t slot0, Lds& S) {
+  const int B = a.B, E = a.E, nrt = a.n_rt, d = a.d, tid = tidx();
+  if (tid < B * nrt) S.ssqv[tid] = a.ssq[tid];
+  const double* rp = a.rpart;
+  double* sums = reinterpret_cast<double*>(S.xs + B * E);  // [B][E], after the keys
+  for (int i = tid; i < B * E; i += NT) {
+    const int b = i / E, e = i - b * E;
+    double sum = 0.0;
+    int r = 0;
+    for (; r + 8 <= nrt; r += 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = rp[((int64_t)(r + u) * B + b) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; r < nrt; ++r) sum += rp[((int64_t)r * B + b) * E + e];
+    sums[i] = sum;
+  }
+  __syncthreads();
+  if (tid < B) {
+    float ss = 0.f;
+    for (int r = 0; r < nrt; ++r) ss += S.ssqv[tid * nrt + r];
+    S.inv[tid] = 1.0f / sqrtf(ss / (float)d + a.eps);
+  }
+  __syncthreads();
+  float* key = S.xs;
+  for (int i = tid; i < B * E; i += NT) {
+    const int b = i / E, e = i - b * E;
+    const float lg = (float)(sums[i] * (double)S.inv[b]) + a.router_bias[e];
+    pub(a.rlogits + ((int64_t)l * B + b) * E + e, lg);
+    key[i] = lg == lg ? lg : -INFINITY;
+  }
+  if (a.dump_n) {  // debug: the RMSNorm output this layer's consumers stage
+    const uint16_t* gm = a.layers[l].attn_norm;
+    for (int i = tid; i < B * d; i += NT) {
+      const int b = i / d, c = i - b * d;
+      a.dump_n[(int64_t)l * B * d + i] = a.x[i] * (bf2f(gm[c]) * S.inv[b]);
+    }
+  }
+  route_select(a, l, slot0, S);
+}
+
+// A row tile of layer lnext's input is complete (rows and sum of squares published): count it into the
+// layer's readiness counter, then add its router partial; the last row tile routes the layer.
+__device__ __forceinline__ void row_tile_done(KA& a, Desc w, int lnext, int r0, int r1, int rt, const float* xr,
+                                              const RouterPre& rp, Lds& S) {
+  signal(a, w[W_SIG], w[W_SIGN]);
+  if (w[W_ARR2] >= 0) {
+    router_partial(a, rp, r0, r1, rt, xr);
+    if (arrive_last(a, w[W_ARR2], w[W_ARRN2], S)) route_from_partials(a, lnext, w[W_RSIG], S);
+  }
+}
+
+// End of an O-proj / expert-down task: the last producer of the row tile adds the partials into x.
 __device__ __forceinline__ void resid_chain(KA& a, Desc w, Lds& S) {
   if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) {
-    resid_rows(a, w[W_R0], w[W_R1], w[W_RT], S);
-    signal(a, w[W_SIG], w[W_SIGN]);
+    const int r0 = w[W_R0], r1 = w[W_R1], lnext = w[W_LAYER] + 1;
+    RouterPre rp;
+    if (w[W_ARR2] >= 0) router_pre(a, lnext, r0, r1, rp);
+    resid_rows(a, r0, r1, w[W_RT], S);
+    row_tile_done(a, w, lnext, r0, r1, w[W_RT], S.xs + a.B * (r1 - r0), rp, S);
   }
 }
 
@@ -462,9 +673,11 @@ __device__ __forceinline__ void mg_compute(const MBuf& buf, f4& acc, const MGeo&
     const int s = pass * NKP + t;
     if (s < g.nks) {
       const int k = k0 + 32 * s;
-      u4 bh = *reinterpret_cast<const u4*>(xh + k);
-      u4 bl = *reinterpret_cast<const u4*>(xl + k);
-      if (!live) bh = bl = u4{0, 0, 0, 0};
+      u4 bh = u4{0, 0, 0, 0}, bl = u4{0, 0, 0, 0};
+      if (live) {  // only the columns of real tokens read LDS
+        bh = *reinterpret_cast<const u4*>(xh + k);
+        bl = *reinterpret_cast<const u4*>(xl + k);
+      }
       const bf16x8 av = __builtin_bit_cast(bf16x8, buf.v[t]);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bh), acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl), acc, 0, 0, 0);
@@ -572,98 +785,13 @@ __device__ __forceinline__ void gemv_run_f64(WBuf<NV, RPW>& buf0, int nrows, int
   }
 }
 
-// ------------------------------------------------------------------------------------------ routing
-// Done once per layer by the router tile that finishes last: top-k of each token's router logits (logit
-// descending, lower index first on ties; a NaN ranks lowest), gates = softmax of the selected logits,
-// and the table of expert slots (slot s = the s-th distinct selected expert in ascending id, with the
-// tokens that chose it, their selection rank and gate).  Each slot's readiness counter (ctr[slot0 + s])
-// then receives the slot's expert and token mask (see slot_routing), so expert tasks learn their expert
-// from the wait itself.
-__device__ __forceinline__ void route_layer(KA& a, int l, int32_t slot0, Lds& S) {
-  const int E = a.E, k = a.k, B = a.B, tid = tidx();
-  const float* lg = a.rlogits + (int64_t)l * B * E;
-  float* key = S.xs;  // [B][E] logits with NaN replaced by -inf
-  for (int i = tid; i < B * E; i += NT) {
-    const float v = lg[i];
-    key[i] = v == v ? v : -INFINITY;
-  }
-  if (tid < 8) S.used[tid] = 0u;
-  __syncthreads();
-  // rank of (b, e) among the token's logits (E is a multiple of 8: 4-wide LDS reads, unrolled)
-  for (int i = tid; i < B * E; i += NT) {
-    const int b = i / E, e = i - b * E;
-    const float v = key[i];
-    const float* kb = key + b * E;
-    int rank = 0;
-#pragma unroll 4
-    for (int q = 0; q < E; q += 4) {
-      const f4 u = *reinterpret_cast<const f4*>(kb + q);
-      rank += (u.x > v) || (u.x == v && q < e);
-      rank += (u.y > v) || (u.y == v && q + 1 < e);
-      rank += (u.z > v) || (u.z == v && q + 2 < e);
-      rank += (u.w > v) || (u.w == v && q + 3 < e);
-    }
-    if (rank < k) {
-      S.sel[b * 8 + rank] = e;
-      atomicOr(&S.used[e >> 5], 1u << (e & 31));
-    }
-  }
-  __syncthreads();
-  if (tid < B) {
-    const int b = tid;
-    const float mx = key[b * E + S.sel[b * 8]];
-    float z = 0.f;
-    for (int j = 0; j < k; ++j) z += expf(key[b * E + S.sel[b * 8 + j]] - mx);
-    for (int j = 0; j < k; ++j) {
-      const float gt = expf(key[b * E + S.sel[b * 8 + j]] - mx) / z;
-      S.gate[b * 8 + j] = gt;
-      pubi(&a.route_sel[((int64_t)l * B + b) * k + j], S.sel[b * 8 + j]);
-      pub(&a.route_gate[((int64_t)l * B + b) * k + j], gt);
-    }
-  }
-  __syncthreads();
-  // slot table (n_slots <= 64 < NT: thread s builds slot s and keeps its counter value)
-  uint32_t sv = 0;
-  for (int s = tid; s < a.n_slots; s += NT) {
-    int e = -1, cnt = 0;
-    for (int wd = 0; wd < 8 && e < 0; ++wd) {
-      const uint32_t m = S.used[wd];
-      const int pc = __popc(m);
-      if (cnt + pc > s) {
-        uint32_t mm = m;
-        for (int q = 0; q < s - cnt; ++q) mm &= mm - 1;
-        e = wd * 32 + __ffs(mm) - 1;
-      }
-      cnt += pc;
-    }
-    int32_t* ent = a.slots + ((int64_t)l * a.n_slots + s) * SLOT_WORDS;
-    int n = 0;
-    uint32_t mask = 0;
-    if (e >= 0)
-      for (int b = 0; b < B; ++b)
-        for (int j = 0; j < k; ++j)
-          if (S.sel[b * 8 + j] == e && n < 8) {
-            pubi(ent + 2 + 3 * n, b);
-            pubi(ent + 3 + 3 * n, j);
-            pubi(ent + 4 + 3 * n, __float_as_int(S.gate[b * 8 + j]));
-            mask |= 1u << b;
-            ++n;
-          }
-    pubi(ent + 0, e);
-    pubi(ent + 1, n);
-    sv = e >= 0 ? (mask << 16) | (uint32_t)(e + 1) : 0x80000000u;
-  }
-  // publish the entries, then release the slots (one counter each, value = routing)
-  drain_stores();
-  __syncthreads();
-  if (tid < a.n_slots && slot0 >= 0) __hip_atomic_store(&a.ctr[slot0 + tid], sv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ------------------------------------------------------------------------------------------ task bodies
 
 __device__ __forceinline__ void task_embed(KA& a, Desc w, int t, Lds& S) {
   const int wave = tidx() >> 6, lane = tidx() & 63;
   const int r0 = w[W_R0], r1 = w[W_R1], rt = w[W_A];
+  RouterPre rp;
+  if (w[W_ARR2] >= 0) router_pre(a, 0, r0, r1, rp);
   if (wave < a.B) {
     const int b = wave;
     int tok = a.tokens[b];
@@ -675,6 +803,7 @@ __device__ __forceinline__ void task_embed(KA& a, Desc w, int t, Lds& S) {
     for (int r = r0 + lane; r < r1; r += 64) {
       const float v = bf2f(a.embed[(int64_t)tok * a.d + r]);
       pub(&a.x[b * a.d + r], v);
+      S.xs[b * (r1 - r0) + r - r0] = v;
       acc = fmaf(v, v, acc);
     }
     const float s = wave_sum(acc);
@@ -692,7 +821,8 @@ __device__ __forceinline__ void task_embed(KA& a, Desc w, int t, Lds& S) {
       pub(&a.rope_cs[(b * half + j) * 2 + 1], (float)sn);
     }
   }
-  signal(a, w[W_SIG], w[W_SIGN]);
+  __syncthreads();
+  row_tile_done(a, w, 0, r0, r1, rt, S.xs, rp, S);
 }
 
 
@@ -714,34 +844,6 @@ __device__ __forceinline__ void task_qkv(KA& a, Desc w, int t, Lds& S) {
       a, w, t, Rows1{W, d}, r1 - r0, d, a.B, 0, N_WAITS, [&] { stage_norm(a, gn, a.B, nullptr, S); },
       [&](int r, int b, float v) { pub(out + b * bstride + r, v); }, S);
   signal(a, w[W_SIG], w[W_SIGN]);
-}
-
-template <class C>
-__device__ __forceinline__ void task_router(KA& a, Desc w, int t, Lds& S) {
-  const int l = w[W_LAYER], r0 = w[W_R0], r1 = w[W_R1];
-  const LayerW& L = a.layers[l];
-  const int d = a.d, nrows = r1 - r0, K8 = d >> 3;
-  const uint16_t* W = L.w_router + (int64_t)r0 * d;
-  float* lg = a.rlogits + (int64_t)l * a.B * a.E;
-  auto out = [&](int r, int b, double v) { pub(lg + b * a.E + r0 + r, (float)v + a.router_bias[r0 + r]); };
-  const NormGain gn = norm_gain(L.attn_norm, d);
-  auto go = [&](auto nvr) {
-    constexpr int NV = decltype(nvr)::nv, RPW = decltype(nvr)::rpw;
-    WBuf<NV, RPW> buf0;
-    gemv_load(buf0, Rows1{W, d}, nrows, K8, 0);
-    wait_deps(a, w, 0, N_WAITS, t);
-    stage_norm(a, gn, a.B, nullptr, S);
-    if (a.dump_n && r0 == 0)  // debug: the normalised input this layer routed on
-      for (int i = tidx(); i < a.B * d; i += NT) a.dump_n[(int64_t)l * a.B * d + i] = S.xs[i];
-    const int nb = a.B;
-    if (nb <= 1) gemv_run_f64<NV, RPW, 1>(buf0, nrows, d, S.xs, d, nb, out);
-    else if (nb <= 2) gemv_run_f64<NV, RPW, 2>(buf0, nrows, d, S.xs, d, nb, out);
-    else if (nb <= 4) gemv_run_f64<NV, RPW, 4>(buf0, nrows, d, S.xs, d, nb, out);
-    else gemv_run_f64<NV, RPW, 8>(buf0, nrows, d, S.xs, d, nb, out);
-  };
-  (void)K8;
-  go(NVR<C::NVD, 2>{});
-  if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) route_layer(a, l, w[W_SIG], S);
 }
 
 template <class C>
@@ -1344,7 +1446,6 @@ __device__ __forceinline__ void run_task(KA* a0, Desc w, int t, Lds& S) {
   }
   switch (w[W_OP]) {
     case OP_EMBED: task_embed(a, w, t, S); break;
-    case OP_ROUTER: task_router<C>(a, w, t, S); break;
     case OP_QKV: task_qkv<C>(a, w, t, S); break;
     case OP_ATTN: task_attn<C>(a, w, t, S); break;
     case OP_UP: task_up<C>(a, w, t, S); break;

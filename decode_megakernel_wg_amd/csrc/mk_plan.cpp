@@ -81,7 +81,7 @@ Tiling choose_tiling(const mk_model_desc* d) {
   Tiling t{};
   t.rt = d->d_model >= 1024 ? 128 : 32;
   t.n_rt = d->d_model / t.rt;
-  t.qkv_rows = 32;
+  t.qkv_rows = 64;
   t.n_qkv_per_group = (d->n_q_heads / d->n_kv_heads + 2) * d->d_head / t.qkv_rows;
   t.router_rows = std::min(d->n_experts, 16);
   t.n_router = (d->n_experts + t.router_rows - 1) / t.router_rows;
@@ -108,10 +108,21 @@ struct Emitter {
     w[W_SIG] = -1;
     w[W_SIGR] = 1;
     w[W_ARR] = -1;
+    w[W_ARR2] = -1;
+    w[W_RSIG] = -1;
     w[W_SEQ] = (int32_t)(o / DESC_WORDS);
     return w;
   }
 };
+// A task that completes a row tile of layer l's input also adds that tile's router partial for layer l
+// (none after the last layer); the last of the n_rt tiles routes layer l and releases its expert slots.
+void router_epilogue(int32_t* w, const CounterLayout& cl, const Tiling& t, int l) {
+  if (l >= cl.n_layers) return;
+  w[W_ARR2] = cl.router_arrive + l;
+  w[W_ARRN2] = t.n_rt;
+  w[W_RSIG] = cl.slot_ready + l * cl.n_slots;
+  w[W_RSIGR] = cl.n_slots;
+}
 void set_wait(int32_t* w, int i, int32_t c, int32_t target) {
   w[W_WAIT0 + 2 * i] = c;
   w[W_WAIT0 + 2 * i + 1] = target;
@@ -128,6 +139,7 @@ void resid_epilogue(int32_t* w, const CounterLayout& cl, const Tiling& t, int l,
   w[W_ARR] = cl.resid_arrive + l * t.n_rt + r;
   w[W_ARRN] = producers;
   set_sig(w, cl.xready + l + 1);
+  router_epilogue(w, cl, t, l + 1);
 }
 }  // namespace
 
@@ -171,19 +183,9 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
     w[W_R1] = (r + 1) * t.rt;
     w[W_RT] = r;
     set_sig(w, cl.xready + 0);
+    router_epilogue(w, cl, t, 0);
   }
   for (int l = 0; l < L; ++l) {
-    for (int i = 0; i < t.n_router; ++i) {
-      int32_t* w = em.add(OP_ROUTER, l);
-      w[W_R0] = i * t.router_rows;
-      w[W_R1] = std::min(E, (i + 1) * t.router_rows);
-      set_wait(w, 0, cl.xready + l, t.n_rt);
-      // issued only by the tile that arrives last, after it routed the layer: one counter per expert slot
-      set_sig(w, cl.slot_ready + l * P->n_slots);
-      w[W_SIGR] = P->n_slots;
-      w[W_ARR] = cl.router_arrive + l;
-      w[W_ARRN] = t.n_router;
-    }
     for (int g = 0; g < Hkv; ++g)
       for (int i = 0; i < t.n_qkv_per_group; ++i) {
         int32_t* w = em.add(OP_QKV, l);

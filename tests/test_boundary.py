@@ -13,8 +13,8 @@ from synth import workloads as W
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # descriptor words (mirrors the library's layout)
-W_OP, W_LAYER, W_A, W_B, W_C, W_D, W_R0, W_R1, W_WAIT0, W_SIG, W_SIGN, W_ARR, W_ARRN, W_SIGR, W_Q = (0, 1, 2, 3, 4, 5, 6, 7, 8, 16,
-                                                                                        17, 18, 19, 20, 23)
+W_OP, W_LAYER, W_A, W_B, W_C, W_D, W_R0, W_R1, W_WAIT0, W_SIG, W_SIGN, W_ARR, W_ARRN, W_SIGR = 0, 1, 2, 3, 4, 5, 6, 7, 8, 16, 17, 18, 19, 20
+W_Q, W_ARR2, W_ARRN2, W_RSIG, W_RSIGR = 23, 24, 25, 26, 27
 Q_ATTN, Q_MOE, Q_ANY = 0, 1, 2
 OP_ATTN, OP_LMHEAD = 4, 9
 
@@ -131,13 +131,19 @@ def simulate(tasks, n_counters, n_workers, rng, first_group=None):
 
 def complete(w, ctr):
     """Counter effects of a finished task: an arrival (only the last arriver goes on), then the signal of
-    W_SIGR consecutive counters (the router's expert-slot counters receive a routing value >= 1)."""
+    W_SIGR consecutive counters; a task that completes a residual row tile then arrives with its router
+    partial, and the last row tile releases the next layer's expert-slot counters (each receives a routing
+    value >= 1)."""
     if w[W_ARR] >= 0:
         ctr[w[W_ARR]] += 1
         if ctr[w[W_ARR]] != w[W_ARRN]:
             return
     if w[W_SIG] >= 0:
         ctr[w[W_SIG]:w[W_SIG] + w[W_SIGR]] += w[W_SIGN]
+    if w[W_ARR2] >= 0:
+        ctr[w[W_ARR2]] += 1
+        if ctr[w[W_ARR2]] == w[W_ARRN2]:
+            ctr[w[W_RSIG]:w[W_RSIG] + w[W_RSIGR]] += 1
 
 
 @pytest.mark.parametrize("name,B_lens", [("tiny", [128]), ("tiny", [5, 300, 17, 0]), ("full", [8192]),

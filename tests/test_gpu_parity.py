@@ -10,13 +10,14 @@ import numpy as np
 import pytest
 import torch
 
-from oracle_runner import OracleRun, rel_l2, top2_gap
+from oracle_runner import OracleRun, kth_gap, rel_l2, top2_gap
 from synth import workloads as W
 
 pytestmark = pytest.mark.gpu
 
 LOGIT_TOL = 1e-2
 TOKEN_GAP = 1e-2
+ROUTE_EPS = 1e-5   # teacher-forced routing: largest k-th logit gap at which the GPU may pick the other set
 
 
 def _session(w, **kw):
@@ -39,6 +40,7 @@ def run_parity(w, steps, check_router_inputs=True, grid=None):
     tokens = list(w.tokens)
     agree = 0
     worst = 0.0
+    near_ties = 0
     for step in range(steps):
         sess.step()
         sess.status()
@@ -53,9 +55,15 @@ def run_parity(w, steps, check_router_inputs=True, grid=None):
             for l in range(s.n_layers):
                 wr = W.host_matrix(7, l, s.n_experts, s.d_model)  # router weights of layer l
                 for b in range(w.B):
+                    # The GPU forms each logit as inv_rms * sum_i w_ei * x_i * gamma_i (fp64) from the row tiles'
+                    # partials; the oracle's router takes the GPU's fp32 RMSNorm output n_i = x_i * (gamma_i *
+                    # inv_rms).  The two agree up to the fp32 rounding of n (a few 1e-8 here), so selections must be
+                    # identical except where the oracle's k-th and (k+1)-th logits are closer than ROUTE_EPS.
                     sel, _, lg = O.router(n_gpu[l, b], wr, s.top_k, w.router_bias)
-                    assert np.array_equal(sel, gsel[l, b]), f"teacher-forced routing differs at step {step} layer {l} seq {b}"
-                    assert np.allclose(lg, rl_gpu[l, b], rtol=1e-6, atol=1e-7)
+                    assert np.allclose(lg, rl_gpu[l, b], rtol=1e-5, atol=1e-6), f"router logits differ at step {step} layer {l}"
+                    if not np.array_equal(sel, gsel[l, b]):
+                        assert kth_gap(lg, s.top_k) < ROUTE_EPS, f"teacher-forced routing differs at step {step} layer {l} seq {b}"
+                        near_ties += 1
         pos = sess.seq_rows_host[step]
         ol, onx, osel, _ = orc.step(tokens, pos, gpu_sel=gsel)
         for b in range(w.B):
@@ -69,13 +77,17 @@ def run_parity(w, steps, check_router_inputs=True, grid=None):
             assert nxt[b] == int(np.argmax(logits[b])), "greedy token is not the argmax of the GPU's own logits"
         tokens = [int(t) for t in nxt]
     assert agree >= 0.99 * steps * w.B
+    if check_router_inputs:
+        assert near_ties <= max(1, 0.01 * steps * w.B * s.n_layers), f"{near_ties} teacher-forced near-tie routings"
+    orc.tf_near_ties = near_ties
     return sess, orc, worst
 
 
 def test_tiny_16_steps():
     w = W.make("tiny")
     sess, orc, worst = run_parity(w, w.steps)
-    print(f"tiny: worst logits rel L2 {worst:.2e}, routing near-ties {orc.near_ties}/{orc.route_checked}")
+    print(f"tiny: worst logits rel L2 {worst:.2e}, routing near-ties {orc.near_ties}/{orc.route_checked}, "
+          f"teacher-forced near-ties {orc.tf_near_ties}")
     # KV written by the kernel equals the oracle's cache: the new K/V are BF16 roundings of fp32 values that
     # agree to ~1e-6, so a rounding may land one step apart (more steps only for values near zero)
     from oracle import oracle as O
