@@ -7,6 +7,8 @@ difference is a failure.
 """
 from __future__ import annotations
 
+import sys
+
 import numpy as np
 
 from oracle import oracle as O
@@ -30,13 +32,13 @@ class OracleRun:
     in memory; for large ones `layer_source(l)` generates a layer's dense weights on demand and experts
     are generated when selected."""
 
-    def __init__(self, w: W.Workload, pt, n_pages, keep_all=None):
+    def __init__(self, w: W.Workload, pt, n_pages, keep_all=None, kv_layers=None):
         self.w = w
         s = self.shape = w.shape
         self.D = dims(s)
         self.pt = pt
         self.n_pages = n_pages
-        self.kv = W.host_kv(w, pt, n_pages)
+        self.kv = W.host_kv(w, pt, n_pages, n_layers=kv_layers)  # kv_layers: only the first layers' caches
         small = s.n_layers * (s.layer_attn_bytes() + s.n_experts * s.expert_bytes()) < 2e9
         self.keep_all = small if keep_all is None else keep_all
         self.final_norm = np.full(s.d_model, W.ONE_BF16, np.uint16)
@@ -67,11 +69,18 @@ class OracleRun:
     def step(self, tokens, pos, gpu_sel=None):
         """One oracle decode step for tokens at positions pos (prior lengths).  gpu_sel: [L][B][k] GPU selections
         (for the near-tie rule).  Returns logits [B][V], next [B], sel [L][B][k], n [L][B][d]."""
+        x, sels, ns = self.layers(tokens, pos, self.shape.n_layers, gpu_sel)
+        logits, nxt = O.head(self.D, x, self.final_norm, self.lm_head)
+        return logits, nxt, np.stack(sels), np.stack(ns)
+
+    def layers(self, tokens, pos, n_layers, gpu_sel=None):
+        """The first n_layers layers of a step: residual stream after them, per-layer selections and
+        normalised inputs."""
         s = self.shape
         B = len(tokens)
         x = O.embed(self.D, W.host_embed_rows(s, tokens), np.arange(B, dtype=np.int32))
         sels, ns = [], []
-        for l in range(s.n_layers):
+        for l in range(n_layers):
             # own routing first (on this layer's normalised input)
             hl = self.layer_weights(l, [])
             n = np.stack([O.rmsnorm(x[b], hl.arrs[0]) for b in range(B)])
@@ -93,8 +102,9 @@ class OracleRun:
             x, aux = O.layer(self.D, Wl, pos, self.pt, self.kv[l], x, sel_force=force if (force >= 0).any() else None)
             sels.append(aux["sel"])
             ns.append(aux["n"])
-        logits, nxt = O.head(self.D, x, self.final_norm, self.lm_head)
-        return logits, nxt, np.stack(sels), np.stack(ns)
+            if s.n_layers >= 24 and l % 12 == 11:  # progress of long oracle runs
+                print(f"[oracle] layer {l + 1}/{s.n_layers}", file=sys.stderr, flush=True)
+        return x, sels, ns
 
 
 def rel_l2(a, b):
