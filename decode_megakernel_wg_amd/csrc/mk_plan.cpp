@@ -157,19 +157,33 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
   }
   P->B = B;
   P->t = choose_tiling(d);
+  // many expert slots (large batches): longer expert up-projection tiles, each streaming several passes
+  if (std::min(d->n_experts, B * d->top_k) >= 32 && d->d_ffn % 64 == 0) {
+    P->t.up_rows = 64;
+    P->t.n_up = d->d_ffn / 64;
+  }
   const Tiling& t = P->t;
   const int L = d->n_layers, Hkv = d->n_kv_heads, E = d->n_experts;
   P->n_slots = std::min(E, B * d->top_k);
   P->cl.build(L, Hkv, B, P->n_slots, t.n_rt);
   const CounterLayout& cl = P->cl;
   P->splits.assign(B, 1);
+  // positions per attention split: ATTN_SPLIT_POS, more when the batch's contexts are long, so that a layer
+  // has about ATTN_TARGET_TASKS splits over all sequences and KV groups (each split then streams several
+  // chunks, and the merge reads fewer partials), up to ATTN_MAX_SPLIT_POS (more splits beyond that)
+  int64_t total = 0;
   for (int b = 0; b < B; ++b) {
     const int32_t len = batch->seq_lens[b];
     if (len < 0 || (int64_t)len / MK_PAGE_SIZE >= d->max_pages_per_seq) {
       *msg = "sequence length negative or beyond max_pages_per_seq";
       return MK_E_INVAL;
     }
-    int64_t s = ((int64_t)len + 1 + ATTN_SPLIT_POS - 1) / ATTN_SPLIT_POS;
+    total += (int64_t)len + 1;
+  }
+  int64_t split_pos = (total * Hkv + ATTN_TARGET_TASKS - 1) / ATTN_TARGET_TASKS;
+  split_pos = std::max<int64_t>(ATTN_SPLIT_POS, std::min<int64_t>((split_pos + 127) / 128 * 128, ATTN_MAX_SPLIT_POS));
+  for (int b = 0; b < B; ++b) {
+    const int64_t s = ((int64_t)batch->seq_lens[b] + 1 + split_pos - 1) / split_pos;
     P->splits[b] = (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, ATTN_MAX_SPLITS));
   }
   P->desc.clear();
