@@ -25,6 +25,12 @@
  * fp64 and is rounded to fp32 once, where the value is stored.  The KV cache
  * holds BF16.  Weights are BF16 bit patterns (uint16).
  *
+ * Pins: every part is tested against closed forms, special cases and library
+ * routines (numpy/torch on the CPU).  A whole decode step of many layers has no
+ * external reference: parity unpinned beyond those per-part pins and the
+ * layer algebra (the layer equals x + Attn(n) + MoE(n) of the separately
+ * called parts).
+ *
  * Error convention: functions returning int give 0 on success and a negative
  * value on invalid arguments (null pointer, page index out of range).
  */
