@@ -134,7 +134,8 @@ enum {
   MK_DBGK_ROUTE_GATE = 2,    /* fp32  [n_layers][batch][top_k]: its gates (always recorded) */
   MK_DBGK_ROUTER_LOGITS = 3, /* fp32  [n_layers][batch][n_experts] (always recorded) */
   MK_DBGK_NORM_IN = 4,       /* fp32  [n_layers][batch][d_model]: each layer's RMSNorm output (MK_DBG_DUMP_N) */
-  MK_DBGK_COUNTERS = 5,      /* uint32 [n_counters] as left by the last step (all zero after a clean step) */
+  MK_DBGK_COUNTERS = 5,      /* uint32 [n_counters]: final values of the last step, copied just before the kernel
+                                resets them to zero for the next step (always recorded) */
   MK_DBGK_TASK_DONE = 6,     /* uint32 [n_tasks]: completions per task in the last step (must be 1 each) */
   MK_DBGK_TIMESTAMPS = 7     /* uint64 [n_tasks][8]: claim, dependencies met, end (100 MHz wall clock), hardware id
                                 (XCC id << 32 | HW_ID register), then up to 4 task-specific sub-phase marks (0 = unset);
@@ -145,8 +146,10 @@ int mk_debug_set(mk_model* m, uint32_t flags);
  * Errors: MK_E_INVAL (unknown kind), MK_E_STATE (kind not enabled), MK_E_RANGE (bytes larger than the buffer). */
 int mk_debug_read(mk_model* m, int kind, void* host_dst, int64_t bytes);
 
-/* Override the grid: n_workgroups persistent workgroups (0 = one per compute unit).  Results do not
- * depend on it (every reduction has a fixed order); it exists for testing and tuning. */
+/* Override the grid: n_workgroups persistent workgroups (0 = one per compute unit, at most 1024).  Results
+ * do not depend on it (every reduction has a fixed order); it exists for testing and tuning.  Takes effect at
+ * the next mk_decode_step, which re-splits the task list into the two claim queues for this grid.
+ * Errors: MK_E_INVAL (null handle, n_workgroups outside 0..1024). */
 int mk_set_grid(mk_model* m, int32_t n_workgroups);
 
 /* Release the handle and its device memory (after the stream's work has finished). */
@@ -156,7 +159,9 @@ int mk_free_model(mk_model* m);
 const char* mk_last_error(void);
 
 /* Pure host planning, for tools and tests (no device needed): the task list mk_build_tasks would emit
- * for `desc` on a grid of n_workgroups.  n_counters (nullable) receives the counter count. */
+ * for `desc` and `batch`, in topological order (before its split into claim queues).  n_tasks receives the
+ * task count, n_counters (nullable) the counter count; tasks_out may be null to query the sizes.
+ * Errors: MK_E_INVAL (bad shape or batch), MK_E_RANGE (cap smaller than the task count). */
 int mk_plan_tasks(const mk_model_desc* desc, const mk_batch* batch, int32_t* tasks_out, int64_t cap, int64_t* n_tasks,
                   int32_t* n_counters);
 
