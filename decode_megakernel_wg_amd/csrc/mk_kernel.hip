@@ -119,6 +119,12 @@ __device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even
 __device__ __forceinline__ void pub(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ void pubi(int32_t* p, int32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ void drain_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// Workgroup barrier for data exchanged through LDS only: LDS operations complete (lgkmcnt(0)), then
+// s_barrier.  Unlike __syncthreads it does not wait for outstanding global loads (weights in flight).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -257,23 +263,28 @@ __device__ __forceinline__ NormGain norm_gain(const uint16_t* gamma, int d) {
 
 // RMSNorm of the residual stream into LDS: xs[j][i] = x[b][i] * (gamma[i] * inv_rms[b]) for staging rows
 // j < nb of tokens b = tok[j] (null = identity).  inv_rms[b] = 1 / sqrt(sum of the row tiles' partial sums
-// of squares (tile order) / d + eps).  One round trip: the rows and the partial sums load together.
-__device__ __forceinline__ void stage_norm(KA& a, const NormGain& gn, int nb, const int* tok, Lds& S) {
+// of squares (tile order) / d + eps).  One round trip: the rows and the partial sums load together, both
+// straight into LDS (stage_norm_issue); stage_norm_finish runs once they have landed.
+__device__ __forceinline__ void stage_norm_issue(KA& a, int nb, const int* tok, Lds& S) {
   const int d = a.d, nrt = a.n_rt;
   for (int j = 0; j < nb; ++j) lds_copy(a.x + (tok ? tok[j] : j) * d, S.xs + j * d, d / 4);
-  if (tidx() < nb * nrt) {
-    const int j = tidx() / nrt, r = tidx() - j * nrt;
-    const int b = tok ? tok[j] : j;
-    S.ssqv[tidx()] = a.ssq[b * nrt + r];
+  // partial sums of squares: one 4-byte lane per row tile, issued by the last wave
+  if ((tidx() >> 6) == NW - 1) {
+    const int lane = tidx() & 63;
+    for (int j = 0; j < nb; ++j)
+      if (lane < nrt)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.ssq + (tok ? tok[j] : j) * nrt + lane),
+                                         (__attribute__((address_space(3))) void*)(S.ssqv + j * nrt), 4, 0, 0);
   }
-  drain_stores();
-  __syncthreads();
+}
+__device__ __forceinline__ void stage_norm_finish(KA& a, const NormGain& gn, int nb, Lds& S) {
+  const int d = a.d, nrt = a.n_rt;
   if (tidx() < nb) {
     float ss = 0.f;
     for (int r = 0; r < nrt; ++r) ss += S.ssqv[tidx() * nrt + r];
     S.inv[tidx()] = 1.0f / sqrtf(ss / (float)d + a.eps);
   }
-  __syncthreads();
+  lds_sync();
 #pragma unroll
   for (int e = 0; e < NORM_PAIRS; ++e) {
     const int p = tidx() + e * NT;
@@ -287,7 +298,13 @@ __device__ __forceinline__ void stage_norm(KA& a, const NormGain& gn, int nb, co
       }
     }
   }
+  lds_sync();
+}
+__device__ __forceinline__ void stage_norm(KA& a, const NormGain& gn, int nb, const int* tok, Lds& S) {
+  stage_norm_issue(a, nb, tok, S);
+  drain_stores();
   __syncthreads();
+  stage_norm_finish(a, gn, nb, S);
 }
 
 // ------------------------------------------------------------------------------------------ GEMV core
@@ -719,7 +736,7 @@ __device__ __forceinline__ void split_x(int nb, int K, Lds& S) {
     S.xb[j * XBP + c] = h;
     S.xb[(8 + j) * XBP + c] = f2bf(x - bf2f(h));
   }
-  __syncthreads();
+  lds_sync();
 }
 
 // Prefetch, wait, stage, stream.  The first AHEAD passes of the tile (16 KB per wave each) are requested
@@ -883,32 +900,44 @@ __device__ __forceinline__ int slot_routing(KA& a, uint32_t v, Lds& S) {
 template <class C>
 __device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
   const int l = w[W_LAYER], s = w[W_A], r0 = w[W_R0], r1 = w[W_R1];
-  const int d = a.d, F = a.F, nr = r1 - r0;
+  const int d = a.d, F = a.F, B = a.B, nr = r1 - r0;
   const LayerW& L = a.layers[l];
   const NormGain gn = norm_gain(L.attn_norm, d);
-  // the layer's expert tables are read before the wait, so the weight requests follow it immediately
   const uint16_t* wg0 = L.w_gate;
   const uint16_t* wu0 = L.w_up;
   __asm__ volatile("" ::"s"(wg0), "s"(wu0));
+  // Small batches: the layer's input exists before its routing does, so every token's normalised input is
+  // staged (and split into BF16 hi/lo) while the router is still being completed; once the slot is
+  // released only the expert's weights are in flight.  Larger batches stage only the slot's tokens, after
+  // routing (staging all of them would read more than a small tile's weights).
+  const bool early = B <= 2;
+  if (early) {
+    wait_deps(a, w, 1, 2, t);
+    stage_norm(a, gn, B, nullptr, S);
+    split_x(B, d, S);
+  }
   const int e = slot_routing(a, wait_value(a, w, 0, t, S), S);
   if (e >= 0) {
     const int n = S.slot_n;
-    // gate rows then up rows of this tile, as one 2*nr-row tile over two bases; the expert is known only
-    // now, so its weights stream while the slot's inputs are normalised into LDS
+    // gate rows then up rows of this tile, as one 2*nr-row tile over two bases
     const uint16_t* Wg = wg0 + ((int64_t)e * F + r0) * d;
     const uint16_t* Wu = wu0 + ((int64_t)e * F + r0) * d;
-    mgemv_task<true, 1>(
-        a, w, t, Rows2{Wg, Wu, d, nr}, 2 * nr, d, n, 0, 0, [&] {
+    mgemv_task<false, 1>(
+        a, w, t, Rows2{Wg, Wu, d, nr}, 2 * nr, d, early ? B : n, 0, 0,
+        [&] {
           mark(a, t, 2);  // weights requested
-          stage_norm(a, gn, n, S.slot_b, S);
+          if (!early) {
+            stage_norm(a, gn, n, S.slot_b, S);
+            split_x(n, d, S);
+          }
         },
-        [&](int r, int b, float v) { S.gu[r * 8 + b] = v; }, S);
+        [&](int r, int j, float v) { S.gu[r * 8 + (early ? j : S.slot_b[j])] = v; }, S);
     __syncthreads();
     for (int i = tidx(); i < nr * n; i += NT) {
-      const int r = i / n, j = i - r * n;
-      const float gv = S.gu[r * 8 + j], uv = S.gu[(nr + r) * 8 + j];
+      const int r = i / n, j = i - r * n, b = S.slot_b[j];
+      const float gv = S.gu[r * 8 + b], uv = S.gu[(nr + r) * 8 + b];
       const float h = gv / (1.0f + expf(-gv)) * uv;
-      pub(a.h + ((int64_t)s * a.B + j) * F + r0 + r, h);
+      pub(a.h + ((int64_t)s * B + j) * F + r0 + r, h);
     }
   }
   signal(a, w[W_SIG], w[W_SIGN]);
