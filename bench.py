@@ -28,6 +28,9 @@ WORKLOAD_TEXT = {
     "long_64k": "same 48-layer model, batch 1, 65536 prior positions, split-KV attention",
     "long_128k": "same 48-layer model, batch 1, 131072 prior positions, split-KV attention",
     "long_256k": "same 48-layer model, batch 1, 262144 prior positions, split-KV attention",
+    "continuous": "same 48-layer model under continuous batching: arrivals every ~64 steps (exponential gaps), "
+                  "geometric output lengths (mean 256), prefixes log-uniform in [512, 65536], LIFO page free list, "
+                  "live batch 1-8, task list rebuilt every step on the host while the previous step runs",
 }
 
 
@@ -119,6 +122,121 @@ def run_gpu(workload, steps, warmup, model=None):
                 tok_s=steps * w.B / (total_ms * 1e-3), kernel_ms=sum(per) / steps)
 
 
+def run_gpu_continuous(steps, warmup):
+    """Continuous batching over the schedule's first `steps` steps, in two passes over the same steps.
+    Pass 1 runs step by step and reads each step's routing back (distinct experts per layer, for the bytes).
+    Pass 2 is the timed one: steps are enqueued back to back, the host rebuilding step t+1's task list while
+    the GPU runs step t; tok/s = tokens / (wall time - GPU time of the admitted prefixes' writes), and each
+    kernel is timed with HIP events on the launch stream (for the roofline).  Both passes must end on the
+    same greedy tokens.  Warm-up: the first `warmup` steps, then a restart from step 0."""
+    import numpy as np
+    import torch
+
+    from decode_megakernel_wg_amd import mk
+    from decode_megakernel_wg_amd import roofline as R
+    from decode_megakernel_wg_amd.continuous import ContinuousSession
+    from synth import workloads as W
+
+    t0 = time.time()
+    log("generating 48-layer synthetic weights in HBM")
+    sess = ContinuousSession(W.FULL, steps)
+    log(f"setup {time.time() - t0:.1f} s; pool {sess.n_pages} pages; warmup {warmup} steps")
+    for _ in range(min(warmup, steps)):
+        sess.step()
+    sess.status()
+    sess.reset()
+    s = W.FULL
+    stream = torch.cuda.current_stream()
+    kern, nbytes, ntok = [], [], 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)  # pass-1 kernel time (logged)
+    orig = sess.h.mk_decode_step
+
+    def timed_step(*a, **k):
+        e0.record(stream)
+        orig(*a, **k)
+        e1.record(stream)
+
+    sess.h.mk_decode_step = timed_step
+    last = None
+    for i in range(steps):
+        sids, _, pos, nxt, _ = sess.step()
+        B = len(sids)
+        kern.append(e0.elapsed_time(e1))
+        sel = sess.h.mk_debug_read(mk.MK_DBGK_ROUTE_SEL, (s.n_layers, B, s.top_k), np.int32)
+        uniq = [len(np.unique(sel[l])) for l in range(s.n_layers)]
+        nbytes.append(R.step_bytes(s, pos, uniq, len(set(int(t) for t in nxt))))
+        ntok += B
+        last = nxt
+        if (i + 1) % 256 == 0:
+            log(f"pass 1 step {i + 1}/{steps}: batch {B}")
+    sess.status()
+    sess.h.mk_decode_step = orig
+    sess.reset()
+    wall, fill_s, kern2 = sess.run_pipelined(steps, kernel_events=True)
+    sess.status()
+    B = len(sess.steps[steps - 1].sids)
+    nxt = mk.read_device(sess.next_ptr, 4 * B)
+    if not np.array_equal(nxt, last):
+        raise RuntimeError("pipelined pass ended on other tokens than the step-by-step pass")
+    log(f"pass 2: {wall:.3f} s wall, {fill_s:.3f} s of prefix writes")
+    log(f"kernel time per step: pass 1 {sum(kern) / steps:.3f} ms, pass 2 {1e3 * sum(kern2) / steps:.3f} ms")
+    return dict(sess=sess, wall_s=wall - fill_s, kernel_s=sum(kern2), bytes=sum(nbytes), tokens=ntok,
+                batch_sizes=[len(st.sids) for st in sess.steps[:steps]], max_ctx=int(max(max(st.pos) for st in sess.steps[:steps])))
+
+
+def cpu_baseline_continuous(min_seconds=10.0, max_steps=16):
+    """The CPU oracle on consecutive steps of the continuous-batching schedule (free-running on its own tokens),
+    until `min_seconds` of timed work or `max_steps` steps; prefix writes and weight generation not timed."""
+    import numpy as np
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import oracle as O
+    from oracle_runner import OracleRun
+    from synth import continuous as CB
+    from synth import synth
+    from synth import workloads as W
+
+    steps, seqs, n_pages, max_pages = CB.schedule(max_steps, n_pages=8192)
+    s = W.FULL
+    orc = OracleRun(W.Workload("continuous", s, [], max_steps), np.zeros((0, max_pages), np.int32), n_pages, keep_all=False)
+    last, timed, n, ntok = {}, 0.0, 0, 0
+    for st in steps:
+        if timed >= min_seconds:
+            break
+        for sid in st.admitted:
+            q = seqs[sid]
+            synth.fill_kv_host(orc.kv, 0, s.n_kv_heads, s.d_head, W.PAGE, np.array(q.pages, np.int32), sid, 0, q.prefix, W.SEED_KV,
+                               W.KV_SIGMA)
+        pt = CB.page_table(st, seqs, max_pages)
+        toks = np.array([last.get(sid, synth.token(W.SEED_TOK, sid, s.vocab)) for sid in st.sids], np.int32)
+        pos = st.pos.astype(np.int64)
+        B = len(st.sids)
+        x = O.embed(orc.D, W.host_embed_rows(s, toks), np.arange(B, dtype=np.int32))
+        for l in range(s.n_layers):
+            hl = orc.layer_weights(l, [])
+            nrm = np.stack([O.rmsnorm(x[b], hl.arrs[0]) for b in range(B)])
+            need = set()
+            for b in range(B):
+                sel, _, _ = O.router(nrm[b], hl.arrs[5], s.top_k, None)
+                need.update(int(e) for e in sel)
+            Wl = orc.layer_weights(l, sorted(need))
+            t1 = time.perf_counter()
+            x, _ = O.layer(orc.D, Wl, pos, pt, orc.kv[l], x)
+            timed += time.perf_counter() - t1
+        t1 = time.perf_counter()
+        _, nxt = O.head(orc.D, x, orc.final_norm, orc.lm_head)
+        timed += time.perf_counter() - t1
+        for b, sid in enumerate(st.sids):
+            last[sid] = int(nxt[b])
+        n += 1
+        ntok += B
+        log(f"oracle step {n}: timed {timed:.2f} s")
+    return {"value": round(ntok / timed, 4), "unit": "tok/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"the continuous-batching schedule's first {n} steps ({ntok} tokens, live batch "
+                      f"{min(len(st.sids) for st in steps[:n])}-{max(len(st.sids) for st in steps[:n])}); fp64-accumulating C oracle "
+                      f"with OpenMP; {timed:.2f} s of timed CPU work; prefix writes and host weight generation excluded"}
+
+
 def cpu_baseline(workload, min_seconds=10.0, max_steps=16):
     """The CPU oracle timed on consecutive greedy decode steps of the same workload (all layers and the LM head
     per step), until at least `min_seconds` of timed work or `max_steps` steps.  Each layer's synthetic weights
@@ -183,6 +301,8 @@ def main():
         sys.exit(2)
     from decode_megakernel_wg_amd import roofline as R
 
+    if args.workload == "continuous":
+        return main_continuous(args)
     r = run_gpu(args.workload, args.steps, args.warmup)
     w = r["w"]
     achieved = r["avg_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
@@ -213,6 +333,43 @@ def main():
         del r
         torch.cuda.empty_cache()
         line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+def main_continuous(args):
+    import torch
+
+    r = run_gpu_continuous(args.steps, args.warmup)
+    tok_s = r["tokens"] / r["wall_s"]
+    achieved = r["bytes"] / r["kernel_s"] / 1e9
+    sol_s = r["bytes"] / 8.0e12
+    bs = r["batch_sizes"]
+    line = {
+        "metric": "decode tok/s + % HBM speed-of-light, batch 1 @8K ctx and batch 8 ragged",
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * r["wall_s"] / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"continuous: {WORKLOAD_TEXT['continuous']}", "global_batch": max(bs),
+                   "mean_batch": round(sum(bs) / len(bs), 3), "seq_len": r["max_ctx"], "parallelism": "single GPU, persistent megakernel"},
+        "sol_tok_s": round(r["tokens"] / sol_s, 1),
+        "pct_of_sol": round(100 * sol_s / r["wall_s"], 2),
+        "sol_bytes_per_step": int(r["bytes"] / args.steps),
+        "kernel_ms_per_step": round(1e3 * r["kernel_s"] / args.steps, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(achieved / 8000.0, 4), "traffic": counter_traffic("continuous")},
+    }
+    if not args.no_cpu_baseline:
+        del r
+        torch.cuda.empty_cache()
+        line["cpu_baseline"] = cpu_baseline_continuous()
     print(json.dumps(line), flush=True)
 
 
