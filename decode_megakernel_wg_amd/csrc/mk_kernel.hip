@@ -85,6 +85,7 @@ struct Lds {
   int lmq[4];                   // LM head: ring of claimed vocabulary chunks
   uint32_t wval;                // value a wait observed (expert slot words)
   int next1, flag;
+  int xb_layer;  // l + 1 while xb holds layer l's normalised input of every token (split); 0 otherwise
 };
 
 // A task descriptor staged in LDS; every word is read as a wave-uniform (scalar) value.
@@ -729,6 +730,7 @@ __device__ __forceinline__ void mg_finish(f4 acc, const MGeo& g, int nb, Out& ou
 
 // Split the staged fp32 inputs S.xs[nb][K] into BF16 hi and lo parts.
 __device__ __forceinline__ void split_x(int nb, int K, Lds& S) {
+  if (tidx() == 0) S.xb_layer = 0;
   for (int i = tidx(); i < nb * K; i += NT) {
     const int j = i / K, c = i - j * K;
     const float x = S.xs[i];
@@ -860,6 +862,7 @@ __device__ __forceinline__ void task_qkv(KA& a, Desc w, int t, Lds& S) {
   mgemv_task<true>(
       a, w, t, Rows1{W, d}, r1 - r0, d, a.B, 0, N_WAITS, [&] { stage_norm(a, gn, a.B, nullptr, S); },
       [&](int r, int b, float v) { pub(out + b * bstride + r, v); }, S);
+  if (tidx() == 0) S.xb_layer = l + 1;  // xb keeps this layer's split input (read after later barriers)
   signal(a, w[W_SIG], w[W_SIGN]);
 }
 
@@ -911,10 +914,11 @@ __device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
   // released only the expert's weights are in flight.  Larger batches stage only the slot's tokens, after
   // routing (staging all of them would read more than a small tile's weights).
   const bool early = B <= 2;
-  if (early) {
+  if (early && __builtin_amdgcn_readfirstlane(S.xb_layer) != l + 1) {  // not staged by this workgroup's last task
     wait_deps(a, w, 1, 2, t);
     stage_norm(a, gn, B, nullptr, S);
     split_x(B, d, S);
+    if (tidx() == 0) S.xb_layer = l + 1;
   }
   const int e = slot_routing(a, wait_value(a, w, 0, t, S), S);
   if (e >= 0) {
@@ -1209,6 +1213,7 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
   const float* cs = a.rope_cs + (int64_t)b * (DH / 2) * 2;
   const float qscale = 1.0f / sqrtf((float)DH);
   uint16_t* qb = S.xb;  // [2][16][DH]: hi then lo
+  if (tid == 0) S.xb_layer = 0;
   for (int i = tid; i < 16 * DH; i += NT) {
     if (i >= GRP * DH) {
       qb[i] = 0;
@@ -1527,7 +1532,10 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
   const int count = second ? a.n_tasks - a.n_first : a.n_first;
   const int ticket = second ? a.c_ticket2 : a.c_ticket;
   // first task: claim and fetch synchronously; then keep two claims and one descriptor ahead
-  if (tid == 0) S.next1 = (int)__hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    S.xb_layer = 0;
+    S.next1 = (int)__hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
   int i = S.next1;
   if (i < count) fetch_desc(a, base + i, S.desc[0]);
