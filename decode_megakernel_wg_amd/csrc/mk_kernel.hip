@@ -859,8 +859,16 @@ __device__ __forceinline__ void task_qkv(KA& a, Desc w, int t, Lds& S) {
   float* out = a.qkv + (int64_t)g * rows + r0;
   const int64_t bstride = (int64_t)a.Hkv * rows;
   const NormGain gn = norm_gain(L.attn_norm, d);
-  mgemv_task<true>(
-      a, w, t, Rows1{W, d}, r1 - r0, d, a.B, 0, N_WAITS, [&] { stage_norm(a, gn, a.B, nullptr, S); },
+  // a workgroup that staged this layer's input for its previous task keeps it
+  const bool staged = __builtin_amdgcn_readfirstlane(S.xb_layer) == l + 1;
+  mgemv_task<false>(
+      a, w, t, Rows1{W, d}, r1 - r0, d, a.B, 0, N_WAITS,
+      [&] {
+        if (!staged) {
+          stage_norm(a, gn, a.B, nullptr, S);
+          split_x(a.B, d, S);
+        }
+      },
       [&](int r, int b, float v) { pub(out + b * bstride + r, v); }, S);
   if (tidx() == 0) S.xb_layer = l + 1;  // xb keeps this layer's split input (read after later barriers)
   signal(a, w[W_SIG], w[W_SIGN]);
@@ -910,9 +918,10 @@ __device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
   const uint16_t* wu0 = L.w_up;
   __asm__ volatile("" ::"s"(wg0), "s"(wu0));
   // Small batches: the layer's input exists before its routing does, so every token's normalised input is
-  // staged (and split into BF16 hi/lo) while the router is still being completed; once the slot is
-  // released only the expert's weights are in flight.  Larger batches stage only the slot's tokens, after
-  // routing (staging all of them would read more than a small tile's weights).
+  // staged (and split into BF16 hi/lo) while the router is still being completed, once per workgroup and
+  // layer (consecutive tiles of the layer reuse it); once the slot is released only the expert's weights
+  // are in flight.  Larger batches stage only the slot's tokens, after routing (staging all of them costs
+  // more than it saves there, measured).
   const bool early = B <= 2;
   if (early && __builtin_amdgcn_readfirstlane(S.xb_layer) != l + 1) {  // not staged by this workgroup's last task
     wait_deps(a, w, 1, 2, t);
