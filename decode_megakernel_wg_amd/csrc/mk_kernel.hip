@@ -1423,11 +1423,30 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
   if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) {
     mark(a, t, 3);
     const float* p0 = a.apart + (((int64_t)b * Hkv + g) * ATTN_MAX_SPLITS) * GRP * (DH + 2);
-    float* wsc = S.xs;                        // [GRP][nsplit] weights exp(m_s - M)
-    float* lsum = S.xs + GRP * ATTN_MAX_SPLITS;  // [GRP]
+    float* wsc = S.xs;                               // [GRP][nsplit] running max, then weights exp(m_s - M)
+    float* lsc = S.xs + GRP * ATTN_MAX_SPLITS;       // [GRP][nsplit] running sums
+    float* lsum = S.xs + 2 * GRP * ATTN_MAX_SPLITS;  // [GRP]
+    // One round trip: each thread requests its two outputs' values of the first 16 splits, then the splits'
+    // (max, sum) pairs go to LDS; later 16-split chunks (long contexts) are requested as they are merged.
+    static_assert(GRP * DH <= 2 * NT, "two outputs per thread");
+    const bool has0 = tid < GRP * DH, has1 = tid + NT < GRP * DH;
+    const int h0 = has0 ? tid / DH : 0, d0 = has0 ? tid - h0 * DH : 0;
+    const int h1 = has1 ? (tid + NT) / DH : h0, d1 = has1 ? (tid + NT) - h1 * DH : d0;
+    float v0[16], v1[16];
+    auto load_chunk = [&](int q) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const bool ok = has0 && q + u < nsplit;
+        v0[u] = ok ? p0[((int64_t)(q + u) * GRP + h0) * (DH + 2) + d0] : 0.f;
+        v1[u] = ok ? p0[((int64_t)(q + u) * GRP + h1) * (DH + 2) + d1] : 0.f;
+      }
+    };
+    load_chunk(0);
     for (int i = tid; i < GRP * nsplit; i += NT) {
       const int h = i / nsplit, q = i - h * nsplit;
-      wsc[i] = p0[((int64_t)q * GRP + h) * (DH + 2) + DH];
+      const float* r = p0 + ((int64_t)q * GRP + h) * (DH + 2) + DH;
+      wsc[i] = r[0];
+      lsc[i] = r[1];
     }
     __syncthreads();
     if (wave < GRP) {
@@ -1440,26 +1459,25 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
         const float mq = wsc[h * nsplit + q];
         const float wq = mq == -INFINITY ? 0.f : expf(mq - M);
         wsc[h * nsplit + q] = wq;
-        Ls = fmaf(p0[((int64_t)q * GRP + h) * (DH + 2) + DH + 1], wq, Ls);
+        Ls = fmaf(lsc[h * nsplit + q], wq, Ls);
       }
       Ls = wave_sum(Ls);
       if (lane == 0) lsum[h] = Ls;
     }
     __syncthreads();
-    for (int i = tid; i < GRP * DH; i += NT) {
-      const int h = i / DH, dd = i - h * DH;
-      float ov = 0.f;
-      int q = 0;
-      for (; q + 8 <= nsplit; q += 8) {
-        float vv[8];
+    float o0 = 0.f, o1 = 0.f;
+    for (int q = 0; q < nsplit; q += 16) {
+      if (q > 0) load_chunk(q);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) vv[u] = p0[((int64_t)(q + u) * GRP + h) * (DH + 2) + dd];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) ov = fmaf(vv[u], wsc[h * nsplit + q + u], ov);
+      for (int u = 0; u < 16; ++u) {
+        if (q + u < nsplit) {
+          o0 = fmaf(v0[u], wsc[h0 * nsplit + q + u], o0);
+          o1 = fmaf(v1[u], wsc[h1 * nsplit + q + u], o1);
+        }
       }
-      for (; q < nsplit; ++q) ov = fmaf(p0[((int64_t)q * GRP + h) * (DH + 2) + dd], wsc[h * nsplit + q], ov);
-      pub(a.attn_o + (int64_t)b * a.Hq * DH + ((int64_t)g * GRP + h) * DH + dd, ov / lsum[h]);
     }
+    if (has0) pub(a.attn_o + (int64_t)b * a.Hq * DH + ((int64_t)g * GRP + h0) * DH + d0, o0 / lsum[h0]);
+    if (has1) pub(a.attn_o + (int64_t)b * a.Hq * DH + ((int64_t)g * GRP + h1) * DH + d1, o1 / lsum[h1]);
     signal(a, w[W_SIG], w[W_SIGN]);
   }
 }
