@@ -703,6 +703,23 @@ __device__ __forceinline__ void mg_compute(const MBuf& buf, f4& acc, const MGeo&
   }
 }
 
+// A tile that is exactly one pass with every wave busy (16-row blocks times K-slices fill the workgroup, and
+// each slice is NKP k-steps): its loads need no predicate, so the compiler counts them and each MFMA waits
+// only for its own weights (vmcnt(15), vmcnt(14), ...): the tile is computed as its data arrives instead of
+// after the last load.  Used where a tile's weights are requested only when the tile can run.
+__device__ __forceinline__ bool mg_one_full_pass(const MGeo& g) {
+  return g.rbn * g.ks == NW && g.nrows == 16 * g.rbn && g.nks == NKP;
+}
+template <class RowPtr>
+__device__ __forceinline__ void mg_load_full(MBuf& buf, const RowPtr& W, const MGeo& g) {
+  const int wave = tidx() >> 6, lane = tidx() & 63;
+  const int rb = wave / g.ks, kp = wave - rb * g.ks;
+  gu4* rp = as_global(W(rb * 16 + (lane & 15)));
+  const int v0 = (kp * g.kw + 8 * (lane >> 4)) >> 3;
+#pragma unroll
+  for (int t = 0; t < NKP; ++t) buf.v[t] = __builtin_nontemporal_load(rp + v0 + 4 * t);
+}
+
 // Sum the K-slice partials of each row block (fixed order) and hand (row, token, value) to out().
 template <class Out>
 __device__ __forceinline__ void mg_finish(f4 acc, const MGeo& g, int nb, Out& out, Lds& S) {
@@ -935,16 +952,30 @@ __device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
     // gate rows then up rows of this tile, as one 2*nr-row tile over two bases
     const uint16_t* Wg = wg0 + ((int64_t)e * F + r0) * d;
     const uint16_t* Wu = wu0 + ((int64_t)e * F + r0) * d;
-    mgemv_task<false, 1>(
-        a, w, t, Rows2{Wg, Wu, d, nr}, 2 * nr, d, early ? B : n, 0, 0,
-        [&] {
-          mark(a, t, 2);  // weights requested
-          if (!early) {
-            stage_norm(a, gn, n, S.slot_b, S);
-            split_x(n, d, S);
-          }
-        },
-        [&](int r, int j, float v) { S.gu[r * 8 + (early ? j : S.slot_b[j])] = v; }, S);
+    const MGeo g = mgeo(2 * nr, d);
+    auto out = [&](int r, int j, float v) { S.gu[r * 8 + (early ? j : S.slot_b[j])] = v; };
+    if (early && mg_one_full_pass(g)) {
+      // inputs already staged: the tile is one pass, computed as its weights arrive
+      MBuf b0;
+      mg_load_full(b0, Rows2{Wg, Wu, d, nr}, g);
+      mark(a, t, 2);  // weights requested
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      mark(a, t, 0);
+      mg_compute(b0, acc, g, 0, B, S);
+      mg_finish(acc, g, B, out, S);
+      mark(a, t, 1);
+    } else {
+      mgemv_task<false, 1>(
+          a, w, t, Rows2{Wg, Wu, d, nr}, 2 * nr, d, early ? B : n, 0, 0,
+          [&] {
+            mark(a, t, 2);  // weights requested
+            if (!early) {
+              stage_norm(a, gn, n, S.slot_b, S);
+              split_x(n, d, S);
+            }
+          },
+          out, S);
+    }
     __syncthreads();
     for (int i = tidx(); i < nr * n; i += NT) {
       const int r = i / n, j = i - r * n, b = S.slot_b[j];
