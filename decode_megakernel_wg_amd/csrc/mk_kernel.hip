@@ -308,6 +308,52 @@ __device__ __forceinline__ void stage_norm(KA& a, const NormGain& gn, int nb, co
   stage_norm_finish(a, gn, nb, S);
 }
 
+// RMSNorm of the residual stream straight into the BF16 hi/lo matrix-core operand (xb rows j and 8 + j for
+// staging row j < nb, token tok[j]): one read of the staged rows, no normalised fp32 copy.  inv_rms[b] is
+// formed as in stage_norm_finish (tile order); wave j sums token j's partials.
+__device__ __forceinline__ void stage_split(KA& a, const NormGain& gn, int nb, const int* tok, Lds& S) {
+  const int d = a.d, nrt = a.n_rt;
+  stage_norm_issue(a, nb, tok, S);
+  drain_stores();
+  __syncthreads();
+  if (tidx() == 0) S.xb_layer = 0;
+  {
+    const int wave = tidx() >> 6, lane = tidx() & 63;
+    for (int j = wave; j < nb; j += NW) {
+      // the same additions in the same order as the serial sum of stage_norm_finish (lane 0 adds them all),
+      // with every partial read first
+      if (lane == 0) {
+        float v[32];
+#pragma unroll
+        for (int r = 0; r < 32; ++r) v[r] = r < nrt ? S.ssqv[j * nrt + r] : 0.f;
+        float ss = 0.f;
+#pragma unroll
+        for (int r = 0; r < 32; ++r)
+          if (r < nrt) ss += v[r];
+        S.inv[j] = 1.0f / sqrtf(ss / (float)d + a.eps);
+      }
+    }
+  }
+  lds_sync();
+#pragma unroll
+  for (int e = 0; e < NORM_PAIRS; ++e) {
+    const int p = tidx() + e * NT;
+    if (2 * p < d) {
+      const float g0 = bf_lo(gn.g[e]), g1 = bf_hi(gn.g[e]);
+      for (int j = 0; j < nb; ++j) {
+        const float inv = S.inv[j];
+        const float2 xv = *reinterpret_cast<const float2*>(S.xs + j * d + 2 * p);
+        const float x0 = xv.x * (g0 * inv), x1 = xv.y * (g1 * inv);
+        const uint16_t h0 = f2bf(x0), h1 = f2bf(x1);
+        const uint16_t l0 = f2bf(x0 - bf2f(h0)), l1 = f2bf(x1 - bf2f(h1));
+        *reinterpret_cast<uint32_t*>(S.xb + j * XBP + 2 * p) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        *reinterpret_cast<uint32_t*>(S.xb + (8 + j) * XBP + 2 * p) = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+    }
+  }
+  lds_sync();
+}
+
 // ------------------------------------------------------------------------------------------ GEMV core
 // A row tile W[0..nrows) x [0..K) (row stride ld) times NB staged vectors xs[b][0..K) (pitch xp).
 // Wave w handles rows [p*NW*RPW + w*RPW, +RPW) of pass p; lane l reads 16-byte vectors l, l+64, ...
@@ -677,30 +723,81 @@ __device__ __forceinline__ void mg_load(MBuf& buf, const RowPtr& W, const MGeo& 
   }
 }
 
-__device__ __forceinline__ void mg_compute(const MBuf& buf, f4& acc, const MGeo& g, int pass, int nb, Lds& S) {
+__device__ __forceinline__ void mg_compute(const MBuf& buf, f4& acc, f4& acc2, const MGeo& g, int pass, int nb, Lds& S) {
+  const int wave = tidx() >> 6, lane = tidx() & 63;
+  const int rb = wave / g.ks, kp = wave - rb * g.ks;
+  if (rb >= g.rbn) return;
+  // Columns of absent tokens (j >= nb) read token 0's row: every lane of a 16-lane group then reads the same
+  // LDS address (a broadcast, so no extra LDS traffic), no lane is masked off, and those MFMA output columns
+  // are never used.
+  const int j = lane & 15;
+  const int jr = j < nb ? j : 0;
+  const uint16_t* xh = S.xb + jr * XBP + kp * g.kw + 8 * (lane >> 4);
+  const uint16_t* xl = xh + 8 * XBP;
+  // activations of 2 k-steps are read from LDS together, then their 4 MFMAs run; the hi and lo parts
+  // accumulate separately (two independent chains), summed by the caller
+#pragma unroll
+  for (int t0 = 0; t0 < NKP; t0 += 2) {
+    u4 bh[2], bl[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int s = pass * NKP + t0 + u;
+      if (s < g.nks) {  // wave-uniform
+        bh[u] = *reinterpret_cast<const u4*>(xh + 32 * s);
+        bl[u] = *reinterpret_cast<const u4*>(xl + 32 * s);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int s = pass * NKP + t0 + u;
+      if (s < g.nks) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, buf.v[t0 + u]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bh[u]), acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl[u]), acc2, 0, 0, 0);
+      }
+    }
+  }
+}
+
+// mg_compute for a pass whose NKP k-steps all exist (g.nks a multiple of NKP): no per-step condition, so the
+// unrolled steps are straight-line code.
+__device__ __forceinline__ void mg_compute_full(const MBuf& buf, f4& acc, f4& acc2, const MGeo& g, int pass, int nb, Lds& S) {
   const int wave = tidx() >> 6, lane = tidx() & 63;
   const int rb = wave / g.ks, kp = wave - rb * g.ks;
   if (rb >= g.rbn) return;
   const int j = lane & 15;
-  const bool live = j < nb;
-  const uint16_t* xh = S.xb + (live ? j : 0) * XBP;
-  const uint16_t* xl = S.xb + (live ? 8 + j : 8) * XBP;
-  const int k0 = kp * g.kw + 8 * (lane >> 4);
+  const int jr = j < nb ? j : 0;
+  const uint16_t* xh = S.xb + jr * XBP + kp * g.kw + 8 * (lane >> 4) + 32 * NKP * pass;
+  const uint16_t* xl = xh + 8 * XBP;
+  // software-pipelined: the activations of step t + 2 are requested before the MFMAs of step t
+  u4 h0 = *reinterpret_cast<const u4*>(xh), l0 = *reinterpret_cast<const u4*>(xl);
+  u4 h1 = *reinterpret_cast<const u4*>(xh + 32), l1 = *reinterpret_cast<const u4*>(xl + 32);
 #pragma unroll
   for (int t = 0; t < NKP; ++t) {
-    const int s = pass * NKP + t;
-    if (s < g.nks) {
-      const int k = k0 + 32 * s;
-      u4 bh = u4{0, 0, 0, 0}, bl = u4{0, 0, 0, 0};
-      if (live) {  // only the columns of real tokens read LDS
-        bh = *reinterpret_cast<const u4*>(xh + k);
-        bl = *reinterpret_cast<const u4*>(xl + k);
-      }
-      const bf16x8 av = __builtin_bit_cast(bf16x8, buf.v[t]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bh), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl), acc, 0, 0, 0);
+    const u4 ch = h0, cl = l0;
+    h0 = h1;
+    l0 = l1;
+    if (t + 2 < NKP) {
+      h1 = *reinterpret_cast<const u4*>(xh + 32 * (t + 2));
+      l1 = *reinterpret_cast<const u4*>(xl + 32 * (t + 2));
     }
+    const bf16x8 av = __builtin_bit_cast(bf16x8, buf.v[t]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, ch), acc, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, cl), acc2, 0, 0, 0);
   }
+  // keep that order in the schedule: 4 LDS reads first, then one MFMA and one read alternately (the
+  // scheduler would otherwise serialise each MFMA behind its own read to save registers)
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < 2 * NKP - 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+__device__ __forceinline__ void mg_compute_any(const MBuf& buf, f4& acc, f4& acc2, const MGeo& g, int pass, int nb, Lds& S) {
+  if (g.nks % NKP == 0) mg_compute_full(buf, acc, acc2, g, pass, nb, S);
+  else mg_compute(buf, acc, acc2, g, pass, nb, S);
 }
 
 // A tile that is exactly one pass with every wave busy (16-row blocks times K-slices fill the workgroup, and
@@ -774,15 +871,15 @@ __device__ __forceinline__ void mgemv_task(KA& a, Desc w, int t, const RowPtr& W
   if (SPLIT) split_x(nb, K, S);
   if (AHEAD == 1 && g.np > 1) mg_load(b1, W, g, 1);
   mark(a, t, 0);
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  f4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
   for (int p = 0; p < g.np; p += 2) {
-    mg_compute(b0, acc, g, p, nb, S);
+    mg_compute_any(b0, acc, acc2, g, p, nb, S);
     if (p + 2 < g.np) mg_load(b0, W, g, p + 2);
     if (p + 1 >= g.np) break;
-    mg_compute(b1, acc, g, p + 1, nb, S);
+    mg_compute_any(b1, acc, acc2, g, p + 1, nb, S);
     if (p + 3 < g.np) mg_load(b1, W, g, p + 3);
   }
-  mg_finish(acc, g, nb, out, S);
+  mg_finish(acc + acc2, g, nb, out, S);
   mark(a, t, 1);
 }
 
@@ -882,8 +979,7 @@ __device__ __forceinline__ void task_qkv(KA& a, Desc w, int t, Lds& S) {
       a, w, t, Rows1{W, d}, r1 - r0, d, a.B, 0, N_WAITS,
       [&] {
         if (!staged) {
-          stage_norm(a, gn, a.B, nullptr, S);
-          split_x(a.B, d, S);
+          stage_split(a, gn, a.B, nullptr, S);
         }
       },
       [&](int r, int b, float v) { pub(out + b * bstride + r, v); }, S);
@@ -942,8 +1038,7 @@ __device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
   const bool early = B <= 2;
   if (early && __builtin_amdgcn_readfirstlane(S.xb_layer) != l + 1) {  // not staged by this workgroup's last task
     wait_deps(a, w, 1, 2, t);
-    stage_norm(a, gn, B, nullptr, S);
-    split_x(B, d, S);
+    stage_split(a, gn, B, nullptr, S);
     if (tidx() == 0) S.xb_layer = l + 1;
   }
   const int e = slot_routing(a, wait_value(a, w, 0, t, S), S);
@@ -959,10 +1054,10 @@ __device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
       MBuf b0;
       mg_load_full(b0, Rows2{Wg, Wu, d, nr}, g);
       mark(a, t, 2);  // weights requested
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      f4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
       mark(a, t, 0);
-      mg_compute(b0, acc, g, 0, B, S);
-      mg_finish(acc, g, B, out, S);
+      mg_compute_full(b0, acc, acc2, g, 0, B, S);
+      mg_finish(acc + acc2, g, B, out, S);
       mark(a, t, 1);
     } else {
       mgemv_task<false, 1>(
@@ -970,8 +1065,7 @@ __device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
           [&] {
             mark(a, t, 2);  // weights requested
             if (!early) {
-              stage_norm(a, gn, n, S.slot_b, S);
-              split_x(n, d, S);
+              stage_split(a, gn, n, S.slot_b, S);
             }
           },
           out, S);
@@ -1060,9 +1154,8 @@ __device__ __forceinline__ void lm_phase(KA& a, Lds& S) {
   float bv = -INFINITY;  // best of this lane's token so far
   int bi = 0x7fffffff;
   if (any) {
-    stage_norm(a, gn, B, nullptr, S);
-    split_x(B, d, S);
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    stage_split(a, gn, B, nullptr, S);
+    f4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
     uint32_t pend = 0;
     bool done = false;
     // pass q: compute, then request pass q + 2 into the same buffer
@@ -1076,21 +1169,23 @@ __device__ __forceinline__ void lm_phase(KA& a, Lds& S) {
         }
         if (tidx() == 0) pend = __hip_atomic_fetch_add(&a.ctr[a.c_lm_pool], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         acc = f4{0.f, 0.f, 0.f, 0.f};
+        acc2 = f4{0.f, 0.f, 0.f, 0.f};
       }
       const int id = S.lmq[k % LMQ];
       if (id >= nch) {
         done = true;
         return;
       }
-      mg_compute(buf, acc, g, p, B, S);
+      mg_compute_any(buf, acc, acc2, g, p, B, S);
       if (p == np - 1) {
+        const f4 tot = acc + acc2;
         const int j = lane & 15, qd = lane >> 4;
         if (j < B) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int row = id * CHR + wave * 16 + 4 * qd + r;
             if (row < V) {
-              const float v = acc[r];
+              const float v = tot[r];
               a.logits[(int64_t)j * V + row] = v;
               if (v > bv || (v == bv && row < bi)) {
                 bv = v;
