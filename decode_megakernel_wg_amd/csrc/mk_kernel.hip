@@ -759,9 +759,13 @@ __device__ __forceinline__ void mg_compute(const MBuf& buf, f4& acc, f4& acc2, c
   }
 }
 
-// mg_compute for a pass whose NKP k-steps all exist (g.nks a multiple of NKP): no per-step condition, so the
-// unrolled steps are straight-line code.
-__device__ __forceinline__ void mg_compute_full(const MBuf& buf, f4& acc, f4& acc2, const MGeo& g, int pass, int nb, Lds& S) {
+// mg_compute for the first STEPS k-steps of a pass, all of which exist: no per-step condition, so the
+// unrolled steps are straight-line code.  The activations of step t + 2 are requested before the MFMAs of
+// step t, and scheduling groups keep four LDS reads in flight ahead of the MFMAs (the scheduler would
+// otherwise serialise each MFMA behind its own read to save registers).
+template <int STEPS>
+__device__ __forceinline__ void mg_compute_steps(const MBuf& buf, f4& acc, f4& acc2, const MGeo& g, int pass, int nb, Lds& S) {
+  static_assert(STEPS >= 2 && STEPS <= NKP, "steps per pass");
   const int wave = tidx() >> 6, lane = tidx() & 63;
   const int rb = wave / g.ks, kp = wave - rb * g.ks;
   if (rb >= g.rbn) return;
@@ -769,15 +773,14 @@ __device__ __forceinline__ void mg_compute_full(const MBuf& buf, f4& acc, f4& ac
   const int jr = j < nb ? j : 0;
   const uint16_t* xh = S.xb + jr * XBP + kp * g.kw + 8 * (lane >> 4) + 32 * NKP * pass;
   const uint16_t* xl = xh + 8 * XBP;
-  // software-pipelined: the activations of step t + 2 are requested before the MFMAs of step t
   u4 h0 = *reinterpret_cast<const u4*>(xh), l0 = *reinterpret_cast<const u4*>(xl);
   u4 h1 = *reinterpret_cast<const u4*>(xh + 32), l1 = *reinterpret_cast<const u4*>(xl + 32);
 #pragma unroll
-  for (int t = 0; t < NKP; ++t) {
+  for (int t = 0; t < STEPS; ++t) {
     const u4 ch = h0, cl = l0;
     h0 = h1;
     l0 = l1;
-    if (t + 2 < NKP) {
+    if (t + 2 < STEPS) {
       h1 = *reinterpret_cast<const u4*>(xh + 32 * (t + 2));
       l1 = *reinterpret_cast<const u4*>(xl + 32 * (t + 2));
     }
@@ -785,18 +788,23 @@ __device__ __forceinline__ void mg_compute_full(const MBuf& buf, f4& acc, f4& ac
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, ch), acc, 0, 0, 0);
     acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, cl), acc2, 0, 0, 0);
   }
-  // keep that order in the schedule: 4 LDS reads first, then one MFMA and one read alternately (the
-  // scheduler would otherwise serialise each MFMA behind its own read to save registers)
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads
 #pragma unroll
-  for (int i = 0; i < 2 * NKP - 4; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  for (int i = 0; i < 2 * STEPS - 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
+__device__ __forceinline__ void mg_compute_full(const MBuf& buf, f4& acc, f4& acc2, const MGeo& g, int pass, int nb, Lds& S) {
+  mg_compute_steps<NKP>(buf, acc, acc2, g, pass, nb, S);
+}
+// A pass of the tile: all NKP k-steps, the first NKP/2 (a K tail such as 768 = 24 steps), or the general
+// predicated form.
 __device__ __forceinline__ void mg_compute_any(const MBuf& buf, f4& acc, f4& acc2, const MGeo& g, int pass, int nb, Lds& S) {
-  if (g.nks % NKP == 0) mg_compute_full(buf, acc, acc2, g, pass, nb, S);
+  const int left = g.nks - pass * NKP;
+  if (left >= NKP) mg_compute_steps<NKP>(buf, acc, acc2, g, pass, nb, S);
+  else if (left == NKP / 2) mg_compute_steps<NKP / 2>(buf, acc, acc2, g, pass, nb, S);
   else mg_compute(buf, acc, acc2, g, pass, nb, S);
 }
 
