@@ -436,23 +436,34 @@ __device__ __forceinline__ void route_select(KA& a, int l, int32_t slot0, Lds& S
   float* key = S.xs;  // [B][E] router logits with NaN replaced by -inf (filled by the caller)
   if (tid < 8) S.used[tid] = 0u;
   __syncthreads();
-  // rank of (b, e) among the token's logits (E is a multiple of 8: 4-wide LDS reads, unrolled)
-  for (int i = tid; i < B * E; i += NT) {
-    const int b = i / E, e = i - b * E;
-    const float v = key[i];
-    const float* kb = key + b * E;
-    int rank = 0;
+  // rank of (b, e) among the token's logits: rq adjacent threads (an aligned group of lanes) share one
+  // (b, e), each counting over its part of the keys (4-wide LDS reads), and their counts are added across
+  // the lanes (E a multiple of 8; four parts when E is a multiple of 16)
+  {
+    const int rq = E % 16 == 0 ? 4 : 1;
+    for (int i0 = tid; i0 < B * E * rq; i0 += NT) {
+      const int i = i0 / rq, qq = i0 - i * rq;
+      const int b = i / E, e = i - b * E;
+      const float v = key[i];
+      const float* kb = key + b * E;
+      const int span = E / rq, q0 = qq * span;
+      int rank = 0;
 #pragma unroll 4
-    for (int q = 0; q < E; q += 4) {
-      const f4 u = *reinterpret_cast<const f4*>(kb + q);
-      rank += (u.x > v) || (u.x == v && q < e);
-      rank += (u.y > v) || (u.y == v && q + 1 < e);
-      rank += (u.z > v) || (u.z == v && q + 2 < e);
-      rank += (u.w > v) || (u.w == v && q + 3 < e);
-    }
-    if (rank < k) {
-      S.sel[b * 8 + rank] = e;
-      atomicOr(&S.used[e >> 5], 1u << (e & 31));
+      for (int q = q0; q < q0 + span; q += 4) {
+        const f4 u = *reinterpret_cast<const f4*>(kb + q);
+        rank += (u.x > v) || (u.x == v && q < e);
+        rank += (u.y > v) || (u.y == v && q + 1 < e);
+        rank += (u.z > v) || (u.z == v && q + 2 < e);
+        rank += (u.w > v) || (u.w == v && q + 3 < e);
+      }
+      if (rq == 4) {
+        rank += __shfl_xor(rank, 1);
+        rank += __shfl_xor(rank, 2);
+      }
+      if (qq == 0 && rank < k) {
+        S.sel[b * 8 + rank] = e;
+        atomicOr(&S.used[e >> 5], 1u << (e & 31));
+      }
     }
   }
   __syncthreads();
@@ -624,12 +635,12 @@ __device__ __forceinline__ void route_from_partials(KA& a, int l, int32_t slot0,
     const int b = i / E, e = i - b * E;
     double sum = 0.0;
     int r = 0;
-    for (; r + 8 <= nrt; r += 8) {
-      double v[8];
+    for (; r + 16 <= nrt; r += 16) {  // 16 partials requested together, then added in tile order
+      double v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = rp[((int64_t)(r + u) * B + b) * E + e];
+      for (int u = 0; u < 16; ++u) v[u] = rp[((int64_t)(r + u) * B + b) * E + e];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sum += v[u];
+      for (int u = 0; u < 16; ++u) sum += v[u];
     }
     for (; r < nrt; ++r) sum += rp[((int64_t)r * B + b) * E + e];
     sums[i] = sum;
