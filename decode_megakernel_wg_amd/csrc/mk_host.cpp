@@ -13,7 +13,7 @@
 #include "mk_kargs.h"
 #include "mk_plan.h"
 
-extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int kclass, int grid, hipStream_t stream);
+extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int kclass, int grid, int wide, hipStream_t stream);
 extern "C" int mk_kernel_class(int d_head, int group, int d_model, int d_ffn);
 
 namespace {
@@ -334,7 +334,7 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   a.task_done = m->task_done;
   a.ts = (m->dbg & MK_DBG_TIMESTAMPS) ? m->ts : nullptr;
   a.ctr_snapshot = m->ctr_snapshot;
-  HIPCHK(mk_launch_persistent(&a, m->kclass, m->grid, s));
+  HIPCHK(mk_launch_persistent(&a, m->kclass, m->grid, (m->dbg & MK_DBG_WIDE_GEMV) ? 1 : 0, s));
   m->stepped = true;
   return MK_OK;
 }

@@ -31,8 +31,8 @@ namespace mk {
 constexpr int NT = 512;          // threads per workgroup
 constexpr int NW = NT / 64;      // waves per workgroup
 constexpr int XS_FLOATS = 16384; // 64 KB LDS staging area (fp32 activations, attention scratch)
-constexpr int XBP = 2048 + 8;     // bf16 row pitch of the split activations (the 16-byte skew spreads rows over banks)
-constexpr int NKP = 16;           // MFMA k-steps (32 K values each) per pass and wave
+constexpr int XBP = 2048 + 32;    // bf16 row pitch of the split activations (rows 64 bytes apart modulo the bank window)
+constexpr int NKP = 16;           // GEMV loads (16 bytes per lane) per pass and wave
 constexpr uint32_t SPIN_LIMIT = 1u << 21;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -47,9 +47,10 @@ struct NVR {
 // the three GEMV reduction lengths (d_model, d_ffn, group * d_head).  One kernel is instantiated per
 // class so that each task type has a single code path (the register allocator handles one variant per
 // task far better than a switch over many).
-template <int DH_, int GRP_, int NVD_, int NVF_, int NVO_>
+template <int DH_, int GRP_, int NVD_, int NVF_, int NVO_, int NB_>
 struct Cfg {
   static constexpr int DH = DH_, GRP = GRP_, NVD = NVD_, NVF = NVF_, NVO = NVO_;
+  static constexpr int NB = NB_;  // batch class of the matrix-core GEMV: at most 2, or at most 8 tokens
 };
 // Global-address-space views: loads through them are global_load (vmcnt only), never flat loads,
 // which would also count against lgkmcnt and make every LDS wait wait for in-flight weight loads.
@@ -64,7 +65,7 @@ typedef const __attribute__((address_space(4))) KArgs KA;
 
 struct Lds {
   float xs[XS_FLOATS];   // activation staging (GEMV inputs), attention reduction scratch
-  uint16_t xb[16 * XBP]; // GEMV inputs split into BF16 hi (rows 0..7) and lo (rows 8..15) parts
+  uint16_t xb[16 * XBP + 64]; // GEMV inputs split into BF16 hi and lo parts (xb_off)
   float q[8 * 128];      // attention: RoPE'd, scaled queries of one KV group
   float sc[8 * 128];     // attention: scores of one chunk [head][position]; LM head: tile logits [row][token]
   float pt[256 * 8];     // attention: probabilities of one chunk [position][head]
@@ -93,6 +94,11 @@ struct Desc {
   const int32_t* p;
   __device__ __forceinline__ int32_t operator[](int i) const { return __builtin_amdgcn_readfirstlane(p[i]); }
 };
+
+// Offset (bf16 elements) of token t's part p (0 = hi, 1 = lo) in S.xb.  Rows are XBP apart (64 bytes
+// modulo the 256-byte bank window) and the lo rows start 128 bytes further, so the four slots read
+// together (tokens 0..3 of one part, or tokens 0..1 of both) fall in distinct bank windows.
+__device__ __forceinline__ int xb_off(int t, int p) { return p * (8 * XBP + 64) + t * XBP; }
 
 // ------------------------------------------------------------------------------------------ helpers
 
@@ -308,9 +314,9 @@ __device__ __forceinline__ void stage_norm(KA& a, const NormGain& gn, int nb, co
   stage_norm_finish(a, gn, nb, S);
 }
 
-// RMSNorm of the residual stream straight into the BF16 hi/lo matrix-core operand (xb rows j and 8 + j for
-// staging row j < nb, token tok[j]): one read of the staged rows, no normalised fp32 copy.  inv_rms[b] is
-// formed as in stage_norm_finish (tile order); wave j sums token j's partials.
+// RMSNorm of the residual stream straight into the BF16 hi/lo matrix-core operand (xb_off(j, 0) and
+// xb_off(j, 1) for staging row j < nb, token tok[j]): one read of the staged rows, no normalised fp32
+// copy.  inv_rms[b] is formed as in stage_norm_finish (tile order); wave j sums token j's partials.
 __device__ __forceinline__ void stage_split(KA& a, const NormGain& gn, int nb, const int* tok, Lds& S) {
   const int d = a.d, nrt = a.n_rt;
   stage_norm_issue(a, nb, tok, S);
@@ -346,25 +352,15 @@ __device__ __forceinline__ void stage_split(KA& a, const NormGain& gn, int nb, c
         const float x0 = xv.x * (g0 * inv), x1 = xv.y * (g1 * inv);
         const uint16_t h0 = f2bf(x0), h1 = f2bf(x1);
         const uint16_t l0 = f2bf(x0 - bf2f(h0)), l1 = f2bf(x1 - bf2f(h1));
-        *reinterpret_cast<uint32_t*>(S.xb + j * XBP + 2 * p) = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        *reinterpret_cast<uint32_t*>(S.xb + (8 + j) * XBP + 2 * p) = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        *reinterpret_cast<uint32_t*>(S.xb + xb_off(j, 0) + 2 * p) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        *reinterpret_cast<uint32_t*>(S.xb + xb_off(j, 1) + 2 * p) = (uint32_t)l0 | ((uint32_t)l1 << 16);
       }
     }
   }
   lds_sync();
 }
 
-// ------------------------------------------------------------------------------------------ GEMV core
-// A row tile W[0..nrows) x [0..K) (row stride ld) times NB staged vectors xs[b][0..K) (pitch xp).
-// Wave w handles rows [p*NW*RPW + w*RPW, +RPW) of pass p; lane l reads 16-byte vectors l, l+64, ...
-// of each row (NV per row).  Loads of pass p+1 are issued before pass p is computed; the caller
-// issues pass 0 before its dependency wait.
-
-template <int NV, int RPW>
-struct WBuf {
-  u4 v[RPW][NV];
-};
-
+// ------------------------------------------------------------------------------------------ weight rows
 // Row addressing of a tile: row r lives at base + r * ld (one segment), or rows [split, ...) at a second base.
 struct Rows1 {
   const uint16_t* base;
@@ -380,48 +376,6 @@ struct Rows2 {
     return r < split ? base0 + (int64_t)r * ld : base1 + (int64_t)(r - split) * ld;
   }
 };
-
-template <int NV, int RPW, class RowPtr>
-__device__ __forceinline__ void gemv_load(WBuf<NV, RPW>& buf, const RowPtr& W, int nrows, int K8, int pass) {
-  const int wave = tidx() >> 6, lane = tidx() & 63;
-  const int row0 = pass * NW * RPW + wave * RPW;
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int row = row0 + r;
-    gu4* rp = as_global(row < nrows ? W(row) : nullptr);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int c8 = lane + 64 * i;
-      if (row < nrows && c8 < K8)
-        buf.v[r][i] = __builtin_nontemporal_load(rp + c8);
-      else
-        buf.v[r][i] = u4{0, 0, 0, 0};
-    }
-  }
-}
-
-__device__ __forceinline__ float dot8(u4 w, const f4& x0, const f4& x1, float acc) {
-  acc = fmaf(bf_lo(w.x), x0.x, acc);
-  acc = fmaf(bf_hi(w.x), x0.y, acc);
-  acc = fmaf(bf_lo(w.y), x0.z, acc);
-  acc = fmaf(bf_hi(w.y), x0.w, acc);
-  acc = fmaf(bf_lo(w.z), x1.x, acc);
-  acc = fmaf(bf_hi(w.z), x1.y, acc);
-  acc = fmaf(bf_lo(w.w), x1.z, acc);
-  acc = fmaf(bf_hi(w.w), x1.w, acc);
-  return acc;
-}
-__device__ __forceinline__ double dot8d(u4 w, const f4& x0, const f4& x1, double acc) {
-  acc = fma((double)bf_lo(w.x), (double)x0.x, acc);
-  acc = fma((double)bf_hi(w.x), (double)x0.y, acc);
-  acc = fma((double)bf_lo(w.y), (double)x0.z, acc);
-  acc = fma((double)bf_hi(w.y), (double)x0.w, acc);
-  acc = fma((double)bf_lo(w.z), (double)x1.x, acc);
-  acc = fma((double)bf_hi(w.z), (double)x1.y, acc);
-  acc = fma((double)bf_lo(w.w), (double)x1.z, acc);
-  acc = fma((double)bf_hi(w.w), (double)x1.w, acc);
-  return acc;
-}
 
 // ------------------------------------------------------------------------------------------ routing
 // Done once per layer by the workgroup that completes the layer's router logits: top-k of each token's
@@ -692,15 +646,26 @@ __device__ __forceinline__ void resid_chain(KA& a, Desc w, Lds& S) {
 }
 
 // ------------------------------------------------------------------------------------------ MFMA GEMV core
-// A tile of nrows x K BF16 weights times nb <= 8 activation vectors, on v_mfma_f32_16x16x32_bf16: the
-// weights are the A operand as loaded (16 rows x 32 K per instruction, no conversion), the activations
-// the B operand with token j in column j, split into BF16 hi + lo parts (two MFMAs, ~16 mantissa bits,
-// fp32 accumulation).  The reduction over K happens inside the MFMA; wave w owns row block w / ks and
-// K-slice w % ks, and the ks partials of a row block are summed in a fixed order through LDS.
-// Operand layout (checked on gfx950): lane l holds A[l%16][8(l/16)+v], B[8(l/16)+v][l%16] and
-// D[4(l/16)+r][l%16].
+// A tile of nrows x K BF16 weights times nb <= 8 activation vectors on v_mfma_f32_16x16x32_bf16, fp32
+// accumulation.  Operand layout of the instruction (checked on gfx950): lane l holds A[l%16][8(l/16)+v],
+// B[8(l/16)+v][l%16] and D[4(l/16)+i][l%16].
+//
+// Row quads.  A row m = 4r + h of the A operand holds weight row r of a quad of four rows at K-part h,
+// where part h of a 128-wide K block is its 16-byte chunks h, h+4, h+8 and h+12.  Lane l therefore loads
+// chunk 4(l/16) + l%4 of quad row (l%16)/4: every four consecutive lanes read 64 contiguous bytes of one
+// row, a pattern the per-CU load path serves about twice as fast as the plain A layout's sixteen rows of
+// 16 bytes (measured on this part).  The activations take the same K order: B column n = 4s + h holds
+// activation slot s at K-part h, so D[4r + h][4s + h] is row r times slot s over part h, and the four
+// parts are added across the four lanes of a quad.  The activations are split into BF16 hi + lo parts
+// (~16 mantissa bits): for nb <= 2 the four slots are (hi, token 0), (hi, token 1), (lo, token 0),
+// (lo, token 1) and one MFMA covers a quad and K block; for larger nb a slot is a token, one MFMA takes
+// the hi parts and one the lo parts of four tokens, both accumulating into the same D.
+//
+// Wave w owns a 16-row block (four quads) and a K slice (w / ks, w % ks); a pass is four K blocks of its
+// four quads, 16 loads of 16 bytes per lane; the K-slice partials of a row block are added in a fixed
+// order through LDS.
 struct MGeo {
-  int nrows, K, rbn, ks, kw, nks, np;
+  int nrows, K, rbn, ks, kw, nkb, np;
 };
 __device__ __forceinline__ MGeo mgeo(int nrows, int K) {
   MGeo g;
@@ -708,157 +673,228 @@ __device__ __forceinline__ MGeo mgeo(int nrows, int K) {
   g.K = K;
   g.rbn = (nrows + 15) >> 4;  // row blocks (at most NW)
   int ks = 1;
-  while (g.rbn * ks * 2 <= NW && K % (64 * ks) == 0) ks *= 2;
+  while (g.rbn * ks * 2 <= NW && K % (256 * ks) == 0) ks *= 2;
   g.ks = ks;
-  g.kw = K / ks;
-  g.nks = g.kw >> 5;
-  g.np = (g.nks + NKP - 1) / NKP;
+  g.kw = K / ks;       // a multiple of 128
+  g.nkb = g.kw >> 7;   // 128-wide K blocks per slice
+  g.np = (g.nkb + 3) >> 2;
   return g;
 }
 struct MBuf {
-  u4 v[NKP];
+  u4 v[NKP];  // unit t = 4 * (K block) + quad
 };
+// per-quad accumulators: slots of tokens 0..3 (or of nb <= 2), and of tokens 4..7
+struct MAcc {
+  f4 a[4], b[4];
+};
+__device__ __forceinline__ void macc_zero(MAcc& m) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    m.a[q] = f4{0.f, 0.f, 0.f, 0.f};
+    m.b[q] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Column offset (bf16 elements) of this lane's 16-byte chunk within pass `pass` of its K slice.
+__device__ __forceinline__ int mg_col(const MGeo& g, int kp, int pass, int lane) {
+  return kp * g.kw + 512 * pass + 32 * (lane >> 4) + 8 * (lane & 3);
+}
 
 template <class RowPtr>
 __device__ __forceinline__ void mg_load(MBuf& buf, const RowPtr& W, const MGeo& g, int pass) {
   const int wave = tidx() >> 6, lane = tidx() & 63;
   const int rb = wave / g.ks, kp = wave - rb * g.ks;
-  const int row = rb * 16 + (lane & 15);
-  const bool ok = rb < g.rbn && row < g.nrows;
-  gu4* rp = as_global(ok ? W(row) : W(0));
-  const int v0 = (kp * g.kw + 8 * (lane >> 4)) >> 3;
+  const int c = mg_col(g, kp, pass, lane);
+  gu4* rp[4];
+  bool ok[4];
 #pragma unroll
-  for (int t = 0; t < NKP; ++t) {
-    const int s = pass * NKP + t;
-    buf.v[t] = (ok && s < g.nks) ? __builtin_nontemporal_load(rp + v0 + 4 * s) : u4{0, 0, 0, 0};
+  for (int q = 0; q < 4; ++q) {
+    const int row = rb * 16 + 4 * q + ((lane & 15) >> 2);
+    ok[q] = rb < g.rbn && row < g.nrows;
+    rp[q] = as_global((ok[q] ? W(row) : W(0)) + c);
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const bool kok = 4 * pass + kb < g.nkb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      buf.v[4 * kb + q] = (ok[q] && kok) ? __builtin_nontemporal_load(rp[q] + 16 * kb) : u4{0, 0, 0, 0};
   }
 }
 
-__device__ __forceinline__ void mg_compute(const MBuf& buf, f4& acc, f4& acc2, const MGeo& g, int pass, int nb, Lds& S) {
-  const int wave = tidx() >> 6, lane = tidx() & 63;
-  const int rb = wave / g.ks, kp = wave - rb * g.ks;
-  if (rb >= g.rbn) return;
-  // Columns of absent tokens (j >= nb) read token 0's row: every lane of a 16-lane group then reads the same
-  // LDS address (a broadcast, so no extra LDS traffic), no lane is masked off, and those MFMA output columns
-  // are never used.
-  const int j = lane & 15;
-  const int jr = j < nb ? j : 0;
-  const uint16_t* xh = S.xb + jr * XBP + kp * g.kw + 8 * (lane >> 4);
-  const uint16_t* xl = xh + 8 * XBP;
-  // activations of 2 k-steps are read from LDS together, then their 4 MFMAs run; the hi and lo parts
-  // accumulate separately (two independent chains), summed by the caller
-#pragma unroll
-  for (int t0 = 0; t0 < NKP; t0 += 2) {
-    u4 bh[2], bl[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int s = pass * NKP + t0 + u;
-      if (s < g.nks) {  // wave-uniform
-        bh[u] = *reinterpret_cast<const u4*>(xh + 32 * s);
-        bl[u] = *reinterpret_cast<const u4*>(xl + 32 * s);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int s = pass * NKP + t0 + u;
-      if (s < g.nks) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, buf.v[t0 + u]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bh[u]), acc, 0, 0, 0);
-        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl[u]), acc2, 0, 0, 0);
-      }
-    }
-  }
-}
-
-// mg_compute for the first STEPS k-steps of a pass, all of which exist: no per-step condition, so the
-// unrolled steps are straight-line code.  The activations of step t + 2 are requested before the MFMAs of
-// step t, and scheduling groups keep four LDS reads in flight ahead of the MFMAs (the scheduler would
-// otherwise serialise each MFMA behind its own read to save registers).
-template <int STEPS>
-__device__ __forceinline__ void mg_compute_steps(const MBuf& buf, f4& acc, f4& acc2, const MGeo& g, int pass, int nb, Lds& S) {
-  static_assert(STEPS >= 2 && STEPS <= NKP, "steps per pass");
-  const int wave = tidx() >> 6, lane = tidx() & 63;
-  const int rb = wave / g.ks, kp = wave - rb * g.ks;
-  if (rb >= g.rbn) return;
-  const int j = lane & 15;
-  const int jr = j < nb ? j : 0;
-  const uint16_t* xh = S.xb + jr * XBP + kp * g.kw + 8 * (lane >> 4) + 32 * NKP * pass;
-  const uint16_t* xl = xh + 8 * XBP;
-  u4 h0 = *reinterpret_cast<const u4*>(xh), l0 = *reinterpret_cast<const u4*>(xl);
-  u4 h1 = *reinterpret_cast<const u4*>(xh + 32), l1 = *reinterpret_cast<const u4*>(xl + 32);
-#pragma unroll
-  for (int t = 0; t < STEPS; ++t) {
-    const u4 ch = h0, cl = l0;
-    h0 = h1;
-    l0 = l1;
-    if (t + 2 < STEPS) {
-      h1 = *reinterpret_cast<const u4*>(xh + 32 * (t + 2));
-      l1 = *reinterpret_cast<const u4*>(xl + 32 * (t + 2));
-    }
-    const bf16x8 av = __builtin_bit_cast(bf16x8, buf.v[t]);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, ch), acc, 0, 0, 0);
-    acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, cl), acc2, 0, 0, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads
-#pragma unroll
-  for (int i = 0; i < 2 * STEPS - 4; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-}
-__device__ __forceinline__ void mg_compute_full(const MBuf& buf, f4& acc, f4& acc2, const MGeo& g, int pass, int nb, Lds& S) {
-  mg_compute_steps<NKP>(buf, acc, acc2, g, pass, nb, S);
-}
-// A pass of the tile: all NKP k-steps, the first NKP/2 (a K tail such as 768 = 24 steps), or the general
-// predicated form.
-__device__ __forceinline__ void mg_compute_any(const MBuf& buf, f4& acc, f4& acc2, const MGeo& g, int pass, int nb, Lds& S) {
-  const int left = g.nks - pass * NKP;
-  if (left >= NKP) mg_compute_steps<NKP>(buf, acc, acc2, g, pass, nb, S);
-  else if (left == NKP / 2) mg_compute_steps<NKP / 2>(buf, acc, acc2, g, pass, nb, S);
-  else mg_compute(buf, acc, acc2, g, pass, nb, S);
-}
-
-// A tile that is exactly one pass with every wave busy (16-row blocks times K-slices fill the workgroup, and
-// each slice is NKP k-steps): its loads need no predicate, so the compiler counts them and each MFMA waits
-// only for its own weights (vmcnt(15), vmcnt(14), ...): the tile is computed as its data arrives instead of
-// after the last load.  Used where a tile's weights are requested only when the tile can run.
+// A tile that is exactly one pass with every wave busy (16-row blocks times K slices fill the workgroup, and
+// each slice is four K blocks): its loads need no predicate, so the compiler counts them and each MFMA waits
+// only for its own weights: the tile is computed as its data arrives instead of after the last load.  Used
+// where a tile's weights are requested only when the tile can run.
 __device__ __forceinline__ bool mg_one_full_pass(const MGeo& g) {
-  return g.rbn * g.ks == NW && g.nrows == 16 * g.rbn && g.nks == NKP;
+  return g.rbn * g.ks == NW && g.nrows == 16 * g.rbn && g.nkb == 4;
 }
 template <class RowPtr>
 __device__ __forceinline__ void mg_load_full(MBuf& buf, const RowPtr& W, const MGeo& g) {
   const int wave = tidx() >> 6, lane = tidx() & 63;
   const int rb = wave / g.ks, kp = wave - rb * g.ks;
-  gu4* rp = as_global(W(rb * 16 + (lane & 15)));
-  const int v0 = (kp * g.kw + 8 * (lane >> 4)) >> 3;
+  const int c = mg_col(g, kp, 0, lane);
+  gu4* rp[4];
 #pragma unroll
-  for (int t = 0; t < NKP; ++t) buf.v[t] = __builtin_nontemporal_load(rp + v0 + 4 * t);
+  for (int q = 0; q < 4; ++q) rp[q] = as_global(W(rb * 16 + 4 * q + ((lane & 15) >> 2)) + c);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) buf.v[4 * kb + q] = __builtin_nontemporal_load(rp[q] + 16 * kb);
+}
+
+__device__ __forceinline__ u4 lds16(const uint16_t* p) { return *reinterpret_cast<const u4*>(p); }
+__device__ __forceinline__ f4 mfma(u4 av, u4 bv, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
+}
+
+// K blocks KB0 .. KB0 + KB - 1 of the pass (units 4 * KB0 ...), all present.
+template <int NB, int KB, int KB0 = 0>
+__device__ __forceinline__ void mg_compute_kb(const MBuf& buf, MAcc& acc, const MGeo& g, int pass, int nb, Lds& S) {
+  constexpr int kb0 = KB0;
+  const int wave = tidx() >> 6, lane = tidx() & 63;
+  const int rb = wave / g.ks, kp = wave - rb * g.ks;
+  if (rb >= g.rbn) return;
+  const int s = (lane & 15) >> 2;  // this lane's B slot
+  const int c = mg_col(g, kp, pass, lane) + 128 * kb0;
+  if (NB <= 2) {
+    // slot s = (part s / 2, token s % 2); absent tokens read token 0 (their D columns are never used)
+    const int tk = s & 1;
+    const uint16_t* xp = S.xb + xb_off(tk < nb ? tk : 0, s >> 1) + c;
+    u4 x0 = lds16(xp), x1 = KB > 1 ? lds16(xp + 128) : x0;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const u4 cx = x0;
+      x0 = x1;
+      if (kb + 2 < KB) x1 = lds16(xp + 128 * (kb + 2));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc.a[q] = mfma(buf.v[4 * (kb0 + kb) + q], cx, acc.a[q]);
+    }
+    // two activation reads ahead of the MFMAs (the scheduler would otherwise put each read right before its
+    // first use)
+    __builtin_amdgcn_sched_group_barrier(0x100, KB > 1 ? 2 : 1, 0);
+#pragma unroll
+    for (int i = 0; i < KB - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, KB > 1 ? 8 : 4, 0);
+  } else {
+    // group 0: tokens 0..3 into acc.a; group 1: tokens 4..7 into acc.b
+    const int t0 = s < nb ? s : 0, t1 = 4 + s < nb ? 4 + s : 0;
+    const uint16_t* xh0 = S.xb + xb_off(t0, 0) + c;
+    const uint16_t* xl0 = S.xb + xb_off(t0, 1) + c;
+    const uint16_t* xh1 = S.xb + xb_off(t1, 0) + c;
+    const uint16_t* xl1 = S.xb + xb_off(t1, 1) + c;
+    const bool g1 = NB > 4 && nb > 4;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const u4 h0 = lds16(xh0 + 128 * kb), l0 = lds16(xl0 + 128 * kb);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc.a[q] = mfma(buf.v[4 * (kb0 + kb) + q], h0, acc.a[q]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc.a[q] = mfma(buf.v[4 * (kb0 + kb) + q], l0, acc.a[q]);
+      if (g1) {
+        const u4 h1 = lds16(xh1 + 128 * kb), l1 = lds16(xl1 + 128 * kb);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc.b[q] = mfma(buf.v[4 * (kb0 + kb) + q], h1, acc.b[q]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc.b[q] = mfma(buf.v[4 * (kb0 + kb) + q], l1, acc.b[q]);
+      }
+    }
+  }
+}
+template <int NB>
+__device__ __forceinline__ void mg_compute_full(const MBuf& buf, MAcc& acc, const MGeo& g, int pass, int nb, Lds& S) {
+  mg_compute_kb<NB, 4>(buf, acc, g, pass, nb, S);
+}
+// A pass of the tile: all four K blocks, or the K tail's one to three (768 = 6 blocks: a pass of 4, then 2).
+template <int NB>
+__device__ __forceinline__ void mg_compute_any(const MBuf& buf, MAcc& acc, const MGeo& g, int pass, int nb, Lds& S) {
+  const int left = g.nkb - 4 * pass;
+  if (left >= 4) {
+    mg_compute_kb<NB, 4>(buf, acc, g, pass, nb, S);
+  } else if (left >= 2) {
+    mg_compute_kb<NB, 2>(buf, acc, g, pass, nb, S);
+    if (left == 3) mg_compute_kb<NB, 1, 2>(buf, acc, g, pass, nb, S);
+  } else {
+    mg_compute_kb<NB, 1>(buf, acc, g, pass, nb, S);
+  }
+}
+
+// Per lane and quad q: the four K parts added across the quad's lanes (lanes 4i..4i+3 all get the sum), and
+// for nb <= 2 the lo slots added to the hi slots.  Lane l with l % 4 == 0 then holds row 4q + l / 16 of the
+// row block for slot (l / 4) % 4: token s in va (nb <= 2: s < 2 only), token 4 + s in vb.
+__device__ __forceinline__ float pick4(f4 v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+template <int NB>
+__device__ __forceinline__ void mg_lane_values(const MAcc& acc, int nb, float (&va)[4], float (&vb)[4]) {
+  const int i = tidx() & 3;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float x = pick4(acc.a[q], i);
+    x += dpp<0xB1>(x);  // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);  // quad_perm [2,3,0,1]
+    if (NB <= 2) x += dpp<0x128>(x);  // row_ror:8: slot s + 2 (lo) onto slot s (hi)
+    va[q] = x;
+    float y = 0.f;
+    if (NB > 4 && nb > 4) {
+      y = pick4(acc.b[q], i);
+      y += dpp<0xB1>(y);
+      y += dpp<0x4E>(y);
+    }
+    vb[q] = y;
+  }
+}
+// Hand (row within the 16-row block, token, value) of this lane's results to f.
+template <int NB, class F>
+__device__ __forceinline__ void mg_emit(const float (&va)[4], const float (&vb)[4], int nb, F&& f) {
+  const int lane = tidx() & 63;
+  if (lane & 3) return;
+  const int s = (lane >> 2) & 3;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 4 * q + (lane >> 4);
+    if (NB <= 2) {
+      if (s < nb) f(r, s, va[q]);
+    } else {
+      if (s < nb) f(r, s, va[q]);
+      if (4 + s < nb) f(r, 4 + s, vb[q]);
+    }
+  }
 }
 
 // Sum the K-slice partials of each row block (fixed order) and hand (row, token, value) to out().
-template <class Out>
-__device__ __forceinline__ void mg_finish(f4 acc, const MGeo& g, int nb, Out& out, Lds& S) {
+template <int NB, class Out>
+__device__ __forceinline__ void mg_finish(const MAcc& acc, const MGeo& g, int nb, Out& out, Lds& S) {
   const int wave = tidx() >> 6, lane = tidx() & 63;
   const int rb = wave / g.ks, kp = wave - rb * g.ks;
+  float va[4], vb[4];
+  mg_lane_values<NB>(acc, nb, va, vb);
   if (g.ks > 1) {
-    float* red = S.pt;  // [NW][64][4]
-    *reinterpret_cast<f4*>(red + (wave * 64 + lane) * 4) = acc;
-    __syncthreads();
-    if (kp == 0 && rb < g.rbn) {
-      f4 s4 = *reinterpret_cast<const f4*>(red + (wave * 64 + lane) * 4);
-      for (int p = 1; p < g.ks; ++p) s4 += *reinterpret_cast<const f4*>(red + ((wave + p) * 64 + lane) * 4);
-      acc = s4;
-    }
-  }
-  const int j = lane & 15, q = lane >> 4;
-  if (kp == 0 && rb < g.rbn && j < nb) {
+    float* red = S.pt;  // [NW][4 quads][16 quad leaders][2]
+    if (rb < g.rbn && (lane & 3) == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = rb * 16 + 4 * q + r;
-      if (row < g.nrows) out(row, j, acc[r]);
+      for (int q = 0; q < 4; ++q) {
+        red[((wave * 4 + q) * 16 + (lane >> 2)) * 2 + 0] = va[q];
+        red[((wave * 4 + q) * 16 + (lane >> 2)) * 2 + 1] = vb[q];
+      }
+    }
+    __syncthreads();
+    if (kp == 0 && rb < g.rbn && (lane & 3) == 0) {
+      for (int p = 1; p < g.ks; ++p) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          va[q] += red[(((wave + p) * 4 + q) * 16 + (lane >> 2)) * 2 + 0];
+          vb[q] += red[(((wave + p) * 4 + q) * 16 + (lane >> 2)) * 2 + 1];
+        }
+      }
     }
   }
+  if (kp == 0 && rb < g.rbn)
+    mg_emit<NB>(va, vb, nb, [&](int r, int j, float v) {
+      const int row = rb * 16 + r;
+      if (row < g.nrows) out(row, j, v);
+    });
 }
 
 // Split the staged fp32 inputs S.xs[nb][K] into BF16 hi and lo parts.
@@ -868,8 +904,8 @@ __device__ __forceinline__ void split_x(int nb, int K, Lds& S) {
     const int j = i / K, c = i - j * K;
     const float x = S.xs[i];
     const uint16_t h = f2bf(x);
-    S.xb[j * XBP + c] = h;
-    S.xb[(8 + j) * XBP + c] = f2bf(x - bf2f(h));
+    S.xb[xb_off(j, 0) + c] = h;
+    S.xb[xb_off(j, 1) + c] = f2bf(x - bf2f(h));
   }
   lds_sync();
 }
@@ -878,7 +914,7 @@ __device__ __forceinline__ void split_x(int nb, int K, Lds& S) {
 // before the dependency wait [wait0, wait1), so weights stream while the inputs are still being produced;
 // afterwards pass p+1 is requested before pass p is computed.  A tile whose weights are known only at run
 // time (expert up-projection) requests one pass ahead, so that its inputs do not queue behind two passes.
-template <bool SPLIT, int AHEAD = 2, class RowPtr, class Stage, class Out>
+template <int NB, bool SPLIT, int AHEAD = 2, class RowPtr, class Stage, class Out>
 __device__ __forceinline__ void mgemv_task(KA& a, Desc w, int t, const RowPtr& W, int nrows, int K, int nb, int wait0,
                                            int wait1, Stage&& stage, Out&& out, Lds& S) {
   const MGeo g = mgeo(nrows, K);
@@ -890,51 +926,17 @@ __device__ __forceinline__ void mgemv_task(KA& a, Desc w, int t, const RowPtr& W
   if (SPLIT) split_x(nb, K, S);
   if (AHEAD == 1 && g.np > 1) mg_load(b1, W, g, 1);
   mark(a, t, 0);
-  f4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+  MAcc acc;
+  macc_zero(acc);
   for (int p = 0; p < g.np; p += 2) {
-    mg_compute_any(b0, acc, acc2, g, p, nb, S);
+    mg_compute_any<NB>(b0, acc, g, p, nb, S);
     if (p + 2 < g.np) mg_load(b0, W, g, p + 2);
     if (p + 1 >= g.np) break;
-    mg_compute_any(b1, acc, acc2, g, p + 1, nb, S);
+    mg_compute_any<NB>(b1, acc, g, p + 1, nb, S);
     if (p + 3 < g.np) mg_load(b1, W, g, p + 3);
   }
-  mg_finish(acc + acc2, g, nb, out, S);
+  mg_finish<NB>(acc, g, nb, out, S);
   mark(a, t, 1);
-}
-
-// fp64-accumulating variant for the router (products of BF16 and fp32 are exact in fp64).
-template <int NV, int RPW, int NB, class Out>
-__device__ __forceinline__ void gemv_run_f64(WBuf<NV, RPW>& buf0, int nrows, int K, const float* xs, int xp, int nb, Out& out) {
-  const int K8 = K >> 3;
-  const int wave = tidx() >> 6, lane = tidx() & 63;
-  // router tiles hold at most NW*RPW rows: one pass
-  double acc[RPW][NB];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[r][b] = 0.0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int c8 = lane + 64 * i;
-    if (c8 < K8) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const f4 x0 = *reinterpret_cast<const f4*>(xs + b * xp + c8 * 8);
-        const f4 x1 = *reinterpret_cast<const f4*>(xs + b * xp + c8 * 8 + 4);
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) acc[r][b] = dot8d(buf0.v[r][i], x0, x1, acc[r][b]);
-      }
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int row = wave * RPW + r;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const double s = wave_sum_d(acc[r][b]);
-      if (row < nrows && b < nb && lane == 0) out(row, b, s);
-    }
-  }
 }
 
 // ------------------------------------------------------------------------------------------ task bodies
@@ -994,7 +996,7 @@ __device__ __forceinline__ void task_qkv(KA& a, Desc w, int t, Lds& S) {
   const NormGain gn = norm_gain(L.attn_norm, d);
   // a workgroup that staged this layer's input for its previous task keeps it
   const bool staged = __builtin_amdgcn_readfirstlane(S.xb_layer) == l + 1;
-  mgemv_task<false>(
+  mgemv_task<C::NB, false>(
       a, w, t, Rows1{W, d}, r1 - r0, d, a.B, 0, N_WAITS,
       [&] {
         if (!staged) {
@@ -1012,7 +1014,7 @@ __device__ __forceinline__ void task_oproj(KA& a, Desc w, int t, Lds& S) {
   const int grp = a.Hq / a.Hkv, K = grp * a.dh, ldo = a.Hq * a.dh, B = a.B, d = a.d;
   const uint16_t* W = a.layers[l].wo + (int64_t)r0 * ldo + (int64_t)g * K;
   float* out = a.opart + (int64_t)g * B * d + r0;
-  mgemv_task<true>(
+  mgemv_task<C::NB, true>(
       a, w, t, Rows1{W, ldo}, r1 - r0, K, B, 0, N_WAITS,
       [&] {
         for (int b = 0; b < B; ++b) lds_copy(a.attn_o + (int64_t)b * ldo + (int64_t)g * K, S.xs + b * K, K / 4);
@@ -1073,13 +1075,14 @@ __device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
       MBuf b0;
       mg_load_full(b0, Rows2{Wg, Wu, d, nr}, g);
       mark(a, t, 2);  // weights requested
-      f4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+      MAcc acc;
+      macc_zero(acc);
       mark(a, t, 0);
-      mg_compute_full(b0, acc, acc2, g, 0, B, S);
-      mg_finish(acc + acc2, g, B, out, S);
+      mg_compute_full<C::NB>(b0, acc, g, 0, B, S);
+      mg_finish<C::NB>(acc, g, B, out, S);
       mark(a, t, 1);
     } else {
-      mgemv_task<false, 1>(
+      mgemv_task<C::NB, false, 1>(
           a, w, t, Rows2{Wg, Wu, d, nr}, 2 * nr, d, early ? B : n, 0, 0,
           [&] {
             mark(a, t, 2);  // weights requested
@@ -1112,7 +1115,7 @@ __device__ __forceinline__ void task_down(KA& a, Desc w, int t, Lds& S) {
     const int n = S.slot_n;
     const uint16_t* W = wd0 + ((int64_t)e * d + r0) * F;
     const int32_t* ent = a.slots + ((int64_t)l * a.n_slots + s) * SLOT_WORDS;
-    mgemv_task<true>(
+    mgemv_task<C::NB, true>(
         a, w, t, Rows1{W, F}, nr, F, n, 1, N_WAITS,
         [&] {
           // hidden state of the slot's tokens, and their selection ranks and gates
@@ -1138,6 +1141,7 @@ __device__ __forceinline__ void task_down(KA& a, Desc w, int t, Lds& S) {
 // requested before it waits for the final residual stream.  Each workgroup publishes its best logit per
 // token (maximum, lowest index on ties: an order-independent choice); the last one to finish reduces them
 // to the next tokens.
+template <class C>
 __device__ __forceinline__ void lm_phase(KA& a, Lds& S) {
   constexpr int CHR = 128;  // rows per chunk: one 16-row block per wave, no K split
   constexpr int LMQ = 4;    // ring of claimed chunk ids
@@ -1170,11 +1174,13 @@ __device__ __forceinline__ void lm_phase(KA& a, Lds& S) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
-  float bv = -INFINITY;  // best of this lane's token so far
-  int bi = 0x7fffffff;
+  // best (value, row) of this lane's tokens so far: token (lane / 4) % 4 and, for batches above 4, 4 + that
+  float bv[2] = {-INFINITY, -INFINITY};
+  int bi[2] = {0x7fffffff, 0x7fffffff};
   if (any) {
     stage_split(a, gn, B, nullptr, S);
-    f4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+    MAcc acc;
+    macc_zero(acc);
     uint32_t pend = 0;
     bool done = false;
     // pass q: compute, then request pass q + 2 into the same buffer
@@ -1187,32 +1193,32 @@ __device__ __forceinline__ void lm_phase(KA& a, Lds& S) {
           __syncthreads();
         }
         if (tidx() == 0) pend = __hip_atomic_fetch_add(&a.ctr[a.c_lm_pool], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        acc = f4{0.f, 0.f, 0.f, 0.f};
-        acc2 = f4{0.f, 0.f, 0.f, 0.f};
+        macc_zero(acc);
       }
       const int id = S.lmq[k % LMQ];
       if (id >= nch) {
         done = true;
         return;
       }
-      mg_compute_any(buf, acc, acc2, g, p, B, S);
+      mg_compute_any<C::NB>(buf, acc, g, p, B, S);
       if (p == np - 1) {
-        const f4 tot = acc + acc2;
-        const int j = lane & 15, qd = lane >> 4;
-        if (j < B) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = id * CHR + wave * 16 + 4 * qd + r;
-            if (row < V) {
-              const float v = tot[r];
-              a.logits[(int64_t)j * V + row] = v;
-              if (v > bv || (v == bv && row < bi)) {
-                bv = v;
-                bi = row;
+        float va[4], vb[4];
+        mg_lane_values<C::NB>(acc, B, va, vb);
+        mg_emit<C::NB>(va, vb, B, [&](int r, int j, float v) {
+          const int row = id * CHR + wave * 16 + r;
+          if (row < V) {
+            a.logits[(int64_t)j * V + row] = v;
+            if (j < 4) {
+              if (v > bv[0] || (v == bv[0] && row < bi[0])) {
+                bv[0] = v;
+                bi[0] = row;
               }
+            } else if (v > bv[1] || (v == bv[1] && row < bi[1])) {
+              bv[1] = v;
+              bi[1] = row;
             }
           }
-        }
+        });
       }
       load(buf, q + 2);
     };
@@ -1222,21 +1228,29 @@ __device__ __forceinline__ void lm_phase(KA& a, Lds& S) {
       comp(b1, q + 1);
     }
   }
-  // this workgroup's best per token: the 4 lanes of a token in each wave, then the waves in order
+  // this workgroup's best per token: the 4 lanes of a token in each wave (lanes 4s + 16i), then the waves in
+  // order
 #pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-    const float ov = __shfl_xor(bv, o);
-    const int oi = __shfl_xor(bi, o);
-    if (ov > bv || (ov == bv && oi < bi)) {
-      bv = ov;
-      bi = oi;
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float ov = __shfl_xor(bv[u], o);
+      const int oi = __shfl_xor(bi[u], o);
+      if (ov > bv[u] || (ov == bv[u] && oi < bi[u])) {
+        bv[u] = ov;
+        bi[u] = oi;
+      }
     }
   }
   float* wbv = S.sc;                                  // [NW][16]
   int* wbi = reinterpret_cast<int*>(S.sc + NW * 16);  // [NW][16]
-  if (lane < 16) {
-    wbv[wave * 16 + lane] = bv;
-    wbi[wave * 16 + lane] = bi;
+  if (lane < 16 && (lane & 3) == 0) {
+    const int sl = lane >> 2;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      wbv[wave * 16 + 4 * u + sl] = bv[u];
+      wbi[wave * 16 + 4 * u + sl] = bi[u];
+    }
   }
   __syncthreads();
   if (tidx() < B) {
@@ -1729,24 +1743,30 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
     i = i1;
     cur ^= 1;
   }
-  lm_phase(*(KA*)a0, S);
+  lm_phase<C>(*(KA*)a0, S);
   exit_step(a, S);
 }
 
 }  // namespace mk
-// Compiled shape classes: (d_head, group, d_model bound, d_ffn bound, group*d_head bound).
-using CfgFull = mk::Cfg<128, 8, 4, 2, 2>;  // d_head 128, group 8, d_model <= 2048, d_ffn <= 1024, group*d_head = 1024
-using CfgTiny = mk::Cfg<64, 2, 1, 1, 1>;   // d_head 64, group 2, d_model <= 512, d_ffn <= 512, group*d_head = 128
+// Compiled shape classes: (d_head, group, d_model bound, d_ffn bound, group*d_head bound), each in two batch
+// classes (at most 2 tokens: one MFMA per weight block; at most 8: hi and lo MFMAs for each group of 4).
+using CfgFull2 = mk::Cfg<128, 8, 4, 2, 2, 2>;  // d_head 128, group 8, d_model <= 2048, d_ffn <= 1024, group*d_head = 1024
+using CfgFull8 = mk::Cfg<128, 8, 4, 2, 2, 8>;
+using CfgTiny2 = mk::Cfg<64, 2, 1, 1, 1, 2>;   // d_head 64, group 2, d_model <= 512, d_ffn <= 512, group*d_head = 128
+using CfgTiny8 = mk::Cfg<64, 2, 1, 1, 1, 8>;
 
 extern "C" int mk_kernel_class(int d_head, int group, int d_model, int d_ffn) {
-  if (d_head == 128 && group == 8 && d_model <= 64 * 8 * CfgFull::NVD && d_ffn <= 64 * 8 * CfgFull::NVF) return 1;
-  if (d_head == 64 && group == 2 && d_model <= 64 * 8 * CfgTiny::NVD && d_ffn <= 64 * 8 * CfgTiny::NVF) return 2;
+  if (d_head == 128 && group == 8 && d_model <= 64 * 8 * CfgFull2::NVD && d_ffn <= 64 * 8 * CfgFull2::NVF) return 1;
+  if (d_head == 64 && group == 2 && d_model <= 64 * 8 * CfgTiny2::NVD && d_ffn <= 64 * 8 * CfgTiny2::NVF) return 2;
   return 0;
 }
 
-extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int kclass, int grid, hipStream_t stream) {
-  if (kclass == 1) hipLaunchKernelGGL(mk::mk_persistent<CfgFull>, dim3(grid), dim3(mk::NT), 0, stream, *a);
-  else if (kclass == 2) hipLaunchKernelGGL(mk::mk_persistent<CfgTiny>, dim3(grid), dim3(mk::NT), 0, stream, *a);
+extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int kclass, int grid, int wide, hipStream_t stream) {
+  const bool small = a->B <= 2 && !wide;
+  if (kclass == 1 && small) hipLaunchKernelGGL(mk::mk_persistent<CfgFull2>, dim3(grid), dim3(mk::NT), 0, stream, *a);
+  else if (kclass == 1) hipLaunchKernelGGL(mk::mk_persistent<CfgFull8>, dim3(grid), dim3(mk::NT), 0, stream, *a);
+  else if (kclass == 2 && small) hipLaunchKernelGGL(mk::mk_persistent<CfgTiny2>, dim3(grid), dim3(mk::NT), 0, stream, *a);
+  else if (kclass == 2) hipLaunchKernelGGL(mk::mk_persistent<CfgTiny8>, dim3(grid), dim3(mk::NT), 0, stream, *a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

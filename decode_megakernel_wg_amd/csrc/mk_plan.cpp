@@ -54,8 +54,8 @@ int validate_desc(const mk_model_desc* d, std::string* msg) {
     *msg = "d_model must be a multiple of 256, at most 4096";
     return MK_E_UNSUPPORTED;
   }
-  if (d->d_ffn % 32 || d->d_ffn > 2048) {
-    *msg = "d_ffn must be a multiple of 32, at most 2048";
+  if (d->d_ffn % 128 || d->d_ffn > 2048) {
+    *msg = "d_ffn must be a multiple of 128, at most 2048";
     return MK_E_UNSUPPORTED;
   }
   if (d->n_q_heads * d->d_head > 8192) {

@@ -19,6 +19,7 @@ MK_DESC_WORDS = 32
 MK_OK, MK_E_INVAL, MK_E_UNSUPPORTED, MK_E_NOMEM, MK_E_HIP, MK_E_STATE, MK_E_RANGE, MK_E_DEVICE = 0, -1, -2, -3, -4, -5, -6, -7
 MK_DBG_DUMP_N = 1
 MK_DBG_TIMESTAMPS = 2
+MK_DBG_WIDE_GEMV = 4
 MK_DBGK_ROUTE_SEL, MK_DBGK_ROUTE_GATE, MK_DBGK_ROUTER_LOGITS, MK_DBGK_NORM_IN, MK_DBGK_COUNTERS, MK_DBGK_TASK_DONE = 1, 2, 3, 4, 5, 6
 MK_DBGK_TIMESTAMPS = 7
 EXPORTS = ("mk_load_model", "mk_build_tasks", "mk_decode_step", "mk_next_tokens", "mk_status", "mk_debug_set", "mk_debug_read",

@@ -51,7 +51,7 @@ enum {
 };
 
 /* Model shape.  Supported: d_head in {64, 128}; n_q_heads / n_kv_heads in {2, 4, 8};
- * d_model a multiple of 256, at most 4096; d_ffn a multiple of 32, at most 2048;
+ * d_model a multiple of 256, at most 4096; d_ffn a multiple of 128, at most 2048;
  * n_experts <= 256, top_k <= 8 and <= n_experts; vocab a multiple of 64; page_size 16;
  * 1 <= max_batch <= 8. */
 typedef struct mk_model_desc {
@@ -127,8 +127,11 @@ int mk_next_tokens(mk_model* m, int32_t** dev_ptr);
  * call (the fault word is cleared and the handle's counters are reset). */
 int mk_status(mk_model* m, void* stream);
 
-/* Debug switches (bit flags, MK_DBG_*) and read-back of the handle's debug buffers. */
-enum { MK_DBG_DUMP_N = 1, MK_DBG_TIMESTAMPS = 2 };
+/* Debug switches (bit flags, MK_DBG_*) and read-back of the handle's debug buffers.  MK_DBG_WIDE_GEMV runs
+ * batches of 1-2 sequences with the matrix-core arithmetic of batches of 3-8 (hi and lo activation parts in
+ * separate instructions accumulating into one sum), so that a sequence's results then equal, bit for bit,
+ * its results inside a larger batch; without it the two batch classes agree to rounding only. */
+enum { MK_DBG_DUMP_N = 1, MK_DBG_TIMESTAMPS = 2, MK_DBG_WIDE_GEMV = 4 };
 enum {
   MK_DBGK_ROUTE_SEL = 1,     /* int32 [n_layers][batch][top_k]: last step's expert selection (always recorded) */
   MK_DBGK_ROUTE_GATE = 2,    /* fp32  [n_layers][batch][top_k]: its gates (always recorded) */

@@ -131,6 +131,10 @@ def test_grid_size_and_page_order_invariance():
 
 
 def test_batch_equals_single_sequences():
+    """A sequence's logits do not depend on the rest of its batch: the batch of 8 equals, bit for bit, each
+    sequence run alone in the same matrix-core arithmetic (MK_DBG_WIDE_GEMV); a batch of 2 equals its two
+    sequences run alone in the small-batch arithmetic; the two arithmetics agree to rounding."""
+    from decode_megakernel_wg_amd import mk
     from decode_megakernel_wg_amd.session import Session
 
     w = W.make("tiny_ragged", steps=1)
@@ -140,12 +144,31 @@ def test_batch_equals_single_sequences():
     sb.step()
     sb.status()
     batch_logits = sb.logits.cpu().numpy()
+    single = {}
     for b in range(w.B):
         w1 = W.Workload(w.name, w.shape, [w.ctx[b]], 1, tokens=[w.tokens[b]])
-        s1 = Session(w1, model=model, kv=_single_kv(w, b, pt, n_pages))
-        s1.step()
-        s1.status()
-        assert np.array_equal(s1.logits.cpu().numpy()[0], batch_logits[b]), f"sequence {b} differs between batch and single run"
+        for wide in (True, False):
+            s1 = Session(w1, model=model, kv=_single_kv(w, b, pt, n_pages))
+            if wide:
+                s1.h.mk_debug_set(mk.MK_DBG_WIDE_GEMV)
+            s1.step()
+            s1.status()
+            single[b, wide] = s1.logits.cpu().numpy()[0].copy()
+        assert np.array_equal(single[b, True], batch_logits[b]), f"sequence {b} differs between batch and single run"
+        assert rel_l2(single[b, False], single[b, True]) < 1e-3, f"sequence {b}: batch classes differ beyond rounding"
+    # a batch of two (sequences 0 and 1, their own pages) against the small-batch single runs
+    w2 = W.Workload(w.name, w.shape, list(w.ctx[:2]), 1, tokens=list(w.tokens[:2]))
+    kv2 = W.DeviceKV(W.Workload(w.name, w.shape, [], w.steps), pt=pt[:2], n_pages=n_pages)
+    from synth import synth
+
+    for b in range(2):
+        synth.fill_kv_dev(kv2.kv, w.shape.n_layers, 0, n_pages, w.shape.n_kv_heads, w.shape.d_head, 16, kv2.pt[b], b, 0, w.ctx[b],
+                          W.SEED_KV, W.KV_SIGMA)
+    s2 = Session(w2, model=model, kv=kv2)
+    s2.step()
+    s2.status()
+    for b in range(2):
+        assert np.array_equal(s2.logits.cpu().numpy()[b], single[b, False]), f"sequence {b} differs between batch of 2 and single run"
 
 
 def _single_kv(w, b, pt, n_pages):
