@@ -47,10 +47,15 @@ enum Word : int {
   W_SEQ = 31    // task index (debug)
 };
 constexpr int N_WAITS = 4;
-// Claim queues.  The workgroups are split into two groups, each claiming from its own in-order queue:
-// the attention branch (embedding, router, QKV, attention, O-projection) and the expert branch (expert
-// up / down projections).  Each queue is a subsequence of the list's topological order, so the earliest
-// unfinished task of the list is always at the head of its queue with every producer finished.
+// Claim queues.  The workgroups are split into two groups.  The expert branch (expert up / down
+// projections) claims from an in-order queue with two tickets claimed ahead.  The attention branch
+// (embedding, QKV, attention, O-projection) runs phases: the embedding tiles, then per layer the QKV
+// tiles, the attention splits and the O-projection tiles, each phase a pool that its workgroups take
+// tasks from one at a time (an atomic counter, nothing claimed ahead) until it is empty, then the next
+// phase.  A phase's tasks thus go to the workgroups that are free, one each, instead of queueing behind
+// busy workgroups that hold tickets.  Both orders are subsequences of the list's topological order, and
+// a workgroup enters a phase only once every task of the previous one has been taken by a workgroup that
+// runs it at once, so the earliest unfinished task can always run.
 enum Queue : int32_t { Q_ATTN = 0, Q_MOE = 1, Q_ANY = 2 };
 constexpr int DESC_WORDS = 32;
 
@@ -65,8 +70,8 @@ constexpr int LM_MAX_WG = 1024;  // most workgroups a launch may have (stride of
 
 // Counter index layout for a model/batch; computed identically by planner and host launcher.
 struct CounterLayout {
-  int32_t ticket, ticket2, done, xready, qkv_done, router_arrive, slot_ready, attn_arrive, attn_done, up_done, resid_arrive, lm_arrive,
-      lm_pool, total;
+  int32_t ticket, ticket2, done, xready, phase, qkv_done, router_arrive, slot_ready, attn_arrive, attn_done, up_done,
+      resid_arrive, lm_arrive, lm_pool, total;
   int32_t n_layers, n_kv, n_slots, n_row_tiles, batch;
   void build(int L, int Hkv, int B, int slots, int nrt) {
     n_layers = L;
@@ -79,6 +84,7 @@ struct CounterLayout {
     ticket2 = o; o += 32;    // queue Q_MOE
     done = o; o += 32;
     xready = o; o += L + 1;
+    phase = o; o += 1 + 3 * L;  // next untaken task of each attention-branch phase
     qkv_done = o; o += L * Hkv;
     router_arrive = o; o += L;
     slot_ready = o; o += L * slots;

@@ -71,6 +71,8 @@ struct mk_model {
   int uploaded_grid = -1;    // grid the device task array was laid out for
   int32_t n_first = 0;       // tasks of the first claim queue in the device array
   int32_t first_group = 0;   // workgroups claiming from the first queue
+  int32_t ph_on = 0;         // attention-branch phases in use (two or more workgroups)
+  int32_t ph_n[4] = {0, 0, 0, 0};
   int32_t* staging = nullptr;  // pinned host copy of the task list
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
@@ -217,7 +219,9 @@ int mk_build_tasks(mk_model* m, const mk_batch* batch, int32_t* tasks_out, int64
 // Lay the task list out in the pinned staging buffer for the current grid.  With two or more workgroups,
 // the attention-branch queue comes first and the expert-branch queue second, each in list order, and the
 // workgroups are split between them in about the proportion of the queues' estimated HBM bytes; tiles of
-// the LM head go to both queues in that same proportion.  With one workgroup the list stays one queue.
+// the LM head go to both queues in that same proportion.  The attention-branch tasks then run as phases
+// (embedding, and per layer QKV, attention, O-projection), whose sizes are derived here.  With one
+// workgroup the list stays one queue.
 static void lay_out_queues(mk_model* m) {
   const mk::Plan& P = m->plan;
   const int64_t n = P.n_tasks();
@@ -227,6 +231,7 @@ static void lay_out_queues(mk_model* m) {
     std::memcpy(dst, src, P.desc.size() * sizeof(int32_t));
     m->n_first = (int32_t)n;
     m->first_group = m->grid;
+    m->ph_on = 0;
   } else {
     const double tot = P.bytes_attn + P.bytes_moe;
     // the expert branch gets 90% of its byte share: its up-projection tiles stream more bytes per
@@ -251,6 +256,14 @@ static void lay_out_queues(mk_model* m) {
       if (pass == 0) m->n_first = (int32_t)o;
     }
     m->first_group = ga;
+    // phase sizes: embedding tiles, then per layer QKV tiles, attention splits, O-projection tiles (the
+    // first queue holds exactly these, layer by layer, in list order)
+    const int L = m->desc.n_layers, Hkv = m->desc.n_kv_heads;
+    m->ph_n[0] = P.t.n_rt;
+    m->ph_n[1] = Hkv * P.t.n_qkv_per_group;
+    m->ph_n[3] = Hkv * P.t.n_rt;
+    m->ph_n[2] = (int32_t)((m->n_first - m->ph_n[0]) / L) - m->ph_n[1] - m->ph_n[3];
+    m->ph_on = n_any == 0 && m->ph_n[2] > 0 && (int64_t)m->ph_n[0] + (int64_t)L * (m->ph_n[1] + m->ph_n[2] + m->ph_n[3]) == m->n_first;
   }
   m->uploaded_grid = m->grid;
 }
@@ -298,6 +311,9 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   a.c_ticket2 = P.cl.ticket2;
   a.n_first = m->n_first;
   a.first_group = m->first_group;
+  a.ph_on = m->ph_on;
+  for (int i = 0; i < 4; ++i) a.ph_n[i] = m->ph_n[i];
+  a.c_phase = P.cl.phase;
   a.c_done = P.cl.done;
   a.layers = m->layers;
   a.embed = m->embed;

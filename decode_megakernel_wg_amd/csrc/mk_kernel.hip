@@ -83,6 +83,7 @@ struct Lds {
   float slot_g[8];
   int slotw[SLOT_WORDS];
   int32_t desc[2][DESC_WORDS];  // current and next task descriptor
+  int pool_tile;                // attention-branch phases: the index a take returned
   int lmq[4];                   // LM head: ring of claimed vocabulary chunks
   uint32_t wval;                // value a wait observed (expert slot words)
   int next1, flag;
@@ -1717,31 +1718,63 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
   const int base = second ? a.n_first : 0;
   const int count = second ? a.n_tasks - a.n_first : a.n_first;
   const int ticket = second ? a.c_ticket2 : a.c_ticket;
-  // first task: claim and fetch synchronously; then keep two claims and one descriptor ahead
+  // attention-branch phases (first group): take tasks from phase ph's pool until it is empty, then ph + 1
+  const bool phases = !second && a.ph_on;
+  // queue: first task claimed and fetched synchronously; then two claims and one descriptor kept ahead
   if (tid == 0) {
     S.xb_layer = 0;
-    S.next1 = (int)__hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!phases) S.next1 = (int)__hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  int i = S.next1;
+  int i = phases ? count : S.next1;
   if (i < count) fetch_desc(a, base + i, S.desc[0]);
-  if (tid == 0) S.next1 = (int)__hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0 && !phases) S.next1 = (int)__hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   drain_stores();
   __syncthreads();
+  const int nph = 1 + 3 * a.L;
+  int ph = 0;
   int cur = 0;
-  while (i < count) {
-    const int i1 = S.next1;
-    __syncthreads();
-    if (i1 < count) fetch_desc(a, base + i1, S.desc[cur ^ 1]);
+  for (;;) {
+    int i1 = 0;
     uint32_t i2 = 0;
-    if (tid == 0) i2 = __hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (phases) {
+      int pos = -1;
+      while (ph < nph) {
+        const int l = (ph - 1) / 3, k = ph - 1 - 3 * l;
+        const int start = ph == 0 ? 0 : a.ph_n[0] + l * (a.ph_n[1] + a.ph_n[2] + a.ph_n[3]) + (k >= 1 ? a.ph_n[1] : 0) + (k >= 2 ? a.ph_n[2] : 0);
+        const int cnt = ph == 0 ? a.ph_n[0] : a.ph_n[1 + k];
+        if (tid == 0) S.pool_tile = (int)__hip_atomic_fetch_add(&a.ctr[a.c_phase + ph], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int tk = __builtin_amdgcn_readfirstlane(S.pool_tile);
+        __syncthreads();  // read by every wave before the next take overwrites it
+        if (tk < cnt) {
+          pos = start + tk;
+          break;
+        }
+        ++ph;  // every task of this phase is taken
+      }
+      if (pos < 0) break;
+      fetch_desc(a, pos, S.desc[cur]);
+      drain_stores();
+      __syncthreads();
+    } else {
+      if (i >= count) break;
+      i1 = S.next1;
+      __syncthreads();
+      if (i1 < count) fetch_desc(a, base + i1, S.desc[cur ^ 1]);
+      if (tid == 0) i2 = __hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     const Desc w{S.desc[cur]};
     run_task<C>(a0, w, w[W_SEQ], S);
     drain_stores();  // the next descriptor has landed in LDS, the claim has returned
-    if (tid == 0) S.next1 = (int)i2;
-    __syncthreads();
-    i = i1;
-    cur ^= 1;
+    if (phases) {
+      __syncthreads();  // every wave is done with the descriptor
+    } else {
+      if (tid == 0) S.next1 = (int)i2;
+      __syncthreads();
+      i = i1;
+      cur ^= 1;
+    }
   }
   lm_phase<C>(*(KA*)a0, S);
   exit_step(a, S);

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 W_OP, W_LAYER, W_A, W_B, W_C, W_D, W_R0, W_R1, W_WAIT0, W_SIG, W_SIGN, W_ARR, W_ARRN, W_SIGR = 0, 1, 2, 3, 4, 5, 6, 7, 8, 16, 17, 18, 19, 20
 W_Q, W_ARR2, W_ARRN2, W_RSIG, W_RSIGR = 23, 24, 25, 26, 27
 Q_ATTN, Q_MOE, Q_ANY = 0, 1, 2
-OP_ATTN, OP_LMHEAD = 4, 9
+OP_EMBED, OP_ATTN, OP_LMHEAD = 1, 4, 9
 
 
 def declared(header):
@@ -68,32 +68,45 @@ def test_batch_validation():
 
 
 def queues(tasks, n_workers, first_group):
-    """The launcher's claim queues for a grid: attention-branch tasks first, expert-branch tasks second, each in
-    list order; vocabulary tiles (Q_ANY) shared in proportion to the two workgroup groups.  One workgroup: one
-    queue in list order."""
+    """The launcher's task order for a grid: attention-branch tasks first, expert-branch tasks second, each in
+    list order; vocabulary tiles (Q_ANY) shared in proportion to the two workgroup groups.  The attention
+    branch runs as phases: maximal runs of one operation and layer (embedding, then per layer QKV, attention,
+    O-projection), each a pool.  One workgroup: one queue in list order, no phases."""
     if n_workers < 2:
-        return [list(range(len(tasks)))], [n_workers]
+        return [list(range(len(tasks)))], [n_workers], None
     q = tasks[:, W_Q].copy()
     lm = np.nonzero(q == Q_ANY)[0]
     lm_first = int(len(lm) * first_group / n_workers + 0.5)
     q[lm[:lm_first]] = Q_ATTN
     q[lm[lm_first:]] = Q_MOE
-    return [list(np.nonzero(q == Q_ATTN)[0]), list(np.nonzero(q == Q_MOE)[0])], [first_group, n_workers - first_group]
+    attn = list(np.nonzero(q == Q_ATTN)[0])
+    phases = []
+    for t in attn:
+        key = (tasks[t, W_OP], tasks[t, W_LAYER])
+        if not phases or phases[-1][0] != key:
+            phases.append((key, []))
+        phases[-1][1].append(int(t))
+    return [attn, list(np.nonzero(q == Q_MOE)[0])], [first_group, n_workers - first_group], [p for _, p in phases]
 
 
 def simulate(tasks, n_counters, n_workers, rng, first_group=None):
-    """Each workgroup group claims from its own queue in order, every workgroup holding its current task and two
-    pre-claimed next tasks; among held tasks any whose waits are met may finish, in random order.  Returns final
-    counters and completion counts; raises on deadlock."""
+    """Every workgroup runs one task at a time.  The expert-branch group claims from its queue in order
+    (each workgroup holding its current task and two claimed ahead); the attention-branch group takes tasks
+    from the phase pools in order, one at a time, moving to the next phase once a take finds the pool empty.
+    Rounds visit the workgroups in random order; each picks its next task if it has none and runs its task
+    if the waits are met.  A round that runs nothing while tasks remain is a deadlock.  Returns final
+    counters and completion counts."""
     if first_group is None:
         first_group = max(1, n_workers // 2)
-    qs, sizes = queues(tasks, n_workers, first_group)
+    qs, sizes, phases = queues(tasks, n_workers, first_group)
     ctr = np.zeros(n_counters, np.int64)
     done = np.zeros(len(tasks), np.int64)
     nxt = [0] * len(qs)
-    held = []
-    held_per = [0] * len(qs)
-    owner = {}
+    taken = [0] * (len(phases) if phases else 0)
+    group = [0 if w < sizes[0] else 1 for w in range(n_workers)]
+    held = [[] for _ in range(n_workers)]
+    cur = [None] * n_workers
+    ph = [0] * n_workers
     completed = 0
 
     def ready(t):
@@ -104,28 +117,36 @@ def simulate(tasks, n_counters, n_workers, rng, first_group=None):
                 return False
         return True
 
+    def pick(wk):
+        g = group[wk]
+        if g == 0 and phases is not None:
+            while ph[wk] < len(phases):
+                p = ph[wk]
+                if taken[p] < len(phases[p]):
+                    taken[p] += 1
+                    return phases[p][taken[p] - 1]
+                ph[wk] += 1
+            return None
+        h = held[wk]
+        while len(h) < 3 and nxt[g] < len(qs[g]):
+            h.append(qs[g][nxt[g]])
+            nxt[g] += 1
+        return h.pop(0) if h else None
+
     while completed < len(tasks):
-        for g, q in enumerate(qs):
-            while held_per[g] < 3 * sizes[g] and nxt[g] < len(q):
-                held.append(q[nxt[g]])
-                owner[q[nxt[g]]] = g
-                held_per[g] += 1
-                nxt[g] += 1
-        # deadlock freedom: the oldest claimed task (list order) must always be runnable
-        oldest = min(held)
-        assert ready(oldest), f"deadlock: oldest claimed task {oldest} waits on an unfinished producer"
-        # finish a random ready held task (a few random probes, else the oldest)
-        t = oldest
-        for c in rng.integers(len(held), size=4):
-            if ready(held[c]):
-                t = held[c]
-                break
-        held.remove(t)
-        held_per[owner.pop(t)] -= 1
-        w = tasks[t]
-        done[t] += 1
-        completed += 1
-        complete(w, ctr)
+        progressed = False
+        for wk in rng.permutation(n_workers):
+            if cur[wk] is None:
+                cur[wk] = pick(wk)
+            t = cur[wk]
+            if t is None or not ready(t):
+                continue
+            cur[wk] = None
+            done[t] += 1
+            completed += 1
+            complete(tasks[t], ctr)
+            progressed = True
+        assert progressed, f"deadlock: no workgroup can run its current task ({completed} of {len(tasks)} done)"
     return ctr, done
 
 
