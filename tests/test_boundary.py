@@ -214,4 +214,5 @@ def test_task_counts_full_model():
     tasks, _ = mk.mk_plan_tasks(d, [8192])
     ops = np.bincount(tasks[:, W_OP], minlength=10)
     assert ops[OP_LMHEAD] == 0   # the LM head is the kernel's closing phase, not tasks
-    assert ops[OP_ATTN] == 48 * 4 * -(-(8192 + 1) // 256)
+    # about 128 splits per layer: 8193 positions x 4 KV groups / 128 = 257 -> 384 positions (3 chunks of 128)
+    assert ops[OP_ATTN] == 48 * 4 * -(-(8192 + 1) // 384)
