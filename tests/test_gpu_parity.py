@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle_runner import OracleRun, kth_gap, rel_l2, top2_gap
+from oracle_runner import OracleRun, rel_l2, tie_ok, top2_gap
 from synth import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -62,7 +62,7 @@ def run_parity(w, steps, check_router_inputs=True, grid=None):
                     sel, _, lg = O.router(n_gpu[l, b], wr, s.top_k, w.router_bias)
                     assert np.allclose(lg, rl_gpu[l, b], rtol=1e-5, atol=1e-6), f"router logits differ at step {step} layer {l}"
                     if not np.array_equal(sel, gsel[l, b]):
-                        assert kth_gap(lg, s.top_k) < ROUTE_EPS, f"teacher-forced routing differs at step {step} layer {l} seq {b}"
+                        assert tie_ok(lg, gsel[l, b], s.top_k, ROUTE_EPS), f"teacher-forced routing differs at step {step} layer {l} seq {b}"
                         near_ties += 1
         pos = sess.seq_rows_host[step]
         ol, onx, osel, _ = orc.step(tokens, pos, gpu_sel=gsel)
