@@ -1352,9 +1352,19 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
     const int ph = S.pages[(pos >> 4) - np0];
     return ph < 0 ? -1 : (((int64_t)ph * 2) * Hkv + g) * 16 * DH + (pos & 15) * DH;
   };
-  // K in the MFMA A-operand layout (16 positions per wave, 8 dims per lane and k-step); V in 4-dim slices
+  // K of the wave's 16 positions (64 bytes per lane); V in 4-dim slices.  d_head 128: in row quads (load u
+  // holds positions 4u..4u+3 of the wave, lane l 16-byte chunk 4(l/16) + l%4 of position (l%16)/4, so every
+  // four lanes read 64 contiguous bytes; see the GEMV core); d_head 64: the plain A-operand layout (16
+  // positions x 32 dims per load).
   auto load_chunk = [&](int c0, u4 (&kk)[NKK], u2 (&vv)[NP]) {
-    {
+    if constexpr (DH == 128) {
+#pragma unroll
+      for (int u = 0; u < NKK; ++u) {
+        const int pos = c0 + 16 * wave + 4 * u + ((lane & 15) >> 2);
+        const int64_t base = pos < jc1 ? kv_base(pos) : -1;
+        kk[u] = base >= 0 ? __builtin_nontemporal_load(as_global(kvl + base + 32 * (lane >> 4) + 8 * (lane & 3))) : u4{0, 0, 0, 0};
+      }
+    } else {
       const int pos = c0 + 16 * wave + (lane & 15);
       int64_t base = pos < jc1 ? kv_base(pos) : -1;
 #pragma unroll
@@ -1429,11 +1439,23 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
     }
   }
   mark(a, t, 0);
+  // query operands.  d_head 128 (row quads): B column 4s + h holds head 4g + s of head group g at K-part h
+  // (chunk 4(l/16) + h of the head's vector); d_head 64: head j in column j, 32 dims per k-step.
+  constexpr int NHG = (GRP + 3) / 4;
   u4 qh[NKK], ql[NKK];
+  if constexpr (DH == 128) {
 #pragma unroll
-  for (int q = 0; q < NKK; ++q) {
-    qh[q] = *reinterpret_cast<const u4*>(qb + (lane & 15) * DH + 8 * (lane >> 4) + 32 * q);
-    ql[q] = *reinterpret_cast<const u4*>(qb + 16 * DH + (lane & 15) * DH + 8 * (lane >> 4) + 32 * q);
+    for (int hg = 0; hg < NHG; ++hg) {
+      const int hd = 4 * hg + ((lane & 15) >> 2);
+      qh[hg] = *reinterpret_cast<const u4*>(qb + hd * DH + 32 * (lane >> 4) + 8 * (lane & 3));
+      ql[hg] = *reinterpret_cast<const u4*>(qb + 16 * DH + hd * DH + 32 * (lane >> 4) + 8 * (lane & 3));
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < NKK; ++q) {
+      qh[q] = *reinterpret_cast<const u4*>(qb + (lane & 15) * DH + 8 * (lane >> 4) + 32 * q);
+      ql[q] = *reinterpret_cast<const u4*>(qb + 16 * DH + (lane & 15) * DH + 8 * (lane >> 4) + 32 * q);
+    }
   }
   float o[GRP][DPT];
 #pragma unroll
@@ -1442,20 +1464,41 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
     for (int i = 0; i < DPT; ++i) o[h][i] = 0.f;
 
   for (int c0 = j0; c0 < jc1; c0 += CH) {
-    // scores on MFMA: D[position][head] = K (16 positions x 32 dims) times q^T (32 dims x heads), hi + lo
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (DH == 128) {
+      // scores on MFMA in row quads: for position quad u and head group g, D[4r + h][4s + h] is position
+      // 4u + r times head 4g + s over K-part h (hi, then lo); the parts are added across each lane quad
 #pragma unroll
-    for (int q = 0; q < NKK; ++q) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, kc[q]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, qh[q]), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, ql[q]), acc, 0, 0, 0);
-    }
-    if ((lane & 15) < GRP) {
-      const int h = lane & 15;
+      for (int u = 0; u < NKK; ++u) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pl = 16 * wave + 4 * (lane >> 4) + r;
-        S.sc[h * CH + pl] = c0 + pl < jc1 ? acc[r] : -INFINITY;
+        for (int hg = 0; hg < NHG; ++hg) {
+          f4 acc = mfma(kc[u], qh[hg], f4{0.f, 0.f, 0.f, 0.f});
+          acc = mfma(kc[u], ql[hg], acc);
+          float v = pick4(acc, lane & 3);
+          v += dpp<0xB1>(v);
+          v += dpp<0x4E>(v);
+          const int hd = 4 * hg + ((lane >> 2) & 3);
+          if ((lane & 3) == 0 && hd < GRP) {
+            const int pl = 16 * wave + 4 * u + (lane >> 4);
+            S.sc[hd * CH + pl] = c0 + pl < jc1 ? v : -INFINITY;
+          }
+        }
+      }
+    } else {
+      // scores on MFMA: D[position][head] = K (16 positions x 32 dims) times q^T (32 dims x heads), hi + lo
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < NKK; ++q) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, kc[q]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, qh[q]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, ql[q]), acc, 0, 0, 0);
+      }
+      if ((lane & 15) < GRP) {
+        const int h = lane & 15;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pl = 16 * wave + 4 * (lane >> 4) + r;
+          S.sc[h * CH + pl] = c0 + pl < jc1 ? acc[r] : -INFINITY;
+        }
       }
     }
     __syncthreads();
