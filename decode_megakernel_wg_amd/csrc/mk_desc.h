@@ -39,7 +39,6 @@ enum Word : int {
   W_SIGR = 20,  // counters signalled: [W_SIG, W_SIG + W_SIGR) (router: one per expert slot, the value
                 // written there is the slot's routing, at least 1)
   W_RT = 22,    // residual row tile of OPROJ / DOWN / EMBED tasks
-  W_Q = 23,     // claim queue: Q_ATTN, Q_MOE, or Q_ANY (placed by the launcher)
   W_ARR2 = 24,  // row-tile tasks: arrival counter of the next layer's router partials (-1 = none: last layer)
   W_ARRN2 = 25, // arrivals expected there (row tiles)
   W_RSIG = 26,  // first expert-slot counter of the next layer, signalled by the tile that routes it
@@ -47,16 +46,15 @@ enum Word : int {
   W_SEQ = 31    // task index (debug)
 };
 constexpr int N_WAITS = 4;
-// Claim queues.  The workgroups are split into two groups.  The expert branch (expert up / down
-// projections) claims from an in-order queue with two tickets claimed ahead.  The attention branch
-// (embedding, QKV, attention, O-projection) runs phases: the embedding tiles, then per layer the QKV
-// tiles, the attention splits and the O-projection tiles, each phase a pool that its workgroups take
-// tasks from one at a time (an atomic counter, nothing claimed ahead) until it is empty, then the next
-// phase.  A phase's tasks thus go to the workgroups that are free, one each, instead of queueing behind
-// busy workgroups that hold tickets.  Both orders are subsequences of the list's topological order, and
-// a workgroup enters a phase only once every task of the previous one has been taken by a workgroup that
-// runs it at once, so the earliest unfinished task can always run.
-enum Queue : int32_t { Q_ATTN = 0, Q_MOE = 1, Q_ANY = 2 };
+// Scheduling.  With two or more workgroups the list runs as phases: the embedding tiles, then per layer
+// each maximal run of one operation (QKV tiles, attention splits, expert up-projection tiles,
+// O-projection tiles, expert down-projection tiles).  Each phase is a pool that every workgroup takes
+// tasks from one at a time (an atomic counter; nothing is claimed ahead), moving on to the next phase
+// once a take finds the pool empty.  A phase's tasks thus go to whichever workgroups are free, one each,
+// instead of queueing behind busy workgroups that hold tickets, and the attention and expert branches
+// of a layer share all compute units.  Phases follow the list's topological order and a workgroup enters
+// a phase only once every task of the previous one has been taken by a workgroup that runs it at once,
+// so the earliest unfinished task can always run.  One workgroup claims the list in order.
 constexpr int DESC_WORDS = 32;
 
 // Tile sizes chosen by the planner (rows per task); the kernel reads r0/r1 from the descriptor.
@@ -70,7 +68,7 @@ constexpr int LM_MAX_WG = 1024;  // most workgroups a launch may have (stride of
 
 // Counter index layout for a model/batch; computed identically by planner and host launcher.
 struct CounterLayout {
-  int32_t ticket, ticket2, done, xready, phase, qkv_done, router_arrive, slot_ready, attn_arrive, attn_done, up_done,
+  int32_t ticket, done, xready, phase, qkv_done, router_arrive, slot_ready, attn_arrive, attn_done, up_done,
       resid_arrive, lm_arrive, lm_pool, total;
   int32_t n_layers, n_kv, n_slots, n_row_tiles, batch;
   void build(int L, int Hkv, int B, int slots, int nrt) {
@@ -80,11 +78,10 @@ struct CounterLayout {
     n_row_tiles = nrt;
     batch = B;
     int32_t o = 0;
-    ticket = o; o += 32;     // own cache line (queue Q_ATTN)
-    ticket2 = o; o += 32;    // queue Q_MOE
+    ticket = o; o += 32;     // own cache line (claim order with one workgroup)
     done = o; o += 32;
     xready = o; o += L + 1;
-    phase = o; o += 1 + 3 * L;  // next untaken task of each attention-branch phase
+    phase = o; o += 1 + 5 * L;  // next untaken task of each phase
     qkv_done = o; o += L * Hkv;
     router_arrive = o; o += L;
     slot_ready = o; o += L * slots;

@@ -69,10 +69,9 @@ struct mk_model {
   mk::Plan plan;
   bool have_plan = false, dirty = false;
   int uploaded_grid = -1;    // grid the device task array was laid out for
-  int32_t n_first = 0;       // tasks of the first claim queue in the device array
-  int32_t first_group = 0;   // workgroups claiming from the first queue
-  int32_t ph_on = 0;         // attention-branch phases in use (two or more workgroups)
-  int32_t ph_n[4] = {0, 0, 0, 0};
+  int32_t ph_on = 0;         // phases in use (two or more workgroups and a regular list)
+  int32_t ph_npl = 0;        // phases per layer
+  int32_t ph_n[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int32_t* staging = nullptr;  // pinned host copy of the task list
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
@@ -216,55 +215,43 @@ int mk_build_tasks(mk_model* m, const mk_batch* batch, int32_t* tasks_out, int64
   return MK_OK;
 }
 
-// Lay the task list out in the pinned staging buffer for the current grid.  With two or more workgroups,
-// the attention-branch queue comes first and the expert-branch queue second, each in list order, and the
-// workgroups are split between them in about the proportion of the queues' estimated HBM bytes; tiles of
-// the LM head go to both queues in that same proportion.  The attention-branch tasks then run as phases
-// (embedding, and per layer QKV, attention, O-projection), whose sizes are derived here.  With one
-// workgroup the list stays one queue.
+// Phases of the list: maximal runs of one operation and layer.  They are used when the list is the
+// embedding tiles followed, layer by layer, by the same sequence of runs with the same sizes (at most 7 per
+// layer); otherwise the workgroups claim the list in order.
+static void derive_phases(mk_model* m, const int32_t* q, int64_t n) {
+  m->ph_on = 0;
+  const int L = m->desc.n_layers;
+  std::vector<int32_t> op, layer, len;
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t* w = q + i * mk::DESC_WORDS;
+    if (op.empty() || op.back() != w[mk::W_OP] || layer.back() != w[mk::W_LAYER]) {
+      op.push_back(w[mk::W_OP]);
+      layer.push_back(w[mk::W_LAYER]);
+      len.push_back(0);
+    }
+    ++len.back();
+  }
+  if (op.empty() || op[0] != mk::OP_EMBED || (op.size() - 1) % L) return;
+  const int npl = (int)((op.size() - 1) / L);
+  if (npl < 1 || npl > 7) return;
+  for (int l = 0; l < L; ++l)
+    for (int k = 0; k < npl; ++k) {
+      const size_t r = 1 + (size_t)l * npl + k;
+      if (layer[r] != l || op[r] != op[1 + k] || len[r] != len[1 + k]) return;
+    }
+  m->ph_npl = npl;
+  m->ph_n[0] = len[0];
+  for (int k = 0; k < npl; ++k) m->ph_n[1 + k] = len[1 + k];
+  m->ph_on = 1;
+}
+
+// Copy the task list to the pinned staging buffer (list order) and derive its phases for grids of two or
+// more workgroups.
 static void lay_out_queues(mk_model* m) {
   const mk::Plan& P = m->plan;
-  const int64_t n = P.n_tasks();
-  const int32_t* src = P.desc.data();
-  int32_t* dst = m->staging;
-  if (m->grid < 2) {
-    std::memcpy(dst, src, P.desc.size() * sizeof(int32_t));
-    m->n_first = (int32_t)n;
-    m->first_group = m->grid;
-    m->ph_on = 0;
-  } else {
-    const double tot = P.bytes_attn + P.bytes_moe;
-    // the expert branch gets 90% of its byte share: its up-projection tiles stream more bytes per
-    // workgroup-microsecond than attention splits and staged GEMV tiles (measured on MI355X)
-    const double fa = 1.0 - 0.9 * (tot > 0 ? P.bytes_moe / tot : 0.5);
-    int ga = (int)(fa * m->grid + 0.5);
-    ga = std::max(1, std::min(m->grid - 1, ga));
-    int64_t n_any = 0;
-    for (int64_t i = 0; i < n; ++i) n_any += src[i * mk::DESC_WORDS + mk::W_Q] == mk::Q_ANY;
-    const int64_t lm_first = (int64_t)((double)n_any * ga / m->grid + 0.5);
-    int64_t o = 0;
-    for (int pass = 0; pass < 2; ++pass) {
-      int64_t lm_seen = 0;
-      for (int64_t i = 0; i < n; ++i) {
-        const int32_t* w = src + i * mk::DESC_WORDS;
-        int q = w[mk::W_Q];
-        if (q == mk::Q_ANY) q = (lm_seen++ < lm_first) ? mk::Q_ATTN : mk::Q_MOE;
-        if (q != pass) continue;
-        std::memcpy(dst + o * mk::DESC_WORDS, w, mk::DESC_WORDS * sizeof(int32_t));
-        ++o;
-      }
-      if (pass == 0) m->n_first = (int32_t)o;
-    }
-    m->first_group = ga;
-    // phase sizes: embedding tiles, then per layer QKV tiles, attention splits, O-projection tiles (the
-    // first queue holds exactly these, layer by layer, in list order)
-    const int L = m->desc.n_layers, Hkv = m->desc.n_kv_heads;
-    m->ph_n[0] = P.t.n_rt;
-    m->ph_n[1] = Hkv * P.t.n_qkv_per_group;
-    m->ph_n[3] = Hkv * P.t.n_rt;
-    m->ph_n[2] = (int32_t)((m->n_first - m->ph_n[0]) / L) - m->ph_n[1] - m->ph_n[3];
-    m->ph_on = n_any == 0 && m->ph_n[2] > 0 && (int64_t)m->ph_n[0] + (int64_t)L * (m->ph_n[1] + m->ph_n[2] + m->ph_n[3]) == m->n_first;
-  }
+  std::memcpy(m->staging, P.desc.data(), P.desc.size() * sizeof(int32_t));
+  m->ph_on = 0;
+  if (m->grid >= 2) derive_phases(m, m->staging, P.n_tasks());
   m->uploaded_grid = m->grid;
 }
 
@@ -308,11 +295,9 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   a.n_tasks = (int32_t)P.n_tasks();
   a.n_counters = P.cl.total;
   a.c_ticket = P.cl.ticket;
-  a.c_ticket2 = P.cl.ticket2;
-  a.n_first = m->n_first;
-  a.first_group = m->first_group;
   a.ph_on = m->ph_on;
-  for (int i = 0; i < 4; ++i) a.ph_n[i] = m->ph_n[i];
+  a.ph_npl = m->ph_npl;
+  for (int i = 0; i < 8; ++i) a.ph_n[i] = m->ph_n[i];
   a.c_phase = P.cl.phase;
   a.c_done = P.cl.done;
   a.layers = m->layers;

@@ -27,14 +27,12 @@ struct KArgs {
   int32_t B, n_slots, max_pages, n_rt;
   int64_t n_pages;
   float eps;
-  int32_t n_tasks, n_counters, c_ticket, c_ticket2, c_done;
+  int32_t n_tasks, n_counters, c_ticket, c_done;
   int32_t c_lm_pool, c_lm_arrive, c_xfinal;  // LM head: chunk pool, arrivals, readiness of the final residual stream
-  int32_t n_first;      // tasks [0, n_first) form the first claim queue, [n_first, n_tasks) the second
-  int32_t first_group;  // workgroups [0, first_group) claim from the first queue, the rest from the second
-  // attention-branch phases (first group, when ph_on): the first queue's tasks are the embedding tiles
-  // (ph_n[0]), then per layer ph_n[1] QKV tiles, ph_n[2] attention splits and ph_n[3] O-projection tiles;
-  // counter c_phase + p is phase p's pool (p = 0 embedding, 1 + 3l + {0, 1, 2})
-  int32_t ph_on, ph_n[4], c_phase;
+  // phases (when ph_on): the list is the embedding tiles (ph_n[0]), then per layer ph_npl runs of one
+  // operation, of ph_n[1] .. ph_n[ph_npl] tasks; counter c_phase + p is phase p's pool (p = 0 embedding,
+  // 1 + ph_npl * l + k).  Otherwise every workgroup claims the list in order (ticket counter c_ticket).
+  int32_t ph_on, ph_npl, ph_n[8], c_phase;
   // model (device)
   const LayerW* layers;
   const uint16_t* embed;

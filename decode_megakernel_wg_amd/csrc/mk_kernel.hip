@@ -3,16 +3,17 @@
 // Design (pages: agenticcommons.xyz "Cohere North Mini Code megakernel serving engine", sections
 // Megakernel 的運作方式 and 三個實際的加速來源; aimodeling.com "Cohere megakernel engine: one CUDA file,
 // 1.58x vLLM on H100", section "One persistent kernel for the whole decode step"):
-//  * one 512-thread workgroup per compute unit stays resident for the whole step and claims tasks
-//    (one operation on one tile) from a task list in global memory, in list order, through an atomic
-//    ticket; two tickets are claimed ahead and the next task's descriptor is copied into LDS while the
-//    current task runs, so a task starts without a round trip to memory;
+//  * one 512-thread workgroup per compute unit stays resident for the whole step and takes tasks (one
+//    operation on one tile) from a task list in global memory, in list order: the list runs as phases
+//    (runs of one operation within a layer), each a pool that free workgroups take tasks from one at a
+//    time through an atomic counter, so a phase spreads over whichever compute units are free;
 //  * dependencies are global counters: a finished task increments its counter, a task that needs an
 //    input spins on the producer's counter (no grid barrier, no kernel boundary);
 //  * weight tiles (immutable) and old KV pages are loaded into registers BEFORE the task waits for its
 //    activations, so HBM streams while dependencies resolve (weight prefetch, item 3);
-//  * tile-granular claiming removes wave quantization and interleaves the attention and MoE branches of
-//    the parallel layer (item 1); per-KV-group and per-expert counters remove false dependencies (item 2).
+//  * tile-granular tasks remove wave quantization, and the attention and MoE branches of the parallel
+//    layer share every compute unit (item 1); per-KV-group and per-expert counters remove false
+//    dependencies (item 2).
 // MI355X specifics: wave64; cross-XCD visibility of task outputs uses write-through (sc1) stores plus a
 // vmcnt drain before the relaxed counter increment, and an agent-scope acquire (L1/L2 invalidate) after
 // the wait; an agent-scope release (L2 writeback) per task costs ~17 us under load on this part and is
@@ -1756,14 +1757,11 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
   __shared__ Lds S;
   const int tid = tidx();
   KA& a = *a0;
-  // this workgroup's claim queue: positions [base, base + count) of the task array, own ticket counter
-  const bool second = (int)blockIdx.x >= a.first_group;
-  const int base = second ? a.n_first : 0;
-  const int count = second ? a.n_tasks - a.n_first : a.n_first;
-  const int ticket = second ? a.c_ticket2 : a.c_ticket;
-  // attention-branch phases (first group): take tasks from phase ph's pool until it is empty, then ph + 1
-  const bool phases = !second && a.ph_on;
-  // queue: first task claimed and fetched synchronously; then two claims and one descriptor kept ahead
+  const int base = 0, count = a.n_tasks, ticket = a.c_ticket;
+  // phases: take tasks from phase ph's pool until it is empty, then ph + 1
+  const bool phases = a.ph_on;
+  // claim order (no phases): first task claimed and fetched synchronously; then two claims and one
+  // descriptor kept ahead
   if (tid == 0) {
     S.xb_layer = 0;
     if (!phases) S.next1 = (int)__hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1774,7 +1772,9 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
   if (tid == 0 && !phases) S.next1 = (int)__hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   drain_stores();
   __syncthreads();
-  const int nph = 1 + 3 * a.L;
+  const int npl = a.ph_npl, nph = 1 + npl * a.L;
+  int per_layer = 0;
+  for (int k = 0; k < npl; ++k) per_layer += a.ph_n[1 + k];
   int ph = 0;
   int cur = 0;
   for (;;) {
@@ -1783,8 +1783,9 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
     if (phases) {
       int pos = -1;
       while (ph < nph) {
-        const int l = (ph - 1) / 3, k = ph - 1 - 3 * l;
-        const int start = ph == 0 ? 0 : a.ph_n[0] + l * (a.ph_n[1] + a.ph_n[2] + a.ph_n[3]) + (k >= 1 ? a.ph_n[1] : 0) + (k >= 2 ? a.ph_n[2] : 0);
+        const int l = ph == 0 ? 0 : (ph - 1) / npl, k = ph == 0 ? 0 : ph - 1 - npl * l;
+        int start = ph == 0 ? 0 : a.ph_n[0] + l * per_layer;
+        for (int j = 0; j < k; ++j) start += a.ph_n[1 + j];
         const int cnt = ph == 0 ? a.ph_n[0] : a.ph_n[1 + k];
         if (tid == 0) S.pool_tile = (int)__hip_atomic_fetch_add(&a.ctr[a.c_phase + ph], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();

@@ -225,7 +225,6 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
     for (int s = 0; s < P->n_slots; ++s)
       for (int i = 0; i < t.n_up; ++i) {
         int32_t* w = em.add(OP_UP, l);
-        w[W_Q] = Q_MOE;
         w[W_A] = s;
         w[W_R0] = i * t.up_rows;
         w[W_R1] = (i + 1) * t.up_rows;
@@ -245,7 +244,6 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
     for (int s = 0; s < P->n_slots; ++s)
       for (int r = 0; r < t.n_rt; ++r) {
         int32_t* w = em.add(OP_DOWN, l);
-        w[W_Q] = Q_MOE;
         w[W_A] = s;
         w[W_R0] = r * t.rt;
         w[W_R1] = (r + 1) * t.rt;
@@ -255,14 +253,6 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
       }
   }
   (void)grp;
-  // HBM bytes of each queue, to size the two workgroup groups: attention-branch weights, router and KV
-  // read, versus the weights of the distinct experts a step can select
-  const double dh = d->d_head, dm = d->d_model;
-  const double attn_w = 2.0 * dm * (2.0 * d->n_q_heads * dh + 2.0 * Hkv * dh) + 2.0 * E * dm + 2.0 * dm;
-  double kv = 0;
-  for (int b = 0; b < B; ++b) kv += ((double)batch->seq_lens[b] + 1) * 2.0 * Hkv * dh * 2.0;
-  P->bytes_attn = L * (attn_w + kv);
-  P->bytes_moe = (double)L * P->n_slots * 3.0 * d->d_ffn * dm * 2.0;
   return MK_OK;
 }
 

@@ -26,7 +26,6 @@ struct Plan {
   CounterLayout cl{};
   std::vector<int32_t> splits;  // attention splits per sequence
   std::vector<int32_t> desc;    // n_tasks * DESC_WORDS
-  double bytes_attn = 0, bytes_moe = 0;  // estimated HBM bytes of the two claim queues (LM head excluded)
   int64_t n_tasks() const { return (int64_t)desc.size() / DESC_WORDS; }
 };
 

@@ -14,8 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # descriptor words (mirrors the library's layout)
 W_OP, W_LAYER, W_A, W_B, W_C, W_D, W_R0, W_R1, W_WAIT0, W_SIG, W_SIGN, W_ARR, W_ARRN, W_SIGR = 0, 1, 2, 3, 4, 5, 6, 7, 8, 16, 17, 18, 19, 20
-W_Q, W_ARR2, W_ARRN2, W_RSIG, W_RSIGR = 23, 24, 25, 26, 27
-Q_ATTN, Q_MOE, Q_ANY = 0, 1, 2
+W_ARR2, W_ARRN2, W_RSIG, W_RSIGR = 24, 25, 26, 27
 OP_EMBED, OP_ATTN, OP_LMHEAD = 1, 4, 9
 
 
@@ -67,44 +66,27 @@ def test_batch_validation():
         mk.mk_plan_tasks(d, [-1])
 
 
-def queues(tasks, n_workers, first_group):
-    """The launcher's task order for a grid: attention-branch tasks first, expert-branch tasks second, each in
-    list order; vocabulary tiles (Q_ANY) shared in proportion to the two workgroup groups.  The attention
-    branch runs as phases: maximal runs of one operation and layer (embedding, then per layer QKV, attention,
-    O-projection), each a pool.  One workgroup: one queue in list order, no phases."""
-    if n_workers < 2:
-        return [list(range(len(tasks)))], [n_workers], None
-    q = tasks[:, W_Q].copy()
-    lm = np.nonzero(q == Q_ANY)[0]
-    lm_first = int(len(lm) * first_group / n_workers + 0.5)
-    q[lm[:lm_first]] = Q_ATTN
-    q[lm[lm_first:]] = Q_MOE
-    attn = list(np.nonzero(q == Q_ATTN)[0])
+def phases_of(tasks):
+    """The launcher's phases: maximal runs of one operation and layer, in list order."""
     phases = []
-    for t in attn:
+    for t in range(len(tasks)):
         key = (tasks[t, W_OP], tasks[t, W_LAYER])
         if not phases or phases[-1][0] != key:
             phases.append((key, []))
-        phases[-1][1].append(int(t))
-    return [attn, list(np.nonzero(q == Q_MOE)[0])], [first_group, n_workers - first_group], [p for _, p in phases]
+        phases[-1][1].append(t)
+    return [p for _, p in phases]
 
 
-def simulate(tasks, n_counters, n_workers, rng, first_group=None):
-    """Every workgroup runs one task at a time.  The expert-branch group claims from its queue in order
-    (each workgroup holding its current task and two claimed ahead); the attention-branch group takes tasks
-    from the phase pools in order, one at a time, moving to the next phase once a take finds the pool empty.
-    Rounds visit the workgroups in random order; each picks its next task if it has none and runs its task
-    if the waits are met.  A round that runs nothing while tasks remain is a deadlock.  Returns final
-    counters and completion counts."""
-    if first_group is None:
-        first_group = max(1, n_workers // 2)
-    qs, sizes, phases = queues(tasks, n_workers, first_group)
+def simulate(tasks, n_counters, n_workers, rng):
+    """Every workgroup runs one task at a time.  One workgroup claims the list in order; two or more take
+    tasks from the phase pools in order, one at a time, moving to the next phase once a take finds the pool
+    empty.  Rounds visit the workgroups in random order; each picks its next task if it has none and runs
+    its task if the waits are met.  A round that runs nothing while tasks remain is a deadlock.  Returns
+    final counters and completion counts."""
+    phases = phases_of(tasks) if n_workers >= 2 else [list(range(len(tasks)))]
     ctr = np.zeros(n_counters, np.int64)
     done = np.zeros(len(tasks), np.int64)
-    nxt = [0] * len(qs)
-    taken = [0] * (len(phases) if phases else 0)
-    group = [0 if w < sizes[0] else 1 for w in range(n_workers)]
-    held = [[] for _ in range(n_workers)]
+    taken = [0] * len(phases)
     cur = [None] * n_workers
     ph = [0] * n_workers
     completed = 0
@@ -118,20 +100,13 @@ def simulate(tasks, n_counters, n_workers, rng, first_group=None):
         return True
 
     def pick(wk):
-        g = group[wk]
-        if g == 0 and phases is not None:
-            while ph[wk] < len(phases):
-                p = ph[wk]
-                if taken[p] < len(phases[p]):
-                    taken[p] += 1
-                    return phases[p][taken[p] - 1]
-                ph[wk] += 1
-            return None
-        h = held[wk]
-        while len(h) < 3 and nxt[g] < len(qs[g]):
-            h.append(qs[g][nxt[g]])
-            nxt[g] += 1
-        return h.pop(0) if h else None
+        while ph[wk] < len(phases):
+            p = ph[wk]
+            if taken[p] < len(phases[p]):
+                taken[p] += 1
+                return phases[p][taken[p] - 1]
+            ph[wk] += 1
+        return None
 
     while completed < len(tasks):
         progressed = False
@@ -185,12 +160,10 @@ def test_task_list_is_a_deadlock_free_topological_order(name, B_lens):
                 assert sim[c] >= tgt, f"task {t} waits on counter {c} beyond earlier signals"
         complete(w, sim)
     rng = np.random.default_rng(0)
-    for workers, first in ((1, 1), (3, 1), (3, 2), (256, 108), (256, 1), (256, 255)):
-        if name == "full" and workers == 256 and first != 108 and len(B_lens) > 1:
-            continue
+    for workers in (1, 2, 3, 256):
         if name == "full" and workers != 256 and len(B_lens) > 1:
             continue
-        ctr, done = simulate(tasks, n_ctr, workers, rng, first)
+        ctr, done = simulate(tasks, n_ctr, workers, rng)
         assert np.all(done == 1)
         for w in tasks:
             for i in range(4):
