@@ -89,6 +89,7 @@ struct Lds {
   uint32_t wval;                // value a wait observed (expert slot words)
   int next1, flag;
   int xb_layer;  // l + 1 while xb holds layer l's normalised input of every token (split); 0 otherwise
+  int route_layer;  // l + 1 while sel / used hold layer l's routing; 0 otherwise
 };
 
 // A task descriptor staged in LDS; every word is read as a wave-uniform (scalar) value.
@@ -387,7 +388,8 @@ struct Rows2 {
 // tokens that chose it, their selection rank and gate).  Each slot's readiness counter (ctr[slot0 + s])
 // then receives the slot's expert and token mask (see slot_routing), so expert tasks learn their expert
 // from the wait itself.
-__device__ __forceinline__ void route_select(KA& a, int l, int32_t slot0, Lds& S) {
+// Top-k of every token's key (S.xs [B][E]) into S.sel [b][rank] and the bitmask of selected experts S.used.
+__device__ __forceinline__ void route_rank(KA& a, Lds& S) {
   const int E = a.E, k = a.k, B = a.B, tid = tidx();
   float* key = S.xs;  // [B][E] router logits with NaN replaced by -inf (filled by the caller)
   if (tid < 8) S.used[tid] = 0u;
@@ -423,6 +425,12 @@ __device__ __forceinline__ void route_select(KA& a, int l, int32_t slot0, Lds& S
     }
   }
   __syncthreads();
+}
+__device__ __forceinline__ void route_select(KA& a, int l, int32_t slot0, Lds& S) {
+  const int E = a.E, k = a.k, B = a.B, tid = tidx();
+  float* key = S.xs;
+  route_rank(a, S);
+  if (tid == 0) S.route_layer = l + 1;  // S.sel / S.used hold layer l's routing
   if (tid < B) {
     const int b = tid;
     const float mx = key[b * E + S.sel[b * 8]];
@@ -580,11 +588,13 @@ __device__ __forceinline__ void router_partial(KA& a, const RouterPre& rp, int r
   }
 }
 
-// The workgroup that completes a layer's router partials: logits, then routing.  inv_rms[b] is formed from
-// the row tiles' partial sums of squares exactly as every consumer's RMSNorm forms it.
-__device__ __forceinline__ void route_from_partials(KA& a, int l, int32_t slot0, Lds& S) {
+// Router logits of layer l into S.xs [B][E] (NaN as -inf) from the row tiles' fp64 partials: inv_rms[b] is
+// formed from the row tiles' partial sums of squares exactly as every consumer's RMSNorm forms it, and the
+// partials are added in tile order.  The partial sums of squares and the router partials are requested
+// together (one round trip).  publish: also record the logits (and the debug RMSNorm dump).
+__device__ __forceinline__ void route_logits(KA& a, int l, Lds& S, bool publish) {
   const int B = a.B, E = a.E, nrt = a.n_rt, d = a.d, tid = tidx();
-  if (tid < B * nrt) S.ssqv[tid] = a.ssq[tid];
+  const float ssq = tid < B * nrt ? a.ssq[tid] : 0.f;
   const double* rp = a.rpart;
   double* sums = reinterpret_cast<double*>(S.xs + B * E);  // [B][E], after the keys
   for (int i = tid; i < B * E; i += NT) {
@@ -601,6 +611,7 @@ __device__ __forceinline__ void route_from_partials(KA& a, int l, int32_t slot0,
     for (; r < nrt; ++r) sum += rp[((int64_t)r * B + b) * E + e];
     sums[i] = sum;
   }
+  if (tid < B * nrt) S.ssqv[tid] = ssq;
   __syncthreads();
   if (tid < B) {
     float ss = 0.f;
@@ -612,16 +623,22 @@ __device__ __forceinline__ void route_from_partials(KA& a, int l, int32_t slot0,
   for (int i = tid; i < B * E; i += NT) {
     const int b = i / E, e = i - b * E;
     const float lg = (float)(sums[i] * (double)S.inv[b]) + a.router_bias[e];
-    pub(a.rlogits + ((int64_t)l * B + b) * E + e, lg);
+    if (publish) pub(a.rlogits + ((int64_t)l * B + b) * E + e, lg);
     key[i] = lg == lg ? lg : -INFINITY;
   }
-  if (a.dump_n) {  // debug: the RMSNorm output this layer's consumers stage
+  if (publish && a.dump_n) {  // debug: the RMSNorm output this layer's consumers stage
     const uint16_t* gm = a.layers[l].attn_norm;
     for (int i = tid; i < B * d; i += NT) {
       const int b = i / d, c = i - b * d;
       a.dump_n[(int64_t)l * B * d + i] = a.x[i] * (bf2f(gm[c]) * S.inv[b]);
     }
   }
+  __syncthreads();
+}
+
+// The workgroup that completes a layer's router partials: logits, routing, slot table, slot release.
+__device__ __forceinline__ void route_from_partials(KA& a, int l, int32_t slot0, Lds& S) {
+  route_logits(a, l, S, true);
   route_select(a, l, slot0, S);
 }
 
@@ -1044,6 +1061,37 @@ __device__ __forceinline__ int slot_routing(KA& a, uint32_t v, Lds& S) {
   return S.slot_n > 0 ? e : -1;
 }
 
+// Expert slot s of the routing held in S.sel / S.used (slot s = the s-th selected expert in ascending id)
+// and its tokens, as slot_routing gives them; -1 for an unused slot.
+__device__ __forceinline__ int slot_local(KA& a, int s, Lds& S) {
+  if (tidx() == 0) {
+    int e = -1, cnt = 0;
+    for (int wd = 0; wd < 8 && e < 0; ++wd) {
+      const uint32_t m = S.used[wd];
+      const int pc = __popc(m);
+      if (cnt + pc > s) {
+        uint32_t mm = m;
+        for (int q = 0; q < s - cnt; ++q) mm &= mm - 1;
+        e = wd * 32 + __ffs(mm) - 1;
+      }
+      cnt += pc;
+    }
+    int n = 0;
+    if (e >= 0)
+      for (int b = 0; b < a.B; ++b)
+        for (int j = 0; j < a.k; ++j)
+          if (S.sel[b * 8 + j] == e) {
+            S.slot_b[n++] = b;
+            break;
+          }
+    S.slot_n = n;
+    S.slot_e = e;
+  }
+  __syncthreads();
+  const int e = __builtin_amdgcn_readfirstlane(S.slot_e);
+  return S.slot_n > 0 ? e : -1;
+}
+
 template <class C>
 __device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
   const int l = w[W_LAYER], s = w[W_A], r0 = w[W_R0], r1 = w[W_R1];
@@ -1059,12 +1107,25 @@ __device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
   // are in flight.  Larger batches stage only the slot's tokens, after routing (staging all of them costs
   // more than it saves there, measured).
   const bool early = B <= 2;
-  if (early && __builtin_amdgcn_readfirstlane(S.xb_layer) != l + 1) {  // not staged by this workgroup's last task
-    wait_deps(a, w, 1, 2, t);
-    stage_split(a, gn, B, nullptr, S);
-    if (tidx() == 0) S.xb_layer = l + 1;
+  int e;
+  if (early) {
+    if (__builtin_amdgcn_readfirstlane(S.xb_layer) != l + 1) {  // not staged by this workgroup's last task
+      wait_deps(a, w, 1, 2, t);
+      stage_split(a, gn, B, nullptr, S);
+      if (tidx() == 0) S.xb_layer = l + 1;
+    }
+    // the routing itself, from the router partials, as soon as the last row tile has added its own (no
+    // wait for the routing workgroup to publish it); kept for this workgroup's later tiles of the layer
+    if (__builtin_amdgcn_readfirstlane(S.route_layer) != l + 1) {
+      wait_deps(a, w, 2, 3, t);
+      route_logits(a, l, S, false);
+      route_rank(a, S);
+      if (tidx() == 0) S.route_layer = l + 1;
+    }
+    e = slot_local(a, s, S);
+  } else {
+    e = slot_routing(a, wait_value(a, w, 0, t, S), S);
   }
-  const int e = slot_routing(a, wait_value(a, w, 0, t, S), S);
   if (e >= 0) {
     const int n = S.slot_n;
     // gate rows then up rows of this tile, as one 2*nr-row tile over two bases
@@ -1764,6 +1825,7 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
   // descriptor kept ahead
   if (tid == 0) {
     S.xb_layer = 0;
+    S.route_layer = 0;
     if (!phases) S.next1 = (int)__hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();

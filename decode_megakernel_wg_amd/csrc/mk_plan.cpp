@@ -230,6 +230,7 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
         w[W_R1] = (i + 1) * t.up_rows;
         set_wait(w, 0, cl.slot_ready + l * P->n_slots + s, 1);  // the slot's routing (expert, tokens)
         set_wait(w, 1, cl.xready + l, t.n_rt);                   // the layer's input, staged before routing
+        set_wait(w, 2, cl.router_arrive + l, t.n_rt);            // small batches route from the partials themselves
         set_sig(w, cl.up_done + l * P->n_slots + s);
       }
     for (int g = 0; g < Hkv; ++g)
