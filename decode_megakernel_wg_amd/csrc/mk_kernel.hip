@@ -741,27 +741,6 @@ __device__ __forceinline__ void mg_load(MBuf& buf, const RowPtr& W, const MGeo& 
   }
 }
 
-// A tile that is exactly one pass with every wave busy (16-row blocks times K slices fill the workgroup, and
-// each slice is four K blocks): its loads need no predicate, so the compiler counts them and each MFMA waits
-// only for its own weights: the tile is computed as its data arrives instead of after the last load.  Used
-// where a tile's weights are requested only when the tile can run.
-__device__ __forceinline__ bool mg_one_full_pass(const MGeo& g) {
-  return g.rbn * g.ks == NW && g.nrows == 16 * g.rbn && g.nkb == 4;
-}
-template <class RowPtr>
-__device__ __forceinline__ void mg_load_full(MBuf& buf, const RowPtr& W, const MGeo& g) {
-  const int wave = tidx() >> 6, lane = tidx() & 63;
-  const int rb = wave / g.ks, kp = wave - rb * g.ks;
-  const int c = mg_col(g, kp, 0, lane);
-  gu4* rp[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) rp[q] = as_global(W(rb * 16 + 4 * q + ((lane & 15) >> 2)) + c);
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) buf.v[4 * kb + q] = __builtin_nontemporal_load(rp[q] + 16 * kb);
-}
-
 __device__ __forceinline__ u4 lds16(const uint16_t* p) { return *reinterpret_cast<const u4*>(p); }
 __device__ __forceinline__ f4 mfma(u4 av, u4 bv, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
@@ -822,10 +801,6 @@ __device__ __forceinline__ void mg_compute_kb(const MBuf& buf, MAcc& acc, const 
       }
     }
   }
-}
-template <int NB>
-__device__ __forceinline__ void mg_compute_full(const MBuf& buf, MAcc& acc, const MGeo& g, int pass, int nb, Lds& S) {
-  mg_compute_kb<NB, 4>(buf, acc, g, pass, nb, S);
 }
 // A pass of the tile: all four K blocks, or the K tail's one to three (768 = 6 blocks: a pass of 4, then 2).
 template <int NB>
@@ -929,21 +904,22 @@ __device__ __forceinline__ void split_x(int nb, int K, Lds& S) {
   lds_sync();
 }
 
-// Prefetch, wait, stage, stream.  The first AHEAD passes of the tile (16 KB per wave each) are requested
+// Prefetch, wait, stage, stream.  The first `ahead` passes of the tile (16 KB per wave each) are requested
 // before the dependency wait [wait0, wait1), so weights stream while the inputs are still being produced;
-// afterwards pass p+1 is requested before pass p is computed.  A tile whose weights are known only at run
-// time (expert up-projection) requests one pass ahead, so that its inputs do not queue behind two passes.
-template <int NB, bool SPLIT, int AHEAD = 2, class RowPtr, class Stage, class Out>
+// afterwards pass p+1 is requested before pass p is computed.  A tile that stages its inputs only after
+// its weights are known (expert up-projection at larger batches) requests one pass ahead, so that its
+// inputs do not queue behind two passes.
+template <int NB, bool SPLIT, class RowPtr, class Stage, class Out>
 __device__ __forceinline__ void mgemv_task(KA& a, Desc w, int t, const RowPtr& W, int nrows, int K, int nb, int wait0,
-                                           int wait1, Stage&& stage, Out&& out, Lds& S) {
+                                           int wait1, Stage&& stage, Out&& out, Lds& S, int ahead = 2) {
   const MGeo g = mgeo(nrows, K);
   MBuf b0, b1;
   mg_load(b0, W, g, 0);
-  if (AHEAD > 1 && g.np > 1) mg_load(b1, W, g, 1);
+  if (ahead > 1 && g.np > 1) mg_load(b1, W, g, 1);
   wait_deps(a, w, wait0, wait1, t);
   stage();
   if (SPLIT) split_x(nb, K, S);
-  if (AHEAD == 1 && g.np > 1) mg_load(b1, W, g, 1);
+  if (ahead == 1 && g.np > 1) mg_load(b1, W, g, 1);
   mark(a, t, 0);
   MAcc acc;
   macc_zero(acc);
@@ -1131,30 +1107,18 @@ __device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
     // gate rows then up rows of this tile, as one 2*nr-row tile over two bases
     const uint16_t* Wg = wg0 + ((int64_t)e * F + r0) * d;
     const uint16_t* Wu = wu0 + ((int64_t)e * F + r0) * d;
-    const MGeo g = mgeo(2 * nr, d);
     auto out = [&](int r, int j, float v) { S.gu[r * 8 + (early ? j : S.slot_b[j])] = v; };
-    if (early && mg_one_full_pass(g)) {
-      // inputs already staged: the tile is one pass, computed as its weights arrive
-      MBuf b0;
-      mg_load_full(b0, Rows2{Wg, Wu, d, nr}, g);
-      mark(a, t, 2);  // weights requested
-      MAcc acc;
-      macc_zero(acc);
-      mark(a, t, 0);
-      mg_compute_full<C::NB>(b0, acc, g, 0, B, S);
-      mg_finish<C::NB>(acc, g, B, out, S);
-      mark(a, t, 1);
-    } else {
-      mgemv_task<C::NB, false, 1>(
-          a, w, t, Rows2{Wg, Wu, d, nr}, 2 * nr, d, early ? B : n, 0, 0,
-          [&] {
-            mark(a, t, 2);  // weights requested
-            if (!early) {
-              stage_split(a, gn, n, S.slot_b, S);
-            }
-          },
-          out, S);
-    }
+    // small batches: inputs already staged, two passes requested ahead; larger batches stage the slot's
+    // tokens once the first pass is in flight
+    mgemv_task<C::NB, false>(
+        a, w, t, Rows2{Wg, Wu, d, nr}, 2 * nr, d, early ? B : n, 0, 0,
+        [&] {
+          mark(a, t, 2);  // weights requested
+          if (!early) {
+            stage_split(a, gn, n, S.slot_b, S);
+          }
+        },
+        out, S, early ? 2 : 1);
     __syncthreads();
     for (int i = tidx(); i < nr * n; i += NT) {
       const int r = i / n, j = i - r * n, b = S.slot_b[j];

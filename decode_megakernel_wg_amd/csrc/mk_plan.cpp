@@ -85,7 +85,7 @@ Tiling choose_tiling(const mk_model_desc* d) {
   t.n_qkv_per_group = (d->n_q_heads / d->n_kv_heads + 2) * d->d_head / t.qkv_rows;
   t.router_rows = std::min(d->n_experts, 16);
   t.n_router = (d->n_experts + t.router_rows - 1) / t.router_rows;
-  t.up_rows = 16;
+  t.up_rows = 64;  // 64 gate + 64 up rows: a 512 KB tile streaming four passes, two in flight
   t.n_up = d->d_ffn / t.up_rows;
   t.lm_rows = 128;  // vocabulary chunk of the LM head's closing phase
   t.n_lm = (d->vocab + t.lm_rows - 1) / t.lm_rows;
@@ -157,11 +157,6 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
   }
   P->B = B;
   P->t = choose_tiling(d);
-  // many expert slots (large batches): longer expert up-projection tiles, each streaming several passes
-  if (std::min(d->n_experts, B * d->top_k) >= 32 && d->d_ffn % 64 == 0) {
-    P->t.up_rows = 64;
-    P->t.n_up = d->d_ffn / 64;
-  }
   const Tiling& t = P->t;
   const int L = d->n_layers, Hkv = d->n_kv_heads, E = d->n_experts;
   P->n_slots = std::min(E, B * d->top_k);
