@@ -1161,7 +1161,7 @@ __device__ __forceinline__ void task_down(KA& a, Desc w, int t, Lds& S) {
   resid_chain(a, w, S);
 }
 
-// LM head, the kernel's closing phase (not a task): once a workgroup's claim queue is exhausted it takes
+// LM head, the kernel's closing phase (not a task): once a workgroup's task phases are exhausted it takes
 // 128-row vocabulary chunks from a shared pool (one atomic per chunk, claimed ahead of use) and streams
 // them as 16 KB-per-wave passes, each requested two passes before its use, so every compute unit keeps
 // reading until the vocabulary is done, whatever its share of the layers was.  Its first chunk is

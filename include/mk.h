@@ -151,7 +151,8 @@ int mk_debug_read(mk_model* m, int kind, void* host_dst, int64_t bytes);
 
 /* Override the grid: n_workgroups persistent workgroups (0 = one per compute unit, at most 1024).  Results
  * do not depend on it (every reduction has a fixed order); it exists for testing and tuning.  Takes effect at
- * the next mk_decode_step, which re-splits the task list into the two claim queues for this grid.
+ * the next mk_decode_step, which lays the task list out for this grid (phase pools for two or more
+ * workgroups, one in-order claim sequence for one).
  * Errors: MK_E_INVAL (null handle, n_workgroups outside 0..1024). */
 int mk_set_grid(mk_model* m, int32_t n_workgroups);
 
@@ -162,7 +163,7 @@ int mk_free_model(mk_model* m);
 const char* mk_last_error(void);
 
 /* Pure host planning, for tools and tests (no device needed): the task list mk_build_tasks would emit
- * for `desc` and `batch`, in topological order (before its split into claim queues).  n_tasks receives the
+ * for `desc` and `batch`, in topological order (the order the phases follow).  n_tasks receives the
  * task count, n_counters (nullable) the counter count; tasks_out may be null to query the sizes.
  * Errors: MK_E_INVAL (bad shape or batch), MK_E_RANGE (cap smaller than the task count). */
 int mk_plan_tasks(const mk_model_desc* desc, const mk_batch* batch, int32_t* tasks_out, int64_t cap, int64_t* n_tasks,

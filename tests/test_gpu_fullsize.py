@@ -1,5 +1,5 @@
 """GPU parity at the full model size, in the launch configuration the benchmark times (one workgroup per
-compute unit, two claim queues, no debug switches unless a check needs them).
+compute unit, phase pools, no debug switches unless a check needs them).
 
 The 48-layer synthetic model (d_model 2048, 32 q / 4 KV heads x 128, 128 experts top-8, d_ffn 768, vocab
 262144) runs one or two decode steps per workload; the oracle (fp64-accumulating C, weights generated per
