@@ -40,12 +40,8 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-template <int N, int R>
-struct NVR {
-  static constexpr int nv = N, rpw = R;
-};
-// A compiled shape class of the kernel: head dim, GQA group, and the 16-byte-vector counts per lane of
-// the three GEMV reduction lengths (d_model, d_ffn, group * d_head).  One kernel is instantiated per
+// A compiled shape class of the kernel: head dim, GQA group, bounds of the three GEMV reduction lengths
+// (d_model <= 512 NVD, d_ffn <= 512 NVF, group * d_head <= 512 NVO) and the batch class NB.  One kernel is instantiated per
 // class so that each task type has a single code path (the register allocator handles one variant per
 // task far better than a switch over many).
 template <int DH_, int GRP_, int NVD_, int NVF_, int NVO_, int NB_>
@@ -148,24 +144,11 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<0x140>(v);  // row_mirror
   return v;
 }
-// sum over each 8-lane half row
-__device__ __forceinline__ float row8_sum(float v) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  v += dpp<0x141>(v);
-  return v;
-}
-// value of lane (i ^ 16) within each 32-lane half (ds_swizzle, bit mode: and 0x1f, xor 0x10)
-__device__ __forceinline__ float swz_xor16(float v) { return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)); }
 __device__ __forceinline__ float rdl(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
 // full-wave sum, uniform result, fixed order
 __device__ __forceinline__ float wave_sum(float v) {
   v = row16_sum(v);
   return ((rdl(v, 0) + rdl(v, 16)) + rdl(v, 32)) + rdl(v, 48);
-}
-__device__ __forceinline__ double wave_sum_d(double v) {
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return __shfl(v, 0);
 }
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -271,10 +254,8 @@ __device__ __forceinline__ NormGain norm_gain(const uint16_t* gamma, int d) {
   return n;
 }
 
-// RMSNorm of the residual stream into LDS: xs[j][i] = x[b][i] * (gamma[i] * inv_rms[b]) for staging rows
-// j < nb of tokens b = tok[j] (null = identity).  inv_rms[b] = 1 / sqrt(sum of the row tiles' partial sums
-// of squares (tile order) / d + eps).  One round trip: the rows and the partial sums load together, both
-// straight into LDS (stage_norm_issue); stage_norm_finish runs once they have landed.
+// Request the residual-stream rows of staging rows j < nb (token tok[j], null = identity) into S.xs and
+// their row tiles' partial sums of squares into S.ssqv, straight into LDS, in one round trip.
 __device__ __forceinline__ void stage_norm_issue(KA& a, int nb, const int* tok, Lds& S) {
   const int d = a.d, nrt = a.n_rt;
   for (int j = 0; j < nb; ++j) lds_copy(a.x + (tok ? tok[j] : j) * d, S.xs + j * d, d / 4);
@@ -287,39 +268,11 @@ __device__ __forceinline__ void stage_norm_issue(KA& a, int nb, const int* tok, 
                                          (__attribute__((address_space(3))) void*)(S.ssqv + j * nrt), 4, 0, 0);
   }
 }
-__device__ __forceinline__ void stage_norm_finish(KA& a, const NormGain& gn, int nb, Lds& S) {
-  const int d = a.d, nrt = a.n_rt;
-  if (tidx() < nb) {
-    float ss = 0.f;
-    for (int r = 0; r < nrt; ++r) ss += S.ssqv[tidx() * nrt + r];
-    S.inv[tidx()] = 1.0f / sqrtf(ss / (float)d + a.eps);
-  }
-  lds_sync();
-#pragma unroll
-  for (int e = 0; e < NORM_PAIRS; ++e) {
-    const int p = tidx() + e * NT;
-    if (2 * p < d) {
-      const float g0 = bf_lo(gn.g[e]), g1 = bf_hi(gn.g[e]);
-      for (int j = 0; j < nb; ++j) {
-        const float inv = S.inv[j];
-        float* xr = S.xs + j * d + 2 * p;
-        xr[0] *= g0 * inv;
-        xr[1] *= g1 * inv;
-      }
-    }
-  }
-  lds_sync();
-}
-__device__ __forceinline__ void stage_norm(KA& a, const NormGain& gn, int nb, const int* tok, Lds& S) {
-  stage_norm_issue(a, nb, tok, S);
-  drain_stores();
-  __syncthreads();
-  stage_norm_finish(a, gn, nb, S);
-}
 
 // RMSNorm of the residual stream straight into the BF16 hi/lo matrix-core operand (xb_off(j, 0) and
-// xb_off(j, 1) for staging row j < nb, token tok[j]): one read of the staged rows, no normalised fp32
-// copy.  inv_rms[b] is formed as in stage_norm_finish (tile order); wave j sums token j's partials.
+// xb_off(j, 1) for staging row j < nb, token tok[j]): n = x[b][i] * (gamma[i] * inv_rms[b]) with
+// inv_rms[b] = 1 / sqrt(sum of the row tiles' partial sums of squares, added in tile order, / d + eps);
+// one read of the staged rows, no normalised fp32 copy.
 __device__ __forceinline__ void stage_split(KA& a, const NormGain& gn, int nb, const int* tok, Lds& S) {
   const int d = a.d, nrt = a.n_rt;
   stage_norm_issue(a, nb, tok, S);
@@ -329,7 +282,7 @@ __device__ __forceinline__ void stage_split(KA& a, const NormGain& gn, int nb, c
   {
     const int wave = tidx() >> 6, lane = tidx() & 63;
     for (int j = wave; j < nb; j += NW) {
-      // the same additions in the same order as the serial sum of stage_norm_finish (lane 0 adds them all),
+      // lane 0 adds the partials in tile order (every consumer forms inv_rms with the same additions),
       // with every partial read first
       if (lane == 0) {
         float v[32];
