@@ -189,3 +189,26 @@ def test_task_counts_full_model():
     assert ops[OP_LMHEAD] == 0   # the LM head is the kernel's closing phase, not tasks
     # about 128 splits per layer: 8193 positions x 4 KV groups / 128 = 257 -> 384 positions (3 chunks of 128)
     assert ops[OP_ATTN] == 48 * 4 * -(-(8192 + 1) // 384)
+
+
+@pytest.mark.parametrize("name,B_lens", [("tiny", [128]), ("tiny", [5, 300, 17, 0]), ("full", [8192]),
+                                         ("full", [1024, 30000, 4000, 70000, 2000, 9000, 1500, 12000])])
+def test_task_list_has_the_regular_phase_structure(name, B_lens):
+    """The launcher runs the list as phases only when it is the embedding tiles followed, layer by layer, by
+    the same sequence of operation runs with the same sizes (otherwise it falls back to in-order claims):
+    every planned list must have that structure."""
+    shape = W.TINY if name == "tiny" else W.FULL
+    maxp = max(B_lens) // 16 + 2
+    d = desc_for(shape, B=len(B_lens), pages=maxp, n_pages=maxp * len(B_lens))
+    tasks, _ = mk.mk_plan_tasks(d, B_lens)
+    runs = phases_of(tasks)
+    assert all(tasks[t, W_OP] == OP_EMBED for t in runs[0])
+    L = shape.n_layers
+    assert (len(runs) - 1) % L == 0
+    npl = (len(runs) - 1) // L
+    assert 1 <= npl <= 7
+    first = [(int(tasks[r[0], W_OP]), len(r)) for r in runs[1:1 + npl]]
+    for l in range(L):
+        layer_runs = runs[1 + l * npl:1 + (l + 1) * npl]
+        assert [(int(tasks[r[0], W_OP]), len(r)) for r in layer_runs] == first
+        assert all(int(tasks[t, W_LAYER]) == l for r in layer_runs for t in r)
