@@ -1303,15 +1303,19 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
     len = 0;
   }
   const int npos = len + 1;
-  int chunk = (npos + nsplit - 1) / nsplit;
-  chunk = (chunk + CH - 1) / CH * CH;
-  if (chunk > ATTN_MAX_SPLIT_PAGES * 16) {  // lengths grew far beyond the planned split count
-    if (tid == 0) raise_error(a, ERRC_SEQLEN, t);
-    chunk = ATTN_MAX_SPLIT_PAGES * 16;
+  // the planner cuts the cached positions [0, len) into splits of w[W_R0] positions (whole 128-position
+  // chunks, fixed for the task list's life); the last split takes the rest of the cached positions (a
+  // context that grew since planning adds to it) and the new token (position len)
+  const int chunk = w[W_R0];
+  const bool last = s == nsplit - 1;
+  const int j0 = chunk > 0 ? (int)min<int64_t>((int64_t)s * chunk, len) : 0;
+  const int j1 = last ? npos : min(j0 + chunk, len);
+  int jc1 = min(j1, len);  // cached positions end
+  if (chunk <= 0 || chunk % CH != 0 || jc1 - j0 > ATTN_MAX_SPLIT_PAGES * 16) {  // bad descriptor, or lengths
+    if (tid == 0) raise_error(a, ERRC_SEQLEN, t);                                  // far beyond the plan
+    jc1 = j0;
   }
-  const int j0 = min(s * chunk, npos), j1 = min(j0 + chunk, npos);
-  const int jc1 = min(j1, len);  // cached positions end
-  const bool has_new = (j0 <= len && len < j1);
+  const bool has_new = last;
   const int32_t* ptab = a.page_tables + (int64_t)b * a.max_pages;
   uint16_t* kvl = a.kv + (int64_t)l * a.n_pages * 2 * Hkv * 16 * DH;
   const int64_t vstride = (int64_t)Hkv * 16 * DH;
@@ -1608,16 +1612,17 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
     float* wsc = S.xs;                               // [GRP][nsplit] running max, then weights exp(m_s - M)
     float* lsc = S.xs + GRP * ATTN_MAX_SPLITS;       // [GRP][nsplit] running sums
     float* lsum = S.xs + 2 * GRP * ATTN_MAX_SPLITS;  // [GRP]
-    // One round trip: each thread requests its two outputs' values of the first 16 splits, then the splits'
-    // (max, sum) pairs go to LDS; later 16-split chunks (long contexts) are requested as they are merged.
+    // One round trip: each thread requests its two outputs' values of the first 32 splits, then the splits'
+    // (max, sum) pairs go to LDS; later 32-split chunks (long contexts) are requested as they are merged.
     static_assert(GRP * DH <= 2 * NT, "two outputs per thread");
     const bool has0 = tid < GRP * DH, has1 = tid + NT < GRP * DH;
     const int h0 = has0 ? tid / DH : 0, d0 = has0 ? tid - h0 * DH : 0;
     const int h1 = has1 ? (tid + NT) / DH : h0, d1 = has1 ? (tid + NT) - h1 * DH : d0;
-    float v0[16], v1[16];
+    constexpr int MQ = 32;
+    float v0[MQ], v1[MQ];
     auto load_chunk = [&](int q) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < MQ; ++u) {
         const bool ok = has0 && q + u < nsplit;
         v0[u] = ok ? p0[((int64_t)(q + u) * GRP + h0) * (DH + 2) + d0] : 0.f;
         v1[u] = ok ? p0[((int64_t)(q + u) * GRP + h1) * (DH + 2) + d1] : 0.f;
@@ -1648,10 +1653,10 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
     }
     __syncthreads();
     float o0 = 0.f, o1 = 0.f;
-    for (int q = 0; q < nsplit; q += 16) {
+    for (int q = 0; q < nsplit; q += MQ) {
       if (q > 0) load_chunk(q);
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < MQ; ++u) {
         if (q + u < nsplit) {
           o0 = fmaf(v0[u], wsc[h0 * nsplit + q + u], o0);
           o1 = fmaf(v1[u], wsc[h1 * nsplit + q + u], o1);

@@ -166,6 +166,7 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
   // positions per attention split: ATTN_SPLIT_POS, more when the batch's contexts are long, so that a layer
   // has about ATTN_TARGET_TASKS splits over all sequences and KV groups (each split then streams several
   // chunks, and the merge reads fewer partials), up to ATTN_MAX_SPLIT_POS (more splits beyond that)
+  // (splits cover the cached positions in whole 128-position chunks; the last one also takes the new token)
   int64_t total = 0;
   for (int b = 0; b < B; ++b) {
     const int32_t len = batch->seq_lens[b];
@@ -173,12 +174,12 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
       *msg = "sequence length negative or beyond max_pages_per_seq";
       return MK_E_INVAL;
     }
-    total += (int64_t)len + 1;
+    total += std::max<int64_t>(len, 1);
   }
-  int64_t split_pos = (total * Hkv + ATTN_TARGET_TASKS - 1) / ATTN_TARGET_TASKS;
-  split_pos = std::max<int64_t>(ATTN_SPLIT_POS, std::min<int64_t>((split_pos + 127) / 128 * 128, ATTN_MAX_SPLIT_POS));
+  int64_t split_pos = (total * Hkv + ATTN_TARGET_TASKS / 2) / ATTN_TARGET_TASKS;
+  split_pos = std::max<int64_t>(ATTN_SPLIT_POS, std::min<int64_t>((split_pos + 64) / 128 * 128, ATTN_MAX_SPLIT_POS));
   for (int b = 0; b < B; ++b) {
-    const int64_t s = ((int64_t)batch->seq_lens[b] + 1 + split_pos - 1) / split_pos;
+    const int64_t s = (std::max<int64_t>(batch->seq_lens[b], 1) + split_pos - 1) / split_pos;
     P->splits[b] = (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, ATTN_MAX_SPLITS));
   }
   P->desc.clear();
@@ -195,58 +196,77 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
     router_epilogue(w, cl, t, 0);
   }
   for (int l = 0; l < L; ++l) {
-    for (int g = 0; g < Hkv; ++g)
-      for (int i = 0; i < t.n_qkv_per_group; ++i) {
-        int32_t* w = em.add(OP_QKV, l);
-        w[W_A] = g;
-        w[W_R0] = i * t.qkv_rows;
-        w[W_R1] = (i + 1) * t.qkv_rows;
-        set_wait(w, 0, cl.xready + l, t.n_rt);
-        set_sig(w, cl.qkv_done + l * Hkv + g);
-      }
-    for (int g = 0; g < Hkv; ++g)
-      for (int b = 0; b < B; ++b)
-        for (int s = 0; s < P->splits[b]; ++s) {
-          int32_t* w = em.add(OP_ATTN, l);
-          w[W_A] = b;
-          w[W_B] = g;
-          w[W_C] = s;
-          w[W_D] = P->splits[b];
-          set_wait(w, 0, cl.qkv_done + l * Hkv + g, t.n_qkv_per_group);
-          set_sig(w, cl.attn_done + l * Hkv + g);  // issued only by the split that arrives last
-          w[W_ARR] = cl.attn_arrive + (l * B + b) * Hkv + g;
-          w[W_ARRN] = P->splits[b];
+    auto emit_qkv = [&] {
+      for (int g = 0; g < Hkv; ++g)
+        for (int i = 0; i < t.n_qkv_per_group; ++i) {
+          int32_t* w = em.add(OP_QKV, l);
+          w[W_A] = g;
+          w[W_R0] = i * t.qkv_rows;
+          w[W_R1] = (i + 1) * t.qkv_rows;
+          set_wait(w, 0, cl.xready + l, t.n_rt);
+          set_sig(w, cl.qkv_done + l * Hkv + g);
         }
-    for (int s = 0; s < P->n_slots; ++s)
-      for (int i = 0; i < t.n_up; ++i) {
-        int32_t* w = em.add(OP_UP, l);
-        w[W_A] = s;
-        w[W_R0] = i * t.up_rows;
-        w[W_R1] = (i + 1) * t.up_rows;
-        set_wait(w, 0, cl.slot_ready + l * P->n_slots + s, 1);  // the slot's routing (expert, tokens)
-        set_wait(w, 1, cl.xready + l, t.n_rt);                   // the layer's input, staged before routing
-        set_wait(w, 2, cl.router_arrive + l, t.n_rt);            // small batches route from the partials themselves
-        set_sig(w, cl.up_done + l * P->n_slots + s);
-      }
-    for (int g = 0; g < Hkv; ++g)
-      for (int r = 0; r < t.n_rt; ++r) {
-        int32_t* w = em.add(OP_OPROJ, l);
-        w[W_A] = g;
-        w[W_R0] = r * t.rt;
-        w[W_R1] = (r + 1) * t.rt;
-        set_wait(w, 0, cl.attn_done + l * Hkv + g, B);
-        resid_epilogue(w, cl, t, l, r, Hkv + P->n_slots);
-      }
-    for (int s = 0; s < P->n_slots; ++s)
-      for (int r = 0; r < t.n_rt; ++r) {
-        int32_t* w = em.add(OP_DOWN, l);
-        w[W_A] = s;
-        w[W_R0] = r * t.rt;
-        w[W_R1] = (r + 1) * t.rt;
-        set_wait(w, 0, cl.slot_ready + l * P->n_slots + s, 1);     // routing known: expert weights can stream
-        set_wait(w, 1, cl.up_done + l * P->n_slots + s, t.n_up);    // this expert's hidden state is complete
-        resid_epilogue(w, cl, t, l, r, Hkv + P->n_slots);
-      }
+    };
+    auto emit_attn = [&] {
+      for (int g = 0; g < Hkv; ++g)
+        for (int b = 0; b < B; ++b)
+          for (int s = 0; s < P->splits[b]; ++s) {
+            int32_t* w = em.add(OP_ATTN, l);
+            w[W_A] = b;
+            w[W_B] = g;
+            w[W_C] = s;
+            w[W_D] = P->splits[b];
+            w[W_R0] = (int32_t)split_pos;  // cached positions per split (the last one takes the rest)
+            set_wait(w, 0, cl.qkv_done + l * Hkv + g, t.n_qkv_per_group);
+            set_sig(w, cl.attn_done + l * Hkv + g);  // issued only by the split that arrives last
+            w[W_ARR] = cl.attn_arrive + (l * B + b) * Hkv + g;
+            w[W_ARRN] = P->splits[b];
+          }
+    };
+    auto emit_up = [&] {
+      for (int s = 0; s < P->n_slots; ++s)
+        for (int i = 0; i < t.n_up; ++i) {
+          int32_t* w = em.add(OP_UP, l);
+          w[W_A] = s;
+          w[W_R0] = i * t.up_rows;
+          w[W_R1] = (i + 1) * t.up_rows;
+          set_wait(w, 0, cl.slot_ready + l * P->n_slots + s, 1);  // the slot's routing (expert, tokens)
+          set_wait(w, 1, cl.xready + l, t.n_rt);                   // the layer's input, staged before routing
+          set_wait(w, 2, cl.router_arrive + l, t.n_rt);            // small batches route from the partials themselves
+          set_sig(w, cl.up_done + l * P->n_slots + s);
+        }
+    };
+    auto emit_oproj = [&] {
+      for (int g = 0; g < Hkv; ++g)
+        for (int r = 0; r < t.n_rt; ++r) {
+          int32_t* w = em.add(OP_OPROJ, l);
+          w[W_A] = g;
+          w[W_R0] = r * t.rt;
+          w[W_R1] = (r + 1) * t.rt;
+          set_wait(w, 0, cl.attn_done + l * Hkv + g, B);
+          resid_epilogue(w, cl, t, l, r, Hkv + P->n_slots);
+        }
+    };
+    auto emit_down = [&] {
+      for (int s = 0; s < P->n_slots; ++s)
+        for (int r = 0; r < t.n_rt; ++r) {
+          int32_t* w = em.add(OP_DOWN, l);
+          w[W_A] = s;
+          w[W_R0] = r * t.rt;
+          w[W_R1] = (r + 1) * t.rt;
+          set_wait(w, 0, cl.slot_ready + l * P->n_slots + s, 1);     // routing known: expert weights can stream
+          set_wait(w, 1, cl.up_done + l * P->n_slots + s, t.n_up);    // this expert's hidden state is complete
+          resid_epilogue(w, cl, t, l, r, Hkv + P->n_slots);
+        }
+    };
+    // per layer: QKV tiles, attention splits, expert up-projection tiles, O-projection tiles, expert
+    // down-projection tiles (topological; as phases, the attention splits are taken first so that their
+    // old K/V stream while the QKV tiles run, and measured faster than the up-projections first)
+    emit_qkv();
+    emit_attn();
+    emit_up();
+    emit_oproj();
+    emit_down();
   }
   (void)grp;
   return MK_OK;
