@@ -59,7 +59,7 @@ constexpr int DESC_WORDS = 32;
 
 // Tile sizes chosen by the planner (rows per task); the kernel reads r0/r1 from the descriptor.
 constexpr int ATTN_SPLIT_POS = 256;  // fewest positions per attention split
-constexpr int ATTN_TARGET_TASKS = 128;  // attention splits per layer the planner aims for (all sequences, KV groups)
+constexpr int ATTN_TARGET_TASKS = 96;  // attention splits per layer the planner aims for (all sequences, KV groups)
 constexpr int ATTN_MAX_SPLIT_POS = 1024;  // most positions per split the planner chooses (before the split cap)
 constexpr int ATTN_MAX_SPLIT_PAGES = 256;  // pages one split may cover (its page list is staged in LDS)
 constexpr int ATTN_MAX_SPLITS = 256;

@@ -187,11 +187,12 @@ def test_task_counts_full_model():
     tasks, _ = mk.mk_plan_tasks(d, [8192])
     ops = np.bincount(tasks[:, W_OP], minlength=10)
     assert ops[OP_LMHEAD] == 0   # the LM head is the kernel's closing phase, not tasks
-    # about 128 splits per layer: 8192 cached positions x 4 KV groups / 128 = 256 positions (2 chunks of 128)
-    # per split; the last split of each (sequence, group) also takes the new token
-    assert ops[OP_ATTN] == 48 * 4 * (8192 // 256)
+    # about 96 splits per layer: 8192 cached positions x 4 KV groups / 96 = 341 -> 384 positions (3 chunks of
+    # 128) per split, 22 splits per KV group; the last split of each (sequence, group) takes the rest (128
+    # cached positions) and the new token
+    assert ops[OP_ATTN] == 48 * 4 * 22
     attn = tasks[tasks[:, W_OP] == 4]
-    assert (attn[:, W_R0] == 256).all() and (attn[:, W_D] == 32).all()
+    assert (attn[:, W_R0] == 384).all() and (attn[:, W_D] == 22).all()
 
 
 @pytest.mark.parametrize("name,B_lens", [("tiny", [128]), ("tiny", [5, 300, 17, 0]), ("full", [8192]),
