@@ -143,8 +143,9 @@ int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out
   HIPCHK(hipGetDevice(&m->device));
   HIPCHK(hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, m->device));
   m->grid = std::min(m->n_cu, mk::LM_MAX_WG);
-  m->tiling = mk::choose_tiling(desc);
+  m->tiling = mk::choose_tiling(desc, desc->max_batch);
   const mk::Tiling& t = m->tiling;
+  const int n_up_max = std::max(t.n_up, mk::choose_tiling(desc, 1).n_up);  // small batches cut finer
   const int d = desc->d_model, Hq = desc->n_q_heads, Hkv = desc->n_kv_heads, dh = desc->d_head, E = desc->n_experts;
   const int k = desc->top_k, F = desc->d_ffn, maxB = desc->max_batch, grp = Hq / Hkv;
   m->max_slots = std::min(E, maxB * k);
@@ -152,7 +153,7 @@ int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out
   cl.build(L, Hkv, maxB, m->max_slots, t.n_rt);
   m->max_counters = cl.total;
   m->max_tasks = (int64_t)t.n_rt + (int64_t)L * (t.n_router + Hkv * t.n_qkv_per_group + (int64_t)Hkv * maxB * mk::ATTN_MAX_SPLITS +
-                                                 (int64_t)m->max_slots * t.n_up + Hkv * t.n_rt + (int64_t)m->max_slots * t.n_rt + t.n_rt) +
+                                                 (int64_t)m->max_slots * n_up_max + Hkv * t.n_rt + (int64_t)m->max_slots * t.n_rt + t.n_rt) +
                  t.n_lm;
 
   auto cleanup = [&](int code) {

@@ -77,7 +77,7 @@ int validate_desc(const mk_model_desc* d, std::string* msg) {
   return MK_OK;
 }
 
-Tiling choose_tiling(const mk_model_desc* d) {
+Tiling choose_tiling(const mk_model_desc* d, int batch) {
   Tiling t{};
   t.rt = d->d_model >= 1024 ? 128 : 32;
   t.n_rt = d->d_model / t.rt;
@@ -85,7 +85,10 @@ Tiling choose_tiling(const mk_model_desc* d) {
   t.n_qkv_per_group = (d->n_q_heads / d->n_kv_heads + 2) * d->d_head / t.qkv_rows;
   t.router_rows = std::min(d->n_experts, 16);
   t.n_router = (d->n_experts + t.router_rows - 1) / t.router_rows;
-  t.up_rows = 64;  // 64 gate + 64 up rows: a 512 KB tile streaming four passes, two in flight
+  // 64 gate + 64 up rows (a 512 KB tile at d_model 2048, four passes, two in flight); at batches of 1-2, 48 + 48
+  // rows where d_ffn allows (more, shorter tiles spread the few experts' 50 MB over more compute units:
+  // measured +1.5 % at batch 1, -3 to -5 % at batch 8, where many experts already fill the machine)
+  t.up_rows = batch <= 2 && d->d_ffn % 48 == 0 ? 48 : 64;
   t.n_up = d->d_ffn / t.up_rows;
   t.lm_rows = 128;  // vocabulary chunk of the LM head's closing phase
   t.n_lm = (d->vocab + t.lm_rows - 1) / t.lm_rows;
@@ -156,7 +159,7 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
     return MK_E_INVAL;
   }
   P->B = B;
-  P->t = choose_tiling(d);
+  P->t = choose_tiling(d, B);
   const Tiling& t = P->t;
   const int L = d->n_layers, Hkv = d->n_kv_heads, E = d->n_experts;
   P->n_slots = std::min(E, B * d->top_k);

@@ -31,7 +31,8 @@ struct Plan {
 
 // Returns MK_OK or an error code with a message.
 int validate_desc(const mk_model_desc* d, std::string* msg);
-Tiling choose_tiling(const mk_model_desc* d);
+// Tile sizes for a batch of `batch` sequences (only the expert up-projection tiles depend on it).
+Tiling choose_tiling(const mk_model_desc* d, int batch);
 int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* out, std::string* msg);
 
 }  // namespace mk

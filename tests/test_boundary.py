@@ -193,6 +193,13 @@ def test_task_counts_full_model():
     assert ops[OP_ATTN] == 48 * 4 * 22
     attn = tasks[tasks[:, W_OP] == 4]
     assert (attn[:, W_R0] == 384).all() and (attn[:, W_D] == 22).all()
+    # expert up-projection tiles: 48 gate + 48 up rows at batches of 1-2 (16 tiles per expert), 64 + 64 above
+    up = tasks[tasks[:, W_OP] == 5]
+    assert ops[5] == 48 * 8 * 16 and ((up[:, W_R1] - up[:, W_R0]) == 48).all()
+    d8 = desc_for(W.FULL, B=8, pages=600 * 8, n_pages=600 * 8)
+    t8, _ = mk.mk_plan_tasks(d8, [8192] * 8)
+    up8 = t8[t8[:, W_OP] == 5]
+    assert ((up8[:, W_R1] - up8[:, W_R0]) == 64).all() and len(up8) == 48 * 64 * 12
 
 
 @pytest.mark.parametrize("name,B_lens", [("tiny", [128]), ("tiny", [5, 300, 17, 0]), ("full", [8192]),
