@@ -1279,6 +1279,74 @@ __device__ __forceinline__ void lm_phase(KA& a, Lds& S) {
 }
 
 // ------------------------------------------------------------------------------------------ attention
+// The last split of (b, g) to finish merges all splits (log-sum-exp) and publishes the group's output.
+template <int DH, int GRP>
+__device__ __forceinline__ void attn_merge(KA& a, Desc w, int t, int b, int g, int nsplit, Lds& S) {
+  const int tid = tidx(), wave = tid >> 6, lane = tid & 63;
+  const int Hkv = a.Hkv;
+  if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) {
+    mark(a, t, 3);
+    const float* p0 = a.apart + (((int64_t)b * Hkv + g) * ATTN_MAX_SPLITS) * GRP * (DH + 2);
+    float* wsc = S.xs;                               // [GRP][nsplit] running max, then weights exp(m_s - M)
+    float* lsc = S.xs + GRP * ATTN_MAX_SPLITS;       // [GRP][nsplit] running sums
+    float* lsum = S.xs + 2 * GRP * ATTN_MAX_SPLITS;  // [GRP]
+    // One round trip: each thread requests its two outputs' values of the first 32 splits, then the splits'
+    // (max, sum) pairs go to LDS; later 32-split chunks (long contexts) are requested as they are merged.
+    static_assert(GRP * DH <= 2 * NT, "two outputs per thread");
+    const bool has0 = tid < GRP * DH, has1 = tid + NT < GRP * DH;
+    const int h0 = has0 ? tid / DH : 0, d0 = has0 ? tid - h0 * DH : 0;
+    const int h1 = has1 ? (tid + NT) / DH : h0, d1 = has1 ? (tid + NT) - h1 * DH : d0;
+    constexpr int MQ = 32;
+    float v0[MQ], v1[MQ];
+    auto load_chunk = [&](int q) {
+#pragma unroll
+      for (int u = 0; u < MQ; ++u) {
+        const bool ok = has0 && q + u < nsplit;
+        v0[u] = ok ? p0[((int64_t)(q + u) * GRP + h0) * (DH + 2) + d0] : 0.f;
+        v1[u] = ok ? p0[((int64_t)(q + u) * GRP + h1) * (DH + 2) + d1] : 0.f;
+      }
+    };
+    load_chunk(0);
+    for (int i = tid; i < GRP * nsplit; i += NT) {
+      const int h = i / nsplit, q = i - h * nsplit;
+      const float* r = p0 + ((int64_t)q * GRP + h) * (DH + 2) + DH;
+      wsc[i] = r[0];
+      lsc[i] = r[1];
+    }
+    __syncthreads();
+    if (wave < GRP) {
+      const int h = wave;
+      float M = -INFINITY;
+      for (int q = lane; q < nsplit; q += 64) M = fmaxf(M, wsc[h * nsplit + q]);
+      M = wave_max(M);
+      float Ls = 0.f;
+      for (int q = lane; q < nsplit; q += 64) {
+        const float mq = wsc[h * nsplit + q];
+        const float wq = mq == -INFINITY ? 0.f : expf(mq - M);
+        wsc[h * nsplit + q] = wq;
+        Ls = fmaf(lsc[h * nsplit + q], wq, Ls);
+      }
+      Ls = wave_sum(Ls);
+      if (lane == 0) lsum[h] = Ls;
+    }
+    __syncthreads();
+    float o0 = 0.f, o1 = 0.f;
+    for (int q = 0; q < nsplit; q += MQ) {
+      if (q > 0) load_chunk(q);
+#pragma unroll
+      for (int u = 0; u < MQ; ++u) {
+        if (q + u < nsplit) {
+          o0 = fmaf(v0[u], wsc[h0 * nsplit + q + u], o0);
+          o1 = fmaf(v1[u], wsc[h1 * nsplit + q + u], o1);
+        }
+      }
+    }
+    if (has0) pub(a.attn_o + (int64_t)b * a.Hq * DH + ((int64_t)g * GRP + h0) * DH + d0, o0 / lsum[h0]);
+    if (has1) pub(a.attn_o + (int64_t)b * a.Hq * DH + ((int64_t)g * GRP + h1) * DH + d1, o1 / lsum[h1]);
+    signal(a, w[W_SIG], w[W_SIGN]);
+  }
+}
+
 // Split s of (sequence b, KV group g) covers positions [j0, j1) of the sequence's 0..len window (len =
 // its prior length; position len is the new token, taken from this step's projections, RoPE'd, rounded
 // to BF16 and written to the cache by the split that holds it).  The split's page list and its first
@@ -1727,73 +1795,353 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
     pub(part + tid * (DH + 2) + DH + 1, S.hl[tid]);
   }
   mark(a, t, 2);
-  // the last split of (b, g) to finish merges all splits (log-sum-exp) and publishes the group's output
-  if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) {
-    mark(a, t, 3);
-    const float* p0 = a.apart + (((int64_t)b * Hkv + g) * ATTN_MAX_SPLITS) * GRP * (DH + 2);
-    float* wsc = S.xs;                               // [GRP][nsplit] running max, then weights exp(m_s - M)
-    float* lsc = S.xs + GRP * ATTN_MAX_SPLITS;       // [GRP][nsplit] running sums
-    float* lsum = S.xs + 2 * GRP * ATTN_MAX_SPLITS;  // [GRP]
-    // One round trip: each thread requests its two outputs' values of the first 32 splits, then the splits'
-    // (max, sum) pairs go to LDS; later 32-split chunks (long contexts) are requested as they are merged.
-    static_assert(GRP * DH <= 2 * NT, "two outputs per thread");
-    const bool has0 = tid < GRP * DH, has1 = tid + NT < GRP * DH;
-    const int h0 = has0 ? tid / DH : 0, d0 = has0 ? tid - h0 * DH : 0;
-    const int h1 = has1 ? (tid + NT) / DH : h0, d1 = has1 ? (tid + NT) - h1 * DH : d0;
-    constexpr int MQ = 32;
-    float v0[MQ], v1[MQ];
-    auto load_chunk = [&](int q) {
-#pragma unroll
-      for (int u = 0; u < MQ; ++u) {
-        const bool ok = has0 && q + u < nsplit;
-        v0[u] = ok ? p0[((int64_t)(q + u) * GRP + h0) * (DH + 2) + d0] : 0.f;
-        v1[u] = ok ? p0[((int64_t)(q + u) * GRP + h1) * (DH + 2) + d1] : 0.f;
-      }
-    };
-    load_chunk(0);
-    for (int i = tid; i < GRP * nsplit; i += NT) {
-      const int h = i / nsplit, q = i - h * nsplit;
-      const float* r = p0 + ((int64_t)q * GRP + h) * (DH + 2) + DH;
-      wsc[i] = r[0];
-      lsc[i] = r[1];
+  attn_merge<DH, GRP>(a, w, t, b, g, nsplit, S);
+}
+
+// d_head 128: split s of (sequence b, KV group g) with every wave independent.  The split's cached
+// positions are cut into blocks of 32; wave w takes blocks w, w + 8, w + 16, ... and runs them start to
+// finish on its own (no workgroup barrier inside the loop): K of the block in registers (row quads, see
+// the GEMV core), V straight into the wave's own 8 KB LDS area by direct loads (swizzled 16-byte slots),
+// the next block of both requested before the current one is computed.  Scores on MFMA (K rows as A,
+// the group's RoPE'd, scaled queries as BF16 hi + lo B operands), online softmax per head over the
+// block (eight lanes per head), then P.V on MFMA: O^T[d][h] += V^T[d][pos] P^T[pos][h] with V^T gathered
+// from the wave's LDS area and P as BF16 hi + lo parts.  Each wave keeps its own running (max, sum, O);
+// the waves are combined once at the end, then the new token (position len, last split only) is added.
+template <int DH, int GRP>
+__device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
+  static_assert(DH == 128 && GRP == 8, "wave-independent attention: d_head 128, eight heads per KV group");
+  constexpr int WB = 32;                 // positions per wave block
+  constexpr int NKQ = WB / 4;            // K loads (position quads) per block and lane
+  constexpr int VLD = WB * DH * 2 / 16 / 64;  // 16-byte direct V loads per block and lane (8)
+  constexpr int VW = WB * DH;            // bf16 elements of a wave's V area (8 KB)
+  static_assert(NKQ + VLD < 64, "vmcnt field");
+  const int l = w[W_LAYER], b = w[W_A], g = w[W_B], s = w[W_C], nsplit = w[W_D];
+  const int tid = tidx(), wave = tid >> 6, lane = tid & 63;
+  const int Hkv = a.Hkv;
+  int len = a.seq_lens[b];
+  if (len < 0 || len / 16 >= a.max_pages) {
+    if (tid == 0) raise_error(a, ERRC_SEQLEN, t);
+    len = 0;
+  }
+  // the planner cuts the cached positions [0, len) into splits of w[W_R0] positions (whole 128-position
+  // chunks, fixed for the task list's life); the last split takes the rest of the cached positions (a
+  // context that grew since planning adds to it) and the new token (position len)
+  const int chunk = w[W_R0];
+  const bool last = s == nsplit - 1;
+  const int j0 = chunk > 0 ? (int)min<int64_t>((int64_t)s * chunk, len) : 0;
+  const int j1 = last ? len + 1 : min(j0 + chunk, len);
+  int jc1 = min(j1, len);  // cached positions end
+  if (chunk <= 0 || chunk % 128 != 0 || jc1 - j0 > ATTN_MAX_SPLIT_PAGES * 16) {
+    if (tid == 0) raise_error(a, ERRC_SEQLEN, t);
+    jc1 = j0;
+  }
+  const bool has_new = last;
+  const int32_t* ptab = a.page_tables + (int64_t)b * a.max_pages;
+  uint16_t* kvl = a.kv + (int64_t)l * a.n_pages * 2 * Hkv * 16 * DH;
+  const int64_t vstride = (int64_t)Hkv * 16 * DH;
+
+  // page list of the split
+  const int np0 = j0 >> 4, npg = jc1 > j0 ? ((jc1 - 1) >> 4) - np0 + 1 : 0;
+  for (int i = tid; i < npg; i += NT) {
+    int ph = ptab[np0 + i];
+    if (ph < 0 || ph >= a.n_pages) {
+      raise_error(a, ERRC_PAGE, t);
+      ph = -1;
     }
-    __syncthreads();
+    S.pages[i] = ph;
+  }
+  if (tid == 0) S.xb_layer = 0;  // the V areas overwrite the staged GEMV input
+  __syncthreads();
+  // cache offset of a position's K row (the layer's first row for positions beyond the split or on a bad
+  // page: every load instruction is issued, so each block is exactly NKQ + VLD loads and the V waits
+  // below can count them; those rows' scores become -inf and their V rows are zeroed where read)
+  auto kv_off = [&](int pos) -> int64_t {
+    if (pos >= jc1) return 0;
+    const int ph = S.pages[(pos >> 4) - np0];
+    return ph < 0 ? 0 : (((int64_t)ph * 2) * Hkv + g) * 16 * DH + (pos & 15) * DH;
+  };
+  const int nblk = (jc1 - j0 + WB - 1) / WB;
+  uint16_t* const va0 = reinterpret_cast<uint16_t*>(S.xs) + wave * VW;  // the wave's two V areas
+  uint16_t* const va1 = S.xb + wave * VW;
+  static_assert(NW * VW * 2 <= XS_FLOATS * 4 && NW * VW <= 16 * XBP + 64, "V areas fit the staging areas");
+  auto load_k = [&](int i, u4 (&kk)[NKQ]) {  // block i of this wave
+    const int c0 = j0 + (i * NW + wave) * WB;
+#pragma unroll
+    for (int u = 0; u < NKQ; ++u) {
+      const int pos = c0 + 4 * u + ((lane & 15) >> 2);
+      kk[u] = __builtin_nontemporal_load(as_global(kvl + kv_off(pos) + 32 * (lane >> 4) + 8 * (lane & 3)));
+    }
+  };
+  // V row r of the block keeps its 16-byte chunk c in slot c ^ 2((r >> 3) & 3) of the row
+  auto load_v = [&](int i, uint16_t* va) {
+    const int c0 = j0 + (i * NW + wave) * WB;
+#pragma unroll
+    for (int j = 0; j < VLD; ++j) {
+      const int n = j * 64 + lane;
+      const int r = n >> 4, cg = (n & 15) ^ (2 * ((r >> 3) & 3));
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kvl + kv_off(c0 + r) + vstride + cg * 8),
+                                       (__attribute__((address_space(3))) void*)(va + j * 512), 16, 0, 0);
+    }
+  };
+  u4 kc[NKQ], kx[NKQ];
+  // the wave's first two blocks of old K/V stream while this step's projections are produced
+  load_k(0, kc);
+  load_v(0, va0);
+  load_k(1, kx);
+  load_v(1, va1);
+
+  wait_deps(a, w, 0, N_WAITS, t);
+
+  // queries of the group: RoPE at position len, times 1/sqrt(dh); fp32 copy for the new token's score and
+  // BF16 hi/lo copies (heads as MFMA columns, zero columns beyond the group) for the cached positions,
+  // staged in the probability area (free until the loop)
+  const float* qsrc = a.qkv + ((int64_t)b * Hkv + g) * (GRP + 2) * DH;
+  const float* cs = a.rope_cs + (int64_t)b * (DH / 2) * 2;
+  const float qscale = 1.0f / sqrtf((float)DH);
+  uint16_t* qb = reinterpret_cast<uint16_t*>(S.pt);  // [2][16][DH]: hi then lo
+  static_assert(2 * 16 * DH * 2 <= (int)sizeof(S.pt), "query staging fits the probability area");
+  for (int i = tid; i < 16 * DH; i += NT) {
+    if (i >= GRP * DH) {
+      qb[i] = 0;
+      qb[16 * DH + i] = 0;
+    }
+  }
+  for (int i = tid; i < GRP * DH / 2; i += NT) {
+    const int h = i / (DH / 2), j = i - h * (DH / 2);
+    const float c = cs[2 * j], sn = cs[2 * j + 1];
+    const float x0 = qsrc[h * DH + j], x1 = qsrc[h * DH + j + DH / 2];
+    const float y0 = (x0 * c - x1 * sn) * qscale, y1 = (x0 * sn + x1 * c) * qscale;
+    S.q[h * DH + j] = y0;
+    S.q[h * DH + j + DH / 2] = y1;
+    const uint16_t h0 = f2bf(y0), h1 = f2bf(y1);
+    qb[h * DH + j] = h0;
+    qb[h * DH + j + DH / 2] = h1;
+    qb[16 * DH + h * DH + j] = f2bf(y0 - bf2f(h0));
+    qb[16 * DH + h * DH + j + DH / 2] = f2bf(y1 - bf2f(h1));
+  }
+  if (has_new) {
+    for (int j = tid; j < DH / 2; j += NT) {
+      const float c = cs[2 * j], sn = cs[2 * j + 1];
+      const float x0 = qsrc[GRP * DH + j], x1 = qsrc[GRP * DH + j + DH / 2];
+      S.kn[j] = bf2f(f2bf(x0 * c - x1 * sn));
+      S.kn[j + DH / 2] = bf2f(f2bf(x0 * sn + x1 * c));
+    }
+    for (int j = tid; j < DH; j += NT) S.vn[j] = bf2f(f2bf(qsrc[(GRP + 1) * DH + j]));
+  }
+  for (int i = tid; i < 32; i += NT) S.sc[i] = 0.f;  // zero B rows for the heads beyond the group
+  __syncthreads();
+  if (has_new) {  // the new token's K/V go to the cache slot of position len (layer l)
+    const int ph = ptab[len >> 4];
+    if (ph >= 0 && ph < a.n_pages) {
+      const int64_t base = (((int64_t)ph * 2) * Hkv + g) * 16 * DH + (len & 15) * DH;
+      for (int j = tid; j < DH; j += NT) {
+        kvl[base + j] = f2bf(S.kn[j]);
+        kvl[base + vstride + j] = f2bf(S.vn[j]);
+      }
+    } else if (tid == 0) {
+      raise_error(a, ERRC_PAGE, t);
+    }
+  }
+  // query operands: B column 4s + h holds head 4hg + s at K-part h (chunk 4(l/16) + h of the head's vector)
+  constexpr int NHG = GRP / 4;
+  u4 qh[NHG], ql[NHG];
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    const int hd = 4 * hg + ((lane & 15) >> 2);
+    qh[hg] = *reinterpret_cast<const u4*>(qb + hd * DH + 32 * (lane >> 4) + 8 * (lane & 3));
+    ql[hg] = *reinterpret_cast<const u4*>(qb + 16 * DH + hd * DH + 32 * (lane >> 4) + 8 * (lane & 3));
+  }
+  __syncthreads();  // the probability area becomes the waves' score / probability scratch
+  mark(a, t, 0);
+
+  float* const scw = S.pt + wave * (GRP * WB);                       // [head][32] scores (fp32)
+  uint16_t* const pbw = reinterpret_cast<uint16_t*>(scw);           // then [hi: 8 rows][lo: 8 rows] x 32 BF16
+  float* const alw = S.gu + wave * 8;                               // per-head rescale of the block
+  const uint16_t* const zrow = reinterpret_cast<const uint16_t*>(S.sc);
+  const int q4 = lane >> 4, hc = lane & 15;                         // P.V: lane's position group and column
+  const int sh = lane >> 3, sp = (lane & 7) * 4;                    // softmax: lane's head and positions
+  float m_run = -INFINITY, l_run = 0.f;                             // of head sh (lanes 8sh..8sh+7)
+  f4 oacc[DH / 16];
+#pragma unroll
+  for (int db = 0; db < DH / 16; ++db) oacc[db] = f4{0.f, 0.f, 0.f, 0.f};
+
+  for (int i = 0; wave + i * NW < nblk; ++i) {
+    const int c0 = j0 + (i * NW + wave) * WB;
+    // scores: for position quad u and head group hg, D[4r + h][4s + h] is position 4u + r times head
+    // 4hg + s over K-part h (hi, then lo); the parts are added across each lane quad
+#pragma unroll
+    for (int u = 0; u < NKQ; ++u) {
+#pragma unroll
+      for (int hg = 0; hg < NHG; ++hg) {
+        f4 acc = mfma(kc[u], qh[hg], f4{0.f, 0.f, 0.f, 0.f});
+        acc = mfma(kc[u], ql[hg], acc);
+        float v = pick4(acc, lane & 3);
+        v += dpp<0xB1>(v);
+        v += dpp<0x4E>(v);
+        const int hd = 4 * hg + ((lane >> 2) & 3), pl = 4 * u + (lane >> 4);
+        if ((lane & 3) == 0) scw[hd * WB + pl] = c0 + pl < jc1 ? v : -INFINITY;
+      }
+    }
+    // online softmax of head sh over the block: lanes 8sh..8sh+7 hold four positions each
+    const f4 s4 = *reinterpret_cast<const f4*>(scw + sh * WB + sp);
+    float bm = fmaxf(fmaxf(s4.x, s4.y), fmaxf(s4.z, s4.w));
+    bm = fmaxf(bm, dpp<0xB1>(bm));
+    bm = fmaxf(bm, dpp<0x4E>(bm));
+    bm = fmaxf(bm, dpp<0x141>(bm));
+    const float mnew = fmaxf(m_run, bm);
+    const float alpha = m_run == -INFINITY ? 0.f : expf(m_run - mnew);
+    float pr[4] = {s4.x, s4.y, s4.z, s4.w};
+    float ps = 0.f;
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pr[e] = pr[e] == -INFINITY ? 0.f : expf(pr[e] - mnew);
+      ps += pr[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint16_t a0 = f2bf(pr[2 * e]), a1 = f2bf(pr[2 * e + 1]);
+      hw[e] = (uint32_t)a0 | ((uint32_t)a1 << 16);
+      lw[e] = (uint32_t)f2bf(pr[2 * e] - bf2f(a0)) | ((uint32_t)f2bf(pr[2 * e + 1] - bf2f(a1)) << 16);
+    }
+    ps += dpp<0xB1>(ps);
+    ps += dpp<0x4E>(ps);
+    ps += dpp<0x141>(ps);
+    l_run = l_run * alpha + ps;
+    m_run = mnew;
+    // the block's probabilities overwrite its scores (this wave's reads above are complete: LDS operations
+    // of one wave run in order)
+    *reinterpret_cast<u2*>(pbw + sh * WB + sp) = u2{hw[0], hw[1]};
+    *reinterpret_cast<u2*>(pbw + (GRP + sh) * WB + sp) = u2{lw[0], lw[1]};
+    if ((lane & 7) == 0) alw[sh] = alpha;
+    // this block's V has landed (the loads issued after it are the next block's NKQ + VLD, when that block
+    // exists)
+    if (wave + (i + 1) * NW < nblk) __builtin_amdgcn_s_waitcnt((0x0F70 | ((NKQ + VLD) & 15)) | (((NKQ + VLD) >> 4) << 14));
+    else drain_stores();
+    const uint16_t* va = i & 1 ? va1 : va0;
+    const u4 ph = lds16(hc < GRP ? pbw + hc * WB + 8 * q4 : zrow + 8 * q4);
+    const u4 pl = lds16(hc < GRP ? pbw + (GRP + hc) * WB + 8 * q4 : zrow + 8 * q4);
+    const float sc = alw[hc & (GRP - 1)];
+    const int nvalid = jc1 - c0 - 8 * q4;  // this lane's rows 8(l/16) + v are valid while v < nvalid
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t ve[4][8];
+#pragma unroll
+      for (int dq = 0; dq < 4; ++dq) {
+        const int dcol = 16 * (4 * half + dq) + hc;
+        const uint16_t* vcol = va + (((dcol >> 3) ^ (2 * q4)) << 3) + (dcol & 7);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) ve[dq][v] = vcol[(8 * q4 + v) * DH];
+      }
+#pragma unroll
+      for (int dq = 0; dq < 4; ++dq) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int v2 = 0; v2 < 4; ++v2) {
+          const uint32_t e0 = 2 * v2 < nvalid ? ve[dq][2 * v2] : 0u;
+          const uint32_t e1 = 2 * v2 + 1 < nvalid ? ve[dq][2 * v2 + 1] : 0u;
+          wv[v2] = e0 | (e1 << 16);
+        }
+        const u4 av = {wv[0], wv[1], wv[2], wv[3]};
+        f4& o = oacc[4 * half + dq];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] *= sc;
+        o = mfma(av, ph, o);
+        o = mfma(av, pl, o);
+      }
+    }
+    // the block's LDS reads are complete before its areas are reused
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < NKQ; ++u) kc[u] = kx[u];
+    if (wave + (i + 2) * NW < nblk) {
+      load_k(i + 2, kx);
+      load_v(i + 2, i & 1 ? va1 : va0);
+    }
+  }
+  drain_stores();  // no direct V load is left in flight (the areas are reused below)
+  mark(a, t, 1);
+  // combine the waves: O[h][d] = sum_w exp(m_w - M) O_w[h][d], l = sum_w exp(m_w - M) l_w, M = max_w m_w
+  __syncthreads();
+  float* const ow = S.xs;                     // [NW][GRP][DH]
+  float* const mlw = S.xs + NW * GRP * DH;    // [NW][GRP] maxima, then [NW][GRP] sums
+  if (hc < GRP) {
+#pragma unroll
+    for (int db = 0; db < DH / 16; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ow[(wave * GRP + hc) * DH + 16 * db + 4 * q4 + e] = oacc[db][e];
+  }
+  if ((lane & 7) == 0) {
+    mlw[wave * GRP + sh] = m_run;
+    mlw[NW * GRP + wave * GRP + sh] = l_run;
+  }
+  __syncthreads();
+  static_assert(GRP * DH == 2 * NT, "two outputs per thread");
+  float o2[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * NT, h = i / DH, dd = i - h * DH;
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) M = fmaxf(M, mlw[q * GRP + h]);
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      const float mq = mlw[q * GRP + h];
+      const float wq = mq == -INFINITY ? 0.f : expf(mq - M);
+      o = fmaf(wq, ow[(q * GRP + h) * DH + dd], o);
+      L = fmaf(wq, mlw[NW * GRP + q * GRP + h], L);
+    }
+    o2[k] = o;
+    if (dd == 0) {
+      S.hm[h] = M;
+      S.hl[h] = L;
+    }
+  }
+  __syncthreads();
+  // the new token
+  if (has_new) {
     if (wave < GRP) {
       const int h = wave;
-      float M = -INFINITY;
-      for (int q = lane; q < nsplit; q += 64) M = fmaxf(M, wsc[h * nsplit + q]);
-      M = wave_max(M);
-      float Ls = 0.f;
-      for (int q = lane; q < nsplit; q += 64) {
-        const float mq = wsc[h * nsplit + q];
-        const float wq = mq == -INFINITY ? 0.f : expf(mq - M);
-        wsc[h * nsplit + q] = wq;
-        Ls = fmaf(lsc[h * nsplit + q], wq, Ls);
+      float sc = 0.f;
+      for (int i = lane; i < DH; i += 64) sc = fmaf(S.q[h * DH + i], S.kn[i], sc);
+      sc = wave_sum(sc);
+      if (lane == 0) {
+        const float mold = S.hm[h], mnew = fmaxf(mold, sc);
+        const float scl = mold == -INFINITY ? 0.f : expf(mold - mnew);
+        const float pn = expf(sc - mnew);
+        S.hscale[h] = scl;
+        S.pnew[h] = pn;
+        S.hl[h] = S.hl[h] * scl + pn;
+        S.hm[h] = mnew;
       }
-      Ls = wave_sum(Ls);
-      if (lane == 0) lsum[h] = Ls;
     }
     __syncthreads();
-    float o0 = 0.f, o1 = 0.f;
-    for (int q = 0; q < nsplit; q += MQ) {
-      if (q > 0) load_chunk(q);
 #pragma unroll
-      for (int u = 0; u < MQ; ++u) {
-        if (q + u < nsplit) {
-          o0 = fmaf(v0[u], wsc[h0 * nsplit + q + u], o0);
-          o1 = fmaf(v1[u], wsc[h1 * nsplit + q + u], o1);
-        }
-      }
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + k * NT, h = i / DH, dd = i - h * DH;
+      o2[k] = fmaf(S.pnew[h], S.vn[dd], o2[k] * S.hscale[h]);
     }
-    if (has0) pub(a.attn_o + (int64_t)b * a.Hq * DH + ((int64_t)g * GRP + h0) * DH + d0, o0 / lsum[h0]);
-    if (has1) pub(a.attn_o + (int64_t)b * a.Hq * DH + ((int64_t)g * GRP + h1) * DH + d1, o1 / lsum[h1]);
-    signal(a, w[W_SIG], w[W_SIGN]);
   }
+  float* part = a.apart + ((((int64_t)b * Hkv + g) * ATTN_MAX_SPLITS + s) * GRP) * (DH + 2);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * NT, h = i / DH, dd = i - h * DH;
+    pub(part + h * (DH + 2) + dd, o2[k]);
+  }
+  if (tid < GRP) {
+    pub(part + tid * (DH + 2) + DH, S.hm[tid]);
+    pub(part + tid * (DH + 2) + DH + 1, S.hl[tid]);
+  }
+  mark(a, t, 2);
+  attn_merge<DH, GRP>(a, w, t, b, g, nsplit, S);
 }
 
 template <class C>
 __device__ __forceinline__ void task_attn(KA& a, Desc w, int t, Lds& S) {
-  attn_split<C::DH, C::GRP>(a, w, t, S);
+  if constexpr (C::DH == 128 && C::GRP == 8) attn_split_w<C::DH, C::GRP>(a, w, t, S);
+  else attn_split<C::DH, C::GRP>(a, w, t, S);
 }
 
 // ------------------------------------------------------------------------------------------ the kernel
