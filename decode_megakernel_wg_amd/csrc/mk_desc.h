@@ -60,8 +60,11 @@ constexpr int DESC_WORDS = 32;
 // Tile sizes chosen by the planner (rows per task); the kernel reads r0/r1 from the descriptor.
 constexpr int ATTN_SPLIT_POS = 256;  // fewest positions per attention split
 constexpr int ATTN_TARGET_TASKS = 96;  // attention splits per layer the planner aims for (all sequences, KV groups)
-constexpr int ATTN_MAX_SPLIT_POS = 1024;  // most positions per split the planner chooses (before the split cap)
-constexpr int ATTN_MAX_SPLIT_PAGES = 256;  // pages one split may cover (its page list is staged in LDS)
+constexpr int ATTN_LONG_MIN_POS = 1024;  // positions per split from which long contexts aim at ATTN_LONG_TASKS
+constexpr int ATTN_LONG_TASKS = 256;     // attention splits per layer for long contexts (one per compute unit)
+constexpr int ATTN_MAX_SPLIT_POS = 4096;  // most positions per split the planner chooses (before the split cap)
+constexpr int ATTN_MAX_SPLIT_PAGES = 512;  // pages one split may cover (its page list is staged in LDS; the
+                                           // last split of a sequence also takes the growth since planning)
 constexpr int ATTN_MAX_SPLITS = 256;
 constexpr int SLOT_WORDS = 32;
 constexpr int LM_MAX_WG = 1024;  // most workgroups a launch may have (stride of the LM head's per-workgroup bests)  // routing table entry per expert slot: expert, token count, (token, rank, gate) x 8

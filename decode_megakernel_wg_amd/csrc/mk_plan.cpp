@@ -168,7 +168,8 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
   P->splits.assign(B, 1);
   // positions per attention split: ATTN_SPLIT_POS, more when the batch's contexts are long, so that a layer
   // has about ATTN_TARGET_TASKS splits over all sequences and KV groups (each split then streams several
-  // chunks, and the merge reads fewer partials), up to ATTN_MAX_SPLIT_POS (more splits beyond that)
+  // blocks, and the merge reads fewer partials); beyond ATTN_LONG_MIN_POS positions per split, about
+  // ATTN_LONG_TASKS splits, up to ATTN_MAX_SPLIT_POS positions each (more splits beyond that)
   // (splits cover the cached positions in whole 128-position chunks; the last one also takes the new token)
   int64_t total = 0;
   for (int b = 0; b < B; ++b) {
@@ -179,8 +180,12 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
     }
     total += std::max<int64_t>(len, 1);
   }
-  int64_t split_pos = (total * Hkv + ATTN_TARGET_TASKS / 2) / ATTN_TARGET_TASKS;
-  split_pos = std::max<int64_t>(ATTN_SPLIT_POS, std::min<int64_t>((split_pos + 64) / 128 * 128, ATTN_MAX_SPLIT_POS));
+  auto round128 = [](int64_t v) { return (v + 64) / 128 * 128; };
+  int64_t split_pos = std::max<int64_t>(ATTN_SPLIT_POS, round128((total * Hkv + ATTN_TARGET_TASKS / 2) / ATTN_TARGET_TASKS));
+  // long contexts: about one split per compute unit (ATTN_LONG_TASKS), each several thousand positions,
+  // which keeps the merges short and every wave streaming many blocks
+  if (split_pos > ATTN_LONG_MIN_POS)
+    split_pos = std::max<int64_t>(ATTN_LONG_MIN_POS, std::min<int64_t>(round128((total * Hkv + ATTN_LONG_TASKS / 2) / ATTN_LONG_TASKS), ATTN_MAX_SPLIT_POS));
   for (int b = 0; b < B; ++b) {
     const int64_t s = (std::max<int64_t>(batch->seq_lens[b], 1) + split_pos - 1) / split_pos;
     P->splits[b] = (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, ATTN_MAX_SPLITS));
