@@ -1347,10 +1347,11 @@ __device__ __forceinline__ void attn_merge(KA& a, Desc w, int t, int b, int g, i
   }
 }
 
-// Split s of (sequence b, KV group g) covers positions [j0, j1) of the sequence's 0..len window (len =
-// its prior length; position len is the new token, taken from this step's projections, RoPE'd, rounded
-// to BF16 and written to the cache by the split that holds it).  The split's page list and its first
-// chunk of K and V (128 positions) are loaded BEFORE the task waits for this step's queries.  Scores run
+// d_head 64 (the tiny shape; d_head 128 runs attn_split_w below): split s of (sequence b, KV group g)
+// covers positions [j0, j1) of the sequence's 0..len window (len = its prior length; position len is the
+// new token, taken from this step's projections, RoPE'd, rounded to BF16 and written to the cache by the
+// split that holds it).  The split's page list and its first two chunks of K and V (128 positions each)
+// are loaded BEFORE the task waits for this step's queries.  Scores run
 // on MFMA: each wave takes 16 positions of a chunk with K as the A operand (as stored) and the group's
 // RoPE'd, scaled queries as BF16 hi + lo B operands held in registers for the whole split.  After the
 // chunk's online softmax (one wave per head), each thread accumulates p * V for a 4-dim slice of its
@@ -1407,44 +1408,14 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
     const int ph = S.pages[(pos >> 4) - np0];
     return ph < 0 ? -1 : (((int64_t)ph * 2) * Hkv + g) * 16 * DH + (pos & 15) * DH;
   };
-  // K of the wave's 16 positions (64 bytes per lane); V in 4-dim slices.  d_head 128: in row quads (load u
-  // holds positions 4u..4u+3 of the wave, lane l 16-byte chunk 4(l/16) + l%4 of position (l%16)/4, so every
-  // four lanes read 64 contiguous bytes; see the GEMV core); d_head 64: the plain A-operand layout (16
-  // positions x 32 dims per load).
-  // d_head 128: every load instruction is issued whatever the positions (rows beyond the split read the
-  // layer's first cache row instead: their scores are replaced by -inf and their V rows zeroed where read),
-  // so that each chunk is exactly NKK K loads plus VLD V loads and the V waits below can count them.
-  constexpr int VLD = CH * DH * 2 / 16 / NT;  // 16-byte direct-to-LDS V loads per thread and chunk (4)
-  auto load_k = [&](int c0, u4 (&kk)[NKK]) {
-#pragma unroll
-    for (int u = 0; u < NKK; ++u) {
-      const int pos = c0 + 16 * wave + 4 * u + ((lane & 15) >> 2);
-      const int64_t base = pos < jc1 ? kv_base(pos) : -1;
-      kk[u] = __builtin_nontemporal_load(as_global(kvl + (base < 0 ? 0 : base) + 32 * (lane >> 4) + 8 * (lane & 3)));
-    }
-  };
-  // V of one chunk straight into LDS (no registers held): position row r (256 bytes) keeps its 16-byte
-  // chunks in swizzled slots, slot = chunk ^ 2((r >> 3) & 3), so that the P.V operand reads below (four rows
-  // 8 apart, 32 bytes each) fall in distinct banks
-  auto load_v = [&](int c0, float* buf) {
-#pragma unroll
-    for (int j = 0; j < VLD; ++j) {
-      const int n0 = (j * NW + wave) * 64, n = n0 + lane;
-      const int r = n >> 4, cg = (n & 15) ^ (2 * ((r >> 3) & 3));
-      const int pos = c0 + r;
-      const int64_t base = pos < jc1 ? kv_base(pos) : -1;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kvl + (base < 0 ? 0 : base) + vstride + cg * 8),
-                                       (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(buf) + n0 * 16), 16, 0, 0);
-    }
-  };
+  // K of the wave's 16 positions in the plain A-operand layout (16 positions x 32 dims per load); V in
+  // 4-dim slices
   auto load_chunk = [&](int c0, u4 (&kk)[NKK], u2 (&vv)[NP]) {
-    {
-      const int pos = c0 + 16 * wave + (lane & 15);
-      int64_t base = pos < jc1 ? kv_base(pos) : -1;
+    const int pos = c0 + 16 * wave + (lane & 15);
+    const int64_t kb = pos < jc1 ? kv_base(pos) : -1;
 #pragma unroll
-      for (int q = 0; q < NKK; ++q)
-        kk[q] = base >= 0 ? __builtin_nontemporal_load(as_global(kvl + base + 8 * (lane >> 4) + 32 * q)) : u4{0, 0, 0, 0};
-    }
+    for (int q = 0; q < NKK; ++q)
+      kk[q] = kb >= 0 ? __builtin_nontemporal_load(as_global(kvl + kb + 8 * (lane >> 4) + 32 * q)) : u4{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int pos = c0 + pp + PPP * i;
@@ -1454,19 +1425,9 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
   };
   u4 kc[NKK], kx[NKK];
   u2 vc[NP], vx[NP];
-  float* const vbuf0 = S.xs;         // d_head 128: V chunks, double-buffered (2 x 32 KB)
-  float* const vbuf1 = S.xs + XS_FLOATS / 2;
   // the split's first two chunks of old K/V stream while this step's projections are produced
-  if constexpr (DH == 128) {
-    static_assert(CH * DH * 2 <= XS_FLOATS * 2, "two V chunks in the staging area");
-    load_k(j0, kc);
-    load_v(j0, vbuf0);
-    load_k(j0 + CH, kx);
-    load_v(j0 + CH, vbuf1);
-  } else {
-    load_chunk(j0, kc, vc);
-    load_chunk(j0 + CH, kx, vx);
-  }
+  load_chunk(j0, kc, vc);
+  load_chunk(j0 + CH, kx, vx);
 
   wait_deps(a, w, 0, N_WAITS, t);
 
@@ -1523,79 +1484,34 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
     }
   }
   mark(a, t, 0);
-  // query operands.  d_head 128 (row quads): B column 4s + h holds head 4g + s of head group g at K-part h
-  // (chunk 4(l/16) + h of the head's vector); d_head 64: head j in column j, 32 dims per k-step.
-  constexpr int NHG = (GRP + 3) / 4;
+  // query operands: head j in column j, 32 dims per k-step
   u4 qh[NKK], ql[NKK];
-  if constexpr (DH == 128) {
 #pragma unroll
-    for (int hg = 0; hg < NHG; ++hg) {
-      const int hd = 4 * hg + ((lane & 15) >> 2);
-      qh[hg] = *reinterpret_cast<const u4*>(qb + hd * DH + 32 * (lane >> 4) + 8 * (lane & 3));
-      ql[hg] = *reinterpret_cast<const u4*>(qb + 16 * DH + hd * DH + 32 * (lane >> 4) + 8 * (lane & 3));
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < NKK; ++q) {
-      qh[q] = *reinterpret_cast<const u4*>(qb + (lane & 15) * DH + 8 * (lane >> 4) + 32 * q);
-      ql[q] = *reinterpret_cast<const u4*>(qb + 16 * DH + (lane & 15) * DH + 8 * (lane >> 4) + 32 * q);
-    }
+  for (int q = 0; q < NKK; ++q) {
+    qh[q] = *reinterpret_cast<const u4*>(qb + (lane & 15) * DH + 8 * (lane >> 4) + 32 * q);
+    ql[q] = *reinterpret_cast<const u4*>(qb + 16 * DH + (lane & 15) * DH + 8 * (lane >> 4) + 32 * q);
   }
   float o[GRP][DPT];
 #pragma unroll
   for (int h = 0; h < GRP; ++h)
 #pragma unroll
     for (int i = 0; i < DPT; ++i) o[h][i] = 0.f;
-  // d_head 128: P.V on the matrix cores, O^T[d][h] = sum over positions of V^T[d][pos] P^T[pos][h]: wave w
-  // owns dims 16w..16w+15 (A = V^T gathered from the staged chunk), heads are the 16 columns (B = the
-  // chunk's probabilities as BF16 hi + lo parts, [head][position] rows PBP apart; heads beyond the group
-  // read a zero row).  Lane l accumulates O^T[16w + 4(l/16) + i][l % 16].
-  constexpr int PBP = CH + 8;                                 // row pitch: the 16 head rows in distinct banks
-  static_assert((2 * GRP + 1) * PBP * 2 <= (int)sizeof(S.pt), "probability rows fit the probability area");
-  uint16_t* const pb = reinterpret_cast<uint16_t*>(S.pt);     // [hi: GRP rows][lo: GRP rows][zero row]
-  f4 oacc = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (DH == 128) {
-    for (int i = tid; i < PBP; i += NT) pb[2 * GRP * PBP + i] = 0;
-    __syncthreads();
-  }
-  int it = 0;
 
-  for (int c0 = j0; c0 < jc1; c0 += CH, ++it) {
-    if constexpr (DH == 128) {
-      // scores on MFMA in row quads: for position quad u and head group g, D[4r + h][4s + h] is position
-      // 4u + r times head 4g + s over K-part h (hi, then lo); the parts are added across each lane quad
+  for (int c0 = j0; c0 < jc1; c0 += CH) {
+    // scores on MFMA: D[position][head] = K (16 positions x 32 dims) times q^T (32 dims x heads), hi + lo
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < NKK; ++u) {
+    for (int q = 0; q < NKK; ++q) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, kc[q]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, qh[q]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, ql[q]), acc, 0, 0, 0);
+    }
+    if ((lane & 15) < GRP) {
+      const int h = lane & 15;
 #pragma unroll
-        for (int hg = 0; hg < NHG; ++hg) {
-          f4 acc = mfma(kc[u], qh[hg], f4{0.f, 0.f, 0.f, 0.f});
-          acc = mfma(kc[u], ql[hg], acc);
-          float v = pick4(acc, lane & 3);
-          v += dpp<0xB1>(v);
-          v += dpp<0x4E>(v);
-          const int hd = 4 * hg + ((lane >> 2) & 3);
-          if ((lane & 3) == 0 && hd < GRP) {
-            const int pl = 16 * wave + 4 * u + (lane >> 4);
-            S.sc[hd * CH + pl] = c0 + pl < jc1 ? v : -INFINITY;
-          }
-        }
-      }
-    } else {
-      // scores on MFMA: D[position][head] = K (16 positions x 32 dims) times q^T (32 dims x heads), hi + lo
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < NKK; ++q) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, kc[q]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, qh[q]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, ql[q]), acc, 0, 0, 0);
-      }
-      if ((lane & 15) < GRP) {
-        const int h = lane & 15;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int pl = 16 * wave + 4 * (lane >> 4) + r;
-          S.sc[h * CH + pl] = c0 + pl < jc1 ? acc[r] : -INFINITY;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int pl = 16 * wave + 4 * (lane >> 4) + r;
+        S.sc[h * CH + pl] = c0 + pl < jc1 ? acc[r] : -INFINITY;
       }
     }
     __syncthreads();
@@ -1616,13 +1532,7 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float pr = v[r] == -INFINITY ? 0.f : expf(v[r] - mnew);
-        if constexpr (DH == 128) {
-          const uint16_t ph = f2bf(pr);
-          pb[h * PBP + lane + 64 * r] = ph;
-          pb[(GRP + h) * PBP + lane + 64 * r] = f2bf(pr - bf2f(ph));
-        } else {
-          S.pt[(lane + 64 * r) * 8 + h] = pr;
-        }
+        S.pt[(lane + 64 * r) * 8 + h] = pr;
         ps += pr;
       }
       const float psum = wave_sum(ps);
@@ -1633,52 +1543,7 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
         S.hm[h] = mnew;
       }
     }
-    if constexpr (DH == 128) {
-      // this chunk's V has landed (the loads issued after it are the next chunk's NKK + VLD, when that chunk
-      // exists), in every wave before the barrier
-      static_assert(NKK + VLD < 16, "vmcnt field");
-      if (c0 + CH < jc1) __builtin_amdgcn_s_waitcnt(0x0F70 | (NKK + VLD));
-      else drain_stores();
-    }
     __syncthreads();
-    if constexpr (DH == 128) {
-      const int q4 = lane >> 4, hc = lane & 15, dcol = 16 * wave + hc;
-      const uint16_t* vb = reinterpret_cast<const uint16_t*>(it & 1 ? vbuf1 : vbuf0);
-      // element (r, dcol) of the chunk: row r, swizzled slot (dcol / 8) ^ 2((r >> 3) & 3); the rows read by
-      // lane l are 32ks + 8(l/16) + v, so (r >> 3) & 3 = l / 16
-      const uint16_t* vcol = vb + (((dcol >> 3) ^ (2 * q4)) << 3) + (dcol & 7);
-      const uint16_t* bh = hc < GRP ? pb + hc * PBP : pb + 2 * GRP * PBP;
-      const uint16_t* bl = hc < GRP ? pb + (GRP + hc) * PBP : pb + 2 * GRP * PBP;
-      const float sc = S.hscale[hc & (GRP - 1)];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[i] *= sc;
-      // every element of the chunk's four A operands is requested before any is packed
-      uint32_t ve[CH / 32][8];
-#pragma unroll
-      for (int ks = 0; ks < CH / 32; ++ks)
-#pragma unroll
-        for (int v = 0; v < 8; ++v) ve[ks][v] = vcol[(32 * ks + 8 * q4 + v) * DH];
-      u4 ph[CH / 32], pl[CH / 32];
-#pragma unroll
-      for (int ks = 0; ks < CH / 32; ++ks) {
-        ph[ks] = lds16(bh + 32 * ks + 8 * q4);
-        pl[ks] = lds16(bl + 32 * ks + 8 * q4);
-      }
-      const int nvalid = jc1 - c0 - 8 * q4;  // rows 32ks + 8(l/16) + v of this lane are valid while 32ks + v < nvalid
-#pragma unroll
-      for (int ks = 0; ks < CH / 32; ++ks) {
-        uint32_t wv[4];
-#pragma unroll
-        for (int v2 = 0; v2 < 4; ++v2) {
-          const uint32_t e0 = 32 * ks + 2 * v2 < nvalid ? ve[ks][2 * v2] : 0u;
-          const uint32_t e1 = 32 * ks + 2 * v2 + 1 < nvalid ? ve[ks][2 * v2 + 1] : 0u;
-          wv[v2] = e0 | (e1 << 16);
-        }
-        const u4 av = {wv[0], wv[1], wv[2], wv[3]};
-        oacc = mfma(av, ph[ks], oacc);
-        oacc = mfma(av, pl[ks], oacc);
-      }
-    } else {
 #pragma unroll
     for (int h = 0; h < GRP; ++h) {
       const float sc = S.hscale[h];
@@ -1699,23 +1564,14 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
 #pragma unroll
         for (int e = 0; e < DPT; ++e) o[h][e] = fmaf(pr[h], vf[e], o[h][e]);
     }
-    }
     __syncthreads();
     // rotate: the next chunk is in flight or has landed; request the one after it
 #pragma unroll
     for (int q = 0; q < NKK; ++q) kc[q] = kx[q];
-    if constexpr (DH == 128) {
-      if (c0 + 2 * CH < jc1) {
-        load_k(c0 + 2 * CH, kx);
-        load_v(c0 + 2 * CH, it & 1 ? vbuf1 : vbuf0);
-      }
-    } else {
 #pragma unroll
-      for (int i = 0; i < NP; ++i) vc[i] = vx[i];
-      if (c0 + 2 * CH < jc1) load_chunk(c0 + 2 * CH, kx, vx);
-    }
+    for (int i = 0; i < NP; ++i) vc[i] = vx[i];
+    if (c0 + 2 * CH < jc1) load_chunk(c0 + 2 * CH, kx, vx);
   }
-  if constexpr (DH == 128) drain_stores();  // no direct-to-LDS V load is left in flight (the area is reused)
   mark(a, t, 1);
   // the new token
   if (has_new) {
@@ -1735,12 +1591,6 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
       }
     }
     __syncthreads();
-    if constexpr (DH == 128) {
-      const int hc = lane & (GRP - 1), d0 = 16 * wave + 4 * (lane >> 4);
-      const float sc = S.hscale[hc], pn = S.pnew[hc];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[i] = fmaf(pn, S.vn[d0 + i], oacc[i] * sc);
-    } else {
 #pragma unroll
     for (int h = 0; h < GRP; ++h) {
       const float sc = S.hscale[h];
@@ -1752,17 +1602,8 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
         for (int e = 0; e < DPT; ++e) o[h][e] = fmaf(pn, S.vn[sl * DPT + e], o[h][e]);
       }
     }
-    }
   }
   float* part = a.apart + ((((int64_t)b * Hkv + g) * ATTN_MAX_SPLITS + s) * GRP) * (DH + 2);
-  if constexpr (DH == 128) {
-    // each lane holds final values: O[h][d] for h = l % 16 (< GRP), d = 16w + 4(l/16) + i
-    if ((lane & 15) < GRP) {
-      const int h = lane & 15, d0 = 16 * wave + 4 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pub(part + h * (DH + 2) + d0 + i, oacc[i]);
-    }
-  } else {
   // reduce the per-thread partial outputs over positions: lanes of one slice within the wave, then the
   // waves in order through LDS
 #pragma unroll
@@ -1788,7 +1629,6 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
 #pragma unroll
     for (int q = 0; q < NW; ++q) v += red[(q * GRP + h) * DH + dd];
     pub(part + h * (DH + 2) + dd, v);
-  }
   }
   if (tid < GRP) {
     pub(part + tid * (DH + 2) + DH, S.hm[tid]);
