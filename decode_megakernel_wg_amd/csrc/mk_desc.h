@@ -61,7 +61,7 @@ constexpr int DESC_WORDS = 32;
 constexpr int ATTN_SPLIT_POS = 256;  // fewest positions per attention split
 constexpr int ATTN_TARGET_TASKS = 96;  // attention splits per layer the planner aims for (all sequences, KV groups)
 constexpr int ATTN_LONG_MIN_POS = 1024;  // positions per split from which long contexts aim at ATTN_LONG_TASKS
-constexpr int ATTN_LONG_TASKS = 256;     // attention splits per layer for long contexts (one per compute unit)
+constexpr int ATTN_LONG_TASKS = 192;     // attention splits per layer for long contexts (measured best of 160-320)
 constexpr int ATTN_MAX_SPLIT_POS = 4096;  // most positions per split the planner chooses (before the split cap)
 constexpr int ATTN_MAX_SPLIT_PAGES = 512;  // pages one split may cover (its page list is staged in LDS; the
                                            // last split of a sequence also takes the growth since planning)

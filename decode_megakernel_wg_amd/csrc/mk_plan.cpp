@@ -182,8 +182,8 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
   }
   auto round128 = [](int64_t v) { return (v + 64) / 128 * 128; };
   int64_t split_pos = std::max<int64_t>(ATTN_SPLIT_POS, round128((total * Hkv + ATTN_TARGET_TASKS / 2) / ATTN_TARGET_TASKS));
-  // long contexts: about one split per compute unit (ATTN_LONG_TASKS), each several thousand positions,
-  // which keeps the merges short and every wave streaming many blocks
+  // long contexts: about ATTN_LONG_TASKS splits (three quarters of the compute units), each of thousands
+  // of positions, which keeps the merges short and every wave streaming many blocks
   if (split_pos > ATTN_LONG_MIN_POS)
     split_pos = std::max<int64_t>(ATTN_LONG_MIN_POS, std::min<int64_t>(round128((total * Hkv + ATTN_LONG_TASKS / 2) / ATTN_LONG_TASKS), ATTN_MAX_SPLIT_POS));
   for (int b = 0; b < B; ++b) {

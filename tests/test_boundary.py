@@ -193,12 +193,12 @@ def test_task_counts_full_model():
     assert ops[OP_ATTN] == 48 * 4 * 22
     attn = tasks[tasks[:, W_OP] == 4]
     assert (attn[:, W_R0] == 384).all() and (attn[:, W_D] == 22).all()
-    # long contexts: about one split per compute unit (256 per layer), at most 4096 positions each
-    for ctx, pos in ((65536, 1024), (131072, 2048), (262144, 4096)):
+    # long contexts: about 192 splits per layer (ctx x 4 / 192 positions rounded to 128), at most 4096 each
+    for ctx, pos in ((65536, 1408), (131072, 2688), (262144, 4096)):
         dl = desc_for(W.FULL, B=1, pages=ctx // 16 + 64, n_pages=ctx // 16 + 64)
         tl, _ = mk.mk_plan_tasks(dl, [ctx])
         al = tl[(tl[:, W_OP] == 4) & (tl[:, 1] == 0)]
-        assert (al[:, W_R0] == pos).all() and len(al) == 4 * ctx // pos
+        assert (al[:, W_R0] == pos).all() and len(al) == 4 * -(-ctx // pos)
     # expert up-projection tiles: 48 gate + 48 up rows at batches of 1-2 (16 tiles per expert), 64 + 64 above
     up = tasks[tasks[:, W_OP] == 5]
     assert ops[5] == 48 * 8 * 16 and ((up[:, W_R1] - up[:, W_R0]) == 48).all()
