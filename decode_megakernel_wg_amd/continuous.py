@@ -24,10 +24,10 @@ from . import mk
 
 class ContinuousSession:
     def __init__(self, shape: W.Shape, n_steps: int, model: W.DeviceModel | None = None, device="cuda", lo=CB.PREFIX_LO,
-                 hi=CB.PREFIX_HI, n_pages=None, router_bias=None):
+                 hi=CB.PREFIX_HI, n_pages=None, router_bias=None, mean_gap=CB.MEAN_GAP):
         self.shape = s = shape
         self.dev = torch.device(device)
-        self.steps, self.seqs, self.n_pages, self.max_pages = CB.schedule(n_steps, n_pages, lo, hi)
+        self.steps, self.seqs, self.n_pages, self.max_pages = CB.schedule(n_steps, n_pages, lo, hi, mean_gap=mean_gap)
         self.model = model if model is not None else W.DeviceModel(s, device)
         m = self.model
         self.kv = torch.zeros(s.n_layers, self.n_pages, 2, s.n_kv_heads, W.PAGE, s.d_head, dtype=torch.bfloat16, device=self.dev)

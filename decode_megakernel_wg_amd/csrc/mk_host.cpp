@@ -63,7 +63,7 @@ struct mk_model {
   double* rpart = nullptr;
   float *rlogits = nullptr, *route_gate = nullptr, *h = nullptr, *ypart = nullptr, *lmbest_v = nullptr, *dump_n = nullptr;
   int32_t *route_sel = nullptr, *lmbest_i = nullptr, *next_tok = nullptr, *slots = nullptr;
-  uint32_t *task_done = nullptr, *ctr_snapshot = nullptr;
+  uint32_t *task_done = nullptr, *ctr_snapshot = nullptr, *pagewalk = nullptr;
   uint64_t* ts = nullptr;
   // task list
   mk::Plan plan;
@@ -247,17 +247,23 @@ static void derive_phases(mk_model* m, const int32_t* q, int64_t n) {
 }
 
 // Copy the task list to the pinned staging buffer (list order) and derive its phases for grids of two or
-// more workgroups.
+// more workgroups.  MK_DBG_DROP_SIGNAL removes the completion signal of the first QKV task (watchdog test).
 static void lay_out_queues(mk_model* m) {
   const mk::Plan& P = m->plan;
   std::memcpy(m->staging, P.desc.data(), P.desc.size() * sizeof(int32_t));
+  if (m->dbg & MK_DBG_DROP_SIGNAL)
+    for (int64_t i = 0; i < P.n_tasks(); ++i)
+      if (m->staging[i * mk::DESC_WORDS + mk::W_OP] == mk::OP_QKV) {
+        m->staging[i * mk::DESC_WORDS + mk::W_SIG] = -1;
+        break;
+      }
   m->ph_on = 0;
   if (m->grid >= 2) derive_phases(m, m->staging, P.n_tasks());
   m->uploaded_grid = m->grid;
 }
 
-int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* page_tables, void* kv_pages,
-                   float* logits_out, void* stream) {
+static int launch_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* first_of, const int32_t* page_tables,
+                       void* kv_pages, float* logits_out, void* stream) {
   if (!m) return fail(MK_E_INVAL, "null handle");
   if (!m->have_plan) return fail(MK_E_STATE, "mk_build_tasks has not been called");
   if (!tokens || !seq_lens || !page_tables || !kv_pages || !logits_out) return fail(MK_E_INVAL, "null step pointer");
@@ -273,6 +279,8 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   }
   if (m->task_done) HIPCHK(hipMemsetAsync(m->task_done, 0, sizeof(uint32_t) * P.n_tasks(), s));
   if (m->ts && (m->dbg & MK_DBG_TIMESTAMPS)) HIPCHK(hipMemsetAsync(m->ts, 0, sizeof(uint64_t) * 8 * P.n_tasks(), s));
+  if (m->pagewalk && (m->dbg & MK_DBG_PAGE_WALK))
+    HIPCHK(hipMemsetAsync(m->pagewalk, 0, sizeof(uint32_t) * 4 * m->desc.n_layers * P.B * m->desc.n_kv_heads, s));
   const mk_model_desc& D = m->desc;
   mk::KArgs a{};
   a.L = D.n_layers;
@@ -309,6 +317,7 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   a.inv_freq = m->inv_freq;
   a.tokens = tokens;
   a.seq_lens = seq_lens;
+  a.first_of = first_of;
   a.page_tables = page_tables;
   a.kv = (uint16_t*)kv_pages;
   a.logits = logits_out;
@@ -336,9 +345,22 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
   a.task_done = m->task_done;
   a.ts = (m->dbg & MK_DBG_TIMESTAMPS) ? m->ts : nullptr;
   a.ctr_snapshot = m->ctr_snapshot;
+  a.pagewalk = (m->dbg & MK_DBG_PAGE_WALK) ? m->pagewalk : nullptr;
+  a.spin_limit = (m->dbg & MK_DBG_DROP_SIGNAL) ? (1u << 12) : (1u << 21);
   HIPCHK(mk_launch_persistent(&a, m->kclass, m->grid, (m->dbg & MK_DBG_WIDE_GEMV) ? 1 : 0, s));
   m->stepped = true;
   return MK_OK;
+}
+
+int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* page_tables, void* kv_pages,
+                   float* logits_out, void* stream) {
+  return launch_step(m, tokens, seq_lens, nullptr, page_tables, kv_pages, logits_out, stream);
+}
+
+int mk_mixed_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* first_of, const int32_t* page_tables,
+                  void* kv_pages, float* logits_out, void* stream) {
+  if (!first_of) return fail(MK_E_INVAL, "null first_of");
+  return launch_step(m, tokens, seq_lens, first_of, page_tables, kv_pages, logits_out, stream);
 }
 
 int mk_next_tokens(mk_model* m, int32_t** dev_ptr) {
@@ -376,6 +398,11 @@ int mk_debug_set(mk_model* m, uint32_t flags) {
     int rc = m->alloc(&m->ts, (size_t)m->max_tasks * 8);
     if (rc) return rc;
   }
+  if ((flags & MK_DBG_PAGE_WALK) && !m->pagewalk) {
+    int rc = m->alloc(&m->pagewalk, (size_t)4 * m->desc.n_layers * m->desc.max_batch * m->desc.n_kv_heads);
+    if (rc) return rc;
+  }
+  if ((flags ^ m->dbg) & MK_DBG_DROP_SIGNAL) m->dirty = true;  // the uploaded task list changes
   m->dbg = flags;
   return MK_OK;
 }
@@ -408,6 +435,12 @@ int mk_debug_read(mk_model* m, int kind, void* host_dst, int64_t bytes) {
       src = m->ts;
       avail = m->plan.n_tasks() * 64;
       break;
+    case MK_DBGK_PAGE_WALK:
+      if (!(m->dbg & MK_DBG_PAGE_WALK)) return fail(MK_E_STATE, "MK_DBG_PAGE_WALK is not enabled");
+      src = m->pagewalk;
+      avail = L * B * D.n_kv_heads * 16;
+      break;
+    case MK_DBGK_SLOTS: src = m->slots; avail = L * m->plan.n_slots * mk::SLOT_WORDS * 4; break;
     default: return fail(MK_E_INVAL, "unknown debug kind");
   }
   if (bytes > avail) return fail(MK_E_RANGE, "request larger than the debug buffer");

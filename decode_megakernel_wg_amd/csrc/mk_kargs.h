@@ -43,6 +43,9 @@ struct KArgs {
   // this step's inputs and outputs (caller-owned device memory)
   const int32_t* tokens;
   const int32_t* seq_lens;
+  // [B] or null: first batch entry of each entry's sequence in this step (a chunk of consecutive positions of
+  // one sequence, prefill); null = every entry is its own sequence (decode)
+  const int32_t* first_of;
   const int32_t* page_tables;
   uint16_t* kv;
   float* logits;
@@ -71,6 +74,9 @@ struct KArgs {
   uint32_t* task_done;     // [n_tasks] or null
   uint64_t* ts;            // [n_tasks][8] (claim, dependencies met, end, hardware id, 4 sub-phase marks) or null
   uint32_t* ctr_snapshot;  // [n_counters] or null
+  uint32_t* pagewalk;      // [L][B][Hkv][4] or null: cache pages read, sum of (logical page + 1) * physical page
+                           // (mod 2^32), positions attended, written slot (physical page * 16 + slot)
+  uint32_t spin_limit;     // polls a dependency wait makes before it reports a time-out
 };
 
 }  // namespace mk

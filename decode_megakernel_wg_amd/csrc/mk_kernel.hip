@@ -34,7 +34,6 @@ constexpr int NW = NT / 64;      // waves per workgroup
 constexpr int XS_FLOATS = 16384; // 64 KB LDS staging area (fp32 activations, attention scratch)
 constexpr int XBP = 2048 + 32;    // bf16 row pitch of the split activations (rows 64 bytes apart modulo the bank window)
 constexpr int NKP = 16;           // GEMV loads (16 bytes per lane) per pass and wave
-constexpr uint32_t SPIN_LIMIT = 1u << 21;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
@@ -164,14 +163,16 @@ __device__ __forceinline__ void raise_error(KA& a, uint32_t code, int task) {
   __hip_atomic_store(&a.err[ERR_ABORT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0 spins until counter c reaches target (or the step is aborted); returns the value it saw.
+// Thread 0 spins until counter c reaches target (or the step is aborted); returns the value it saw.  After
+// a.spin_limit polls (about 0.4 us each) the wait reports a time-out and aborts the step: every other wait
+// then returns at its next abort check, so every workgroup still runs out its task list and exits.
 __device__ __forceinline__ uint32_t spin_ge(KA& a, int32_t c, int32_t target, int task) {
   if (c < 0) return 0u;
   uint32_t n = 0, v;
   while ((v = __hip_atomic_load(&a.ctr[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < (uint32_t)target) {
     if ((++n & 63) == 0) {
       if (__hip_atomic_load(&a.err[ERR_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return 0u;
-      if (n > SPIN_LIMIT) {
+      if (n > a.spin_limit) {
         raise_error(a, ERRC_TIMEOUT, task);
         return 0u;
       }
@@ -1279,6 +1280,53 @@ __device__ __forceinline__ void lm_phase(KA& a, Lds& S) {
 }
 
 // ------------------------------------------------------------------------------------------ attention
+// Batch entry j's new key (RoPE at its position, from the angles task_embed computed) and value of KV group
+// g, both rounded to BF16 as the cache stores them, into S.kn / S.vn.
+template <int DH, int GRP>
+__device__ __forceinline__ void stage_new_kv(KA& a, int j, int g, Lds& S) {
+  const float* src = a.qkv + ((int64_t)j * a.Hkv + g) * (GRP + 2) * DH;
+  const float* cs = a.rope_cs + (int64_t)j * (DH / 2) * 2;
+  for (int i = tidx(); i < DH / 2; i += NT) {
+    const float c = cs[2 * i], sn = cs[2 * i + 1];
+    const float x0 = src[GRP * DH + i], x1 = src[GRP * DH + i + DH / 2];
+    S.kn[i] = bf2f(f2bf(x0 * c - x1 * sn));
+    S.kn[i + DH / 2] = bf2f(f2bf(x0 * sn + x1 * c));
+  }
+  for (int i = tidx(); i < DH; i += NT) S.vn[i] = bf2f(f2bf(src[(GRP + 1) * DH + i]));
+}
+
+// Where the step's entry b reads the cache.  Entries b0..b of a chunk (consecutive positions of one sequence
+// in one step, prefill: first_of[b] = b0) all read the cached positions [0, len0), len0 being the position of
+// the chunk's first token, and take the keys and values of positions len0..len from this step's projections
+// (the cache slots of those positions are written in this same step).  A decode entry is a chunk of one.
+struct SeqView {
+  int len;   // the entry's own position (its query's RoPE position, the slot its K/V are written to)
+  int b0;    // first entry of its chunk
+  int len0;  // cached positions read: [0, len0)
+};
+__device__ __forceinline__ SeqView seq_view(KA& a, int b, int t) {
+  SeqView v;
+  v.len = a.seq_lens[b];
+  if (v.len < 0 || v.len / 16 >= a.max_pages) {
+    if (tidx() == 0) raise_error(a, ERRC_SEQLEN, t);
+    v.len = 0;
+  }
+  v.b0 = a.first_of ? a.first_of[b] : b;
+  v.len0 = v.len - (b - v.b0);
+  if (v.b0 < 0 || v.b0 > b || v.len0 < 0 || a.seq_lens[v.b0] != v.len0) {  // not a chunk of consecutive positions
+    if (tidx() == 0) raise_error(a, ERRC_SEQLEN, t);
+    v.b0 = b;
+    v.len0 = v.len;
+  }
+  return v;
+}
+
+// Debug page-walk record of (layer, entry, KV group): pages read (npg from logical page np0), positions
+// attended; all additions are modulo 2^32 and commutative, so the splits' order does not matter.
+__device__ __forceinline__ uint32_t* walk_rec(KA& a, int l, int b, int g) {
+  return a.pagewalk ? a.pagewalk + (((int64_t)l * a.B + b) * a.Hkv + g) * 4 : nullptr;
+}
+
 // The last split of (b, g) to finish merges all splits (log-sum-exp) and publishes the group's output.
 template <int DH, int GRP>
 __device__ __forceinline__ void attn_merge(KA& a, Desc w, int t, int b, int g, int nsplit, Lds& S) {
@@ -1370,20 +1418,15 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
   const int tid = tidx(), wave = tid >> 6, lane = tid & 63;
   const int sl = tid % SL, pp = tid / SL;
   const int Hkv = a.Hkv;
-  int len = a.seq_lens[b];
-  if (len < 0 || len / 16 >= a.max_pages) {
-    if (tid == 0) raise_error(a, ERRC_SEQLEN, t);
-    len = 0;
-  }
-  const int npos = len + 1;
-  // the planner cuts the cached positions [0, len) into splits of w[W_R0] positions (whole 128-position
+  const SeqView sv = seq_view(a, b, t);
+  const int len = sv.len, len0 = sv.len0, b0 = sv.b0;
+  // the planner cuts the cached positions [0, len0) into splits of w[W_R0] positions (whole 128-position
   // chunks, fixed for the task list's life); the last split takes the rest of the cached positions (a
-  // context that grew since planning adds to it) and the new token (position len)
+  // context that grew since planning adds to it) and the new positions len0..len
   const int chunk = w[W_R0];
   const bool last = s == nsplit - 1;
-  const int j0 = chunk > 0 ? (int)min<int64_t>((int64_t)s * chunk, len) : 0;
-  const int j1 = last ? npos : min(j0 + chunk, len);
-  int jc1 = min(j1, len);  // cached positions end
+  const int j0 = chunk > 0 ? (int)min<int64_t>((int64_t)s * chunk, len0) : 0;
+  int jc1 = last ? len0 : min(j0 + chunk, len0);  // cached positions end
   if (chunk <= 0 || chunk % CH != 0 || jc1 - j0 > ATTN_MAX_SPLIT_PAGES * 16) {  // bad descriptor, or lengths
     if (tid == 0) raise_error(a, ERRC_SEQLEN, t);                                  // far beyond the plan
     jc1 = j0;
@@ -1392,6 +1435,7 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
   const int32_t* ptab = a.page_tables + (int64_t)b * a.max_pages;
   uint16_t* kvl = a.kv + (int64_t)l * a.n_pages * 2 * Hkv * 16 * DH;
   const int64_t vstride = (int64_t)Hkv * 16 * DH;
+  uint32_t* const pw = walk_rec(a, l, b, g);
 
   // page list of the split
   const int np0 = j0 >> 4, npg = jc1 > j0 ? ((jc1 - 1) >> 4) - np0 + 1 : 0;
@@ -1402,6 +1446,11 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
       ph = -1;
     }
     S.pages[i] = ph;
+    if (pw) atomicAdd(pw + 1, (uint32_t)(np0 + i + 1) * (uint32_t)ph);
+  }
+  if (pw && tid == 0) {
+    atomicAdd(pw + 0, (uint32_t)npg);
+    atomicAdd(pw + 2, (uint32_t)(jc1 - j0 + (has_new ? b - b0 + 1 : 0)));
   }
   __syncthreads();
   auto kv_base = [&](int pos) -> int64_t {
@@ -1457,21 +1506,13 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
     qb[16 * DH + h * DH + j] = f2bf(y0 - bf2f(h0));
     qb[16 * DH + h * DH + j + DH / 2] = f2bf(y1 - bf2f(h1));
   }
-  if (has_new) {
-    for (int j = tid; j < DH / 2; j += NT) {
-      const float c = cs[2 * j], sn = cs[2 * j + 1];
-      const float x0 = qsrc[GRP * DH + j], x1 = qsrc[GRP * DH + j + DH / 2];
-      S.kn[j] = bf2f(f2bf(x0 * c - x1 * sn));
-      S.kn[j + DH / 2] = bf2f(f2bf(x0 * sn + x1 * c));
-    }
-    for (int j = tid; j < DH; j += NT) S.vn[j] = bf2f(f2bf(qsrc[(GRP + 1) * DH + j]));
-  }
+  if (has_new) stage_new_kv<DH, GRP>(a, b, g, S);
   if (tid < GRP) {
     S.hm[tid] = -INFINITY;
     S.hl[tid] = 0.f;
   }
   __syncthreads();
-  if (has_new) {  // the new token's K/V go to the cache slot of position len (layer l)
+  if (has_new) {  // this entry's K/V go to the cache slot of position len (layer l)
     const int ph = ptab[len >> 4];
     if (ph >= 0 && ph < a.n_pages) {
       const int64_t base = (((int64_t)ph * 2) * Hkv + g) * 16 * DH + (len & 15) * DH;
@@ -1479,6 +1520,7 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
         kvl[base + j] = f2bf(S.kn[j]);
         kvl[base + vstride + j] = f2bf(S.vn[j]);
       }
+      if (pw && tid == 0) pw[3] = 1u + (uint32_t)ph * 16u + (uint32_t)(len & 15);
     } else if (tid == 0) {
       raise_error(a, ERRC_PAGE, t);
     }
@@ -1573,33 +1615,40 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
     if (c0 + 2 * CH < jc1) load_chunk(c0 + 2 * CH, kx, vx);
   }
   mark(a, t, 1);
-  // the new token
+  // the new positions len0..len, one at a time (entries b0..b; a decode entry has only its own)
   if (has_new) {
-    if (wave < GRP) {
-      const int h = wave;
-      float sc = 0.f;
-      for (int i = lane; i < DH; i += 64) sc = fmaf(S.q[h * DH + i], S.kn[i], sc);
-      sc = wave_sum(sc);
-      if (lane == 0) {
-        const float mold = S.hm[h], mnew = fmaxf(mold, sc);
-        const float scl = mold == -INFINITY ? 0.f : expf(mold - mnew);
-        const float pn = expf(sc - mnew);
-        S.hscale[h] = scl;
-        S.pnew[h] = pn;
-        S.hl[h] = S.hl[h] * scl + pn;
-        S.hm[h] = mnew;
+    for (int j = b0; j <= b; ++j) {
+      if (b0 != b) {  // a chunk: entry j's key and value (S.kn / S.vn held the previous one)
+        __syncthreads();
+        stage_new_kv<DH, GRP>(a, j, g, S);
+        __syncthreads();
       }
-    }
-    __syncthreads();
+      if (wave < GRP) {
+        const int h = wave;
+        float sc = 0.f;
+        for (int i = lane; i < DH; i += 64) sc = fmaf(S.q[h * DH + i], S.kn[i], sc);
+        sc = wave_sum(sc);
+        if (lane == 0) {
+          const float mold = S.hm[h], mnew = fmaxf(mold, sc);
+          const float scl = mold == -INFINITY ? 0.f : expf(mold - mnew);
+          const float pn = expf(sc - mnew);
+          S.hscale[h] = scl;
+          S.pnew[h] = pn;
+          S.hl[h] = S.hl[h] * scl + pn;
+          S.hm[h] = mnew;
+        }
+      }
+      __syncthreads();
 #pragma unroll
-    for (int h = 0; h < GRP; ++h) {
-      const float sc = S.hscale[h];
+      for (int h = 0; h < GRP; ++h) {
+        const float sc = S.hscale[h];
 #pragma unroll
-      for (int e = 0; e < DPT; ++e) o[h][e] *= sc;
-      if (pp == 0) {
-        const float pn = S.pnew[h];
+        for (int e = 0; e < DPT; ++e) o[h][e] *= sc;
+        if (pp == 0) {
+          const float pn = S.pnew[h];
 #pragma unroll
-        for (int e = 0; e < DPT; ++e) o[h][e] = fmaf(pn, S.vn[sl * DPT + e], o[h][e]);
+          for (int e = 0; e < DPT; ++e) o[h][e] = fmaf(pn, S.vn[sl * DPT + e], o[h][e]);
+        }
       }
     }
   }
@@ -1658,19 +1707,15 @@ __device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
   const int l = w[W_LAYER], b = w[W_A], g = w[W_B], s = w[W_C], nsplit = w[W_D];
   const int tid = tidx(), wave = tid >> 6, lane = tid & 63;
   const int Hkv = a.Hkv;
-  int len = a.seq_lens[b];
-  if (len < 0 || len / 16 >= a.max_pages) {
-    if (tid == 0) raise_error(a, ERRC_SEQLEN, t);
-    len = 0;
-  }
-  // the planner cuts the cached positions [0, len) into splits of w[W_R0] positions (whole 128-position
+  const SeqView sv = seq_view(a, b, t);
+  const int len = sv.len, len0 = sv.len0, b0 = sv.b0;
+  // the planner cuts the cached positions [0, len0) into splits of w[W_R0] positions (whole 128-position
   // chunks, fixed for the task list's life); the last split takes the rest of the cached positions (a
-  // context that grew since planning adds to it) and the new token (position len)
+  // context that grew since planning adds to it) and the new positions len0..len
   const int chunk = w[W_R0];
   const bool last = s == nsplit - 1;
-  const int j0 = chunk > 0 ? (int)min<int64_t>((int64_t)s * chunk, len) : 0;
-  const int j1 = last ? len + 1 : min(j0 + chunk, len);
-  int jc1 = min(j1, len);  // cached positions end
+  const int j0 = chunk > 0 ? (int)min<int64_t>((int64_t)s * chunk, len0) : 0;
+  int jc1 = last ? len0 : min(j0 + chunk, len0);  // cached positions end
   if (chunk <= 0 || chunk % 128 != 0 || jc1 - j0 > ATTN_MAX_SPLIT_PAGES * 16) {
     if (tid == 0) raise_error(a, ERRC_SEQLEN, t);
     jc1 = j0;
@@ -1679,6 +1724,7 @@ __device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
   const int32_t* ptab = a.page_tables + (int64_t)b * a.max_pages;
   uint16_t* kvl = a.kv + (int64_t)l * a.n_pages * 2 * Hkv * 16 * DH;
   const int64_t vstride = (int64_t)Hkv * 16 * DH;
+  uint32_t* const pw = walk_rec(a, l, b, g);
 
   // page list of the split
   const int np0 = j0 >> 4, npg = jc1 > j0 ? ((jc1 - 1) >> 4) - np0 + 1 : 0;
@@ -1689,6 +1735,11 @@ __device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
       ph = -1;
     }
     S.pages[i] = ph;
+    if (pw) atomicAdd(pw + 1, (uint32_t)(np0 + i + 1) * (uint32_t)ph);
+  }
+  if (pw && tid == 0) {
+    atomicAdd(pw + 0, (uint32_t)npg);
+    atomicAdd(pw + 2, (uint32_t)(jc1 - j0 + (has_new ? b - b0 + 1 : 0)));
   }
   if (tid == 0) S.xb_layer = 0;  // the V areas overwrite the staged GEMV input
   __syncthreads();
@@ -1759,18 +1810,10 @@ __device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
     qb[16 * DH + h * DH + j] = f2bf(y0 - bf2f(h0));
     qb[16 * DH + h * DH + j + DH / 2] = f2bf(y1 - bf2f(h1));
   }
-  if (has_new) {
-    for (int j = tid; j < DH / 2; j += NT) {
-      const float c = cs[2 * j], sn = cs[2 * j + 1];
-      const float x0 = qsrc[GRP * DH + j], x1 = qsrc[GRP * DH + j + DH / 2];
-      S.kn[j] = bf2f(f2bf(x0 * c - x1 * sn));
-      S.kn[j + DH / 2] = bf2f(f2bf(x0 * sn + x1 * c));
-    }
-    for (int j = tid; j < DH; j += NT) S.vn[j] = bf2f(f2bf(qsrc[(GRP + 1) * DH + j]));
-  }
+  if (has_new) stage_new_kv<DH, GRP>(a, b, g, S);
   for (int i = tid; i < 32; i += NT) S.sc[i] = 0.f;  // zero B rows for the heads beyond the group
   __syncthreads();
-  if (has_new) {  // the new token's K/V go to the cache slot of position len (layer l)
+  if (has_new) {  // this entry's K/V go to the cache slot of position len (layer l)
     const int ph = ptab[len >> 4];
     if (ph >= 0 && ph < a.n_pages) {
       const int64_t base = (((int64_t)ph * 2) * Hkv + g) * 16 * DH + (len & 15) * DH;
@@ -1778,6 +1821,7 @@ __device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
         kvl[base + j] = f2bf(S.kn[j]);
         kvl[base + vstride + j] = f2bf(S.vn[j]);
       }
+      if (pw && tid == 0) pw[3] = 1u + (uint32_t)ph * 16u + (uint32_t)(len & 15);
     } else if (tid == 0) {
       raise_error(a, ERRC_PAGE, t);
     }
@@ -1940,28 +1984,35 @@ __device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
     }
   }
   __syncthreads();
-  // the new token
+  // the new positions len0..len, one at a time (entries b0..b; a decode entry has only its own)
   if (has_new) {
-    if (wave < GRP) {
-      const int h = wave;
-      float sc = 0.f;
-      for (int i = lane; i < DH; i += 64) sc = fmaf(S.q[h * DH + i], S.kn[i], sc);
-      sc = wave_sum(sc);
-      if (lane == 0) {
-        const float mold = S.hm[h], mnew = fmaxf(mold, sc);
-        const float scl = mold == -INFINITY ? 0.f : expf(mold - mnew);
-        const float pn = expf(sc - mnew);
-        S.hscale[h] = scl;
-        S.pnew[h] = pn;
-        S.hl[h] = S.hl[h] * scl + pn;
-        S.hm[h] = mnew;
+    for (int j = b0; j <= b; ++j) {
+      if (b0 != b) {  // a chunk: entry j's key and value (S.kn / S.vn held the previous one)
+        __syncthreads();
+        stage_new_kv<DH, GRP>(a, j, g, S);
+        __syncthreads();
       }
-    }
-    __syncthreads();
+      if (wave < GRP) {
+        const int h = wave;
+        float sc = 0.f;
+        for (int i = lane; i < DH; i += 64) sc = fmaf(S.q[h * DH + i], S.kn[i], sc);
+        sc = wave_sum(sc);
+        if (lane == 0) {
+          const float mold = S.hm[h], mnew = fmaxf(mold, sc);
+          const float scl = mold == -INFINITY ? 0.f : expf(mold - mnew);
+          const float pn = expf(sc - mnew);
+          S.hscale[h] = scl;
+          S.pnew[h] = pn;
+          S.hl[h] = S.hl[h] * scl + pn;
+          S.hm[h] = mnew;
+        }
+      }
+      __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = tid + k * NT, h = i / DH, dd = i - h * DH;
-      o2[k] = fmaf(S.pnew[h], S.vn[dd], o2[k] * S.hscale[h]);
+      for (int k = 0; k < 2; ++k) {
+        const int i = tid + k * NT, h = i / DH, dd = i - h * DH;
+        o2[k] = fmaf(S.pnew[h], S.vn[dd], o2[k] * S.hscale[h]);
+      }
     }
   }
   float* part = a.apart + ((((int64_t)b * Hkv + g) * ATTN_MAX_SPLITS + s) * GRP) * (DH + 2);

@@ -3,12 +3,13 @@
 // The step's graph is expressed as per-tile tasks in topological order, the way the pages describe the
 // task list: each task is one operation on one tile, and dependencies are counters, not kernel
 // boundaries (agenticcommons.xyz "Cohere North Mini Code megakernel serving engine", section
-// Megakernel 的運作方式).  Per layer the order is
-//   ROUTER, QKV, ATTN, UP, OPROJ, DOWN, RESID
-// so that workgroups claiming the next layer's router and QKV tasks start their weight loads while the
-// current layer's tail still runs (same page, section 三個實際的加速來源, item 3: router and QKV weights
-// are prefetched most aggressively, from the previous layer's O-proj tail), attention and MoE tasks of
-// one layer interleave to backfill idle compute units (item 1, parallel layer), and each KV group's
+// Megakernel 的運作方式).  The list is the embedding row tiles, then per layer
+//   QKV tiles, ATTN splits, expert UP tiles, OPROJ tiles, expert DOWN tiles
+// (the router is the residual epilogue's last row tile, the residual add the epilogue of the last O-proj or
+// down-projection task of a row tile, and the LM head the kernel's closing phase: none of them is a task).
+// Workgroups take the next layer's QKV, attention and up-projection tiles and start their weight (and old
+// K/V) loads while the current layer's tail still runs (same page, section 三個實際的加速來源, item 3), the
+// attention and MoE tasks of one layer share all compute units (item 1, parallel layer), and each KV group's
 // O-proj waits only on that group's attention and each expert's down projection only on its own up
 // projection (item 2, false dependencies).
 #include "mk_plan.h"
@@ -171,6 +172,9 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
   // blocks, and the merge reads fewer partials); beyond ATTN_LONG_MIN_POS positions per split, about
   // ATTN_LONG_TASKS splits, up to ATTN_MAX_SPLIT_POS positions each (more splits beyond that)
   // (splits cover the cached positions in whole 128-position chunks; the last one also takes the new token)
+  // cached positions each entry's attention reads: its own length, or for an entry of a chunk (first_of) the
+  // position of the chunk's first token (the chunk's own positions come from the step's projections)
+  std::vector<int64_t> cached(B);
   int64_t total = 0;
   for (int b = 0; b < B; ++b) {
     const int32_t len = batch->seq_lens[b];
@@ -178,7 +182,14 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
       *msg = "sequence length negative or beyond max_pages_per_seq";
       return MK_E_INVAL;
     }
-    total += std::max<int64_t>(len, 1);
+    const int32_t f = batch->first_of ? batch->first_of[b] : b;
+    if (f < 0 || f > b || (f != b && (batch->first_of[f] != f || batch->first_of[b - 1] != f)) ||
+        (int64_t)len != (int64_t)batch->seq_lens[f] + (b - f)) {
+      *msg = "first_of: entry " + std::to_string(b) + " is not part of a run of consecutive positions of one sequence";
+      return MK_E_INVAL;
+    }
+    cached[b] = batch->seq_lens[f];
+    total += std::max<int64_t>(cached[b], 1);
   }
   auto round128 = [](int64_t v) { return (v + 64) / 128 * 128; };
   int64_t split_pos = std::max<int64_t>(ATTN_SPLIT_POS, round128((total * Hkv + ATTN_TARGET_TASKS / 2) / ATTN_TARGET_TASKS));
@@ -187,7 +198,7 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
   if (split_pos > ATTN_LONG_MIN_POS)
     split_pos = std::max<int64_t>(ATTN_LONG_MIN_POS, std::min<int64_t>(round128((total * Hkv + ATTN_LONG_TASKS / 2) / ATTN_LONG_TASKS), ATTN_MAX_SPLIT_POS));
   for (int b = 0; b < B; ++b) {
-    const int64_t s = (std::max<int64_t>(batch->seq_lens[b], 1) + split_pos - 1) / split_pos;
+    const int64_t s = (std::max<int64_t>(cached[b], 1) + split_pos - 1) / split_pos;
     P->splits[b] = (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, ATTN_MAX_SPLITS));
   }
   P->desc.clear();

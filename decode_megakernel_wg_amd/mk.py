@@ -14,15 +14,19 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmk.so")
 
-MK_ABI_VERSION = 1
+MK_ABI_VERSION = 2
 MK_DESC_WORDS = 32
 MK_OK, MK_E_INVAL, MK_E_UNSUPPORTED, MK_E_NOMEM, MK_E_HIP, MK_E_STATE, MK_E_RANGE, MK_E_DEVICE = 0, -1, -2, -3, -4, -5, -6, -7
 MK_DBG_DUMP_N = 1
 MK_DBG_TIMESTAMPS = 2
 MK_DBG_WIDE_GEMV = 4
+MK_DBG_PAGE_WALK = 8
+MK_DBG_DROP_SIGNAL = 16
 MK_DBGK_ROUTE_SEL, MK_DBGK_ROUTE_GATE, MK_DBGK_ROUTER_LOGITS, MK_DBGK_NORM_IN, MK_DBGK_COUNTERS, MK_DBGK_TASK_DONE = 1, 2, 3, 4, 5, 6
 MK_DBGK_TIMESTAMPS = 7
-EXPORTS = ("mk_load_model", "mk_build_tasks", "mk_decode_step", "mk_next_tokens", "mk_status", "mk_debug_set", "mk_debug_read",
+MK_DBGK_PAGE_WALK = 8
+MK_DBGK_SLOTS = 9
+EXPORTS = ("mk_load_model", "mk_build_tasks", "mk_decode_step", "mk_mixed_step", "mk_next_tokens", "mk_status", "mk_debug_set", "mk_debug_read",
            "mk_set_grid", "mk_free_model", "mk_last_error", "mk_plan_tasks")
 
 
@@ -45,7 +49,7 @@ class mk_weights(C.Structure):
 
 
 class mk_batch(C.Structure):
-    _fields_ = [("batch", C.c_int32), ("seq_lens", C.c_void_p)]
+    _fields_ = [("batch", C.c_int32), ("seq_lens", C.c_void_p), ("first_of", C.c_void_p)]
 
 
 _lib = None
@@ -62,6 +66,7 @@ def lib():
         L.mk_load_model.argtypes = [vp, vp, C.POINTER(vp)]
         L.mk_build_tasks.argtypes = [vp, vp, vp, i64, C.POINTER(i64)]
         L.mk_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+        L.mk_mixed_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
         L.mk_next_tokens.argtypes = [vp, C.POINTER(vp)]
         L.mk_status.argtypes = [vp, vp]
         L.mk_debug_set.argtypes = [vp, C.c_uint32]
@@ -134,8 +139,8 @@ def make_desc(shape, max_batch, max_pages_per_seq, n_pages, router_bias=None):
 
 
 class Model:
-    """Handle over mk_model*: mk_load_model / mk_build_tasks / mk_decode_step / mk_next_tokens / mk_status /
-    mk_debug_set / mk_debug_read / mk_set_grid / mk_free_model."""
+    """Handle over mk_model*: mk_load_model / mk_build_tasks / mk_decode_step / mk_mixed_step / mk_next_tokens /
+    mk_status / mk_debug_set / mk_debug_read / mk_set_grid / mk_free_model."""
 
     def __init__(self, desc: mk_model_desc, weights: dict):
         L = desc.n_layers
@@ -153,9 +158,10 @@ class Model:
         self.h = h
         self.B = None
 
-    def mk_build_tasks(self, seq_lens, want_tasks=False):
+    def mk_build_tasks(self, seq_lens, want_tasks=False, first_of=None):
         sl = np.ascontiguousarray(seq_lens, np.int32)
-        b = mk_batch(len(sl), sl.ctypes.data)
+        fo = None if first_of is None else np.ascontiguousarray(first_of, np.int32)
+        b = mk_batch(len(sl), sl.ctypes.data, None if fo is None else fo.ctypes.data)
         n = C.c_int64()
         if want_tasks:
             _check(lib().mk_build_tasks(self.h, C.byref(b), None, 0, C.byref(n)))
@@ -171,6 +177,10 @@ class Model:
     def mk_decode_step(self, tokens, seq_lens, page_tables, kv_pages, logits_out, stream=None):
         _check(lib().mk_decode_step(self.h, _ptr(tokens), _ptr(seq_lens), _ptr(page_tables), _ptr(kv_pages), _ptr(logits_out),
                                     _stream(stream)))
+
+    def mk_mixed_step(self, tokens, seq_lens, first_of, page_tables, kv_pages, logits_out, stream=None):
+        _check(lib().mk_mixed_step(self.h, _ptr(tokens), _ptr(seq_lens), _ptr(first_of), _ptr(page_tables), _ptr(kv_pages),
+                                   _ptr(logits_out), _stream(stream)))
 
     def mk_next_tokens(self):
         p = C.c_void_p()
@@ -203,9 +213,10 @@ class Model:
             pass
 
 
-def mk_plan_tasks(desc: mk_model_desc, seq_lens):
+def mk_plan_tasks(desc: mk_model_desc, seq_lens, first_of=None):
     sl = np.ascontiguousarray(seq_lens, np.int32)
-    b = mk_batch(len(sl), sl.ctypes.data)
+    fo = None if first_of is None else np.ascontiguousarray(first_of, np.int32)
+    b = mk_batch(len(sl), sl.ctypes.data, None if fo is None else fo.ctypes.data)
     n = C.c_int64()
     nc = C.c_int32()
     _check(lib().mk_plan_tasks(C.byref(desc), C.byref(b), None, 0, C.byref(n), C.byref(nc)))

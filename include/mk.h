@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 1
+#define MK_ABI_VERSION 2
 #define MK_DESC_WORDS 32   /* int32 words per task descriptor (128 bytes) */
 #define MK_MAX_BATCH 8
 #define MK_PAGE_SIZE 16
@@ -83,10 +83,16 @@ typedef struct mk_weights {
   const void* const* w_down;    /* [L] -> [n_experts][d_model][d_ffn] */
 } mk_weights;
 
-/* A step's batch as seen by the task builder. */
+/* A step's batch as seen by the task builder.  An entry is one token: a decode token of its own sequence,
+ * or one token of a chunk of consecutive positions of one sequence (chunked prefill, mixed prefill +
+ * decode steps): first_of[b] names the chunk's first entry; the chunk's entries are consecutive, in
+ * position order (seq_lens[b] = seq_lens[first_of[b]] + b - first_of[b]), and read the cache only below the
+ * chunk's first position (each entry writes its own K/V slot).  first_of NULL = every entry is a decode
+ * token of its own sequence. */
 typedef struct mk_batch {
   int32_t batch;            /* 1..max_batch */
   const int32_t* seq_lens;  /* host [batch]: prior positions of each sequence (its new token's position) */
+  const int32_t* first_of;  /* host [batch] or NULL: first entry of each entry's chunk */
 } mk_batch;
 
 typedef struct mk_model mk_model;
@@ -119,6 +125,22 @@ int mk_build_tasks(mk_model* m, const mk_batch* batch, int32_t* tasks_out, int64
 int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* page_tables, void* kv_pages,
                    float* logits_out, void* stream);
 
+/* One step whose batch holds chunks of consecutive positions of one sequence (chunked prefill, or prefill
+ * chunks mixed with decode tokens); the same tasks and kernel as mk_decode_step (each entry is a token of
+ * the batch), except that the attention of a chunk's entry b reads the cache below the chunk's first
+ * position and takes positions first_of..b from this step's own projections (causal within the chunk).
+ * Arguments as mk_decode_step, plus
+ *  first_of    device int32 [B]   the host first_of of the last mk_build_tasks (its batch's chunk map)
+ * Entries of one chunk pass the same page table row.  A first_of that contradicts seq_lens (not a run of
+ * consecutive positions) is reported by mk_status as a sequence-length fault.
+ * Passage: aimodeling.com "Cohere megakernel engine: one CUDA file, 1.58x vLLM on H100", section "Caveats and
+ * takeaways" and debriefse.vercel.app "Cohere släpper inferensmotor som minskar väntan på GPU:n", section
+ * "Fortfarande en smal motor": on the pages prefill runs outside the megakernel and is never mixed with
+ * decode; this call runs both inside it.
+ * Errors before launch: as mk_decode_step, and MK_E_INVAL for a null first_of. */
+int mk_mixed_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* first_of, const int32_t* page_tables,
+                  void* kv_pages, float* logits_out, void* stream);
+
 /* Device buffer int32 [max_batch] holding the last step's greedy tokens (argmax, lowest index on ties);
  * it may be passed straight back as the next step's `tokens`.  Owned by the handle. */
 int mk_next_tokens(mk_model* m, int32_t** dev_ptr);
@@ -131,7 +153,11 @@ int mk_status(mk_model* m, void* stream);
  * batches of 1-2 sequences with the matrix-core arithmetic of batches of 3-8 (hi and lo activation parts in
  * separate instructions accumulating into one sum), so that a sequence's results then equal, bit for bit,
  * its results inside a larger batch; without it the two batch classes agree to rounding only. */
-enum { MK_DBG_DUMP_N = 1, MK_DBG_TIMESTAMPS = 2, MK_DBG_WIDE_GEMV = 4 };
+enum { MK_DBG_DUMP_N = 1, MK_DBG_TIMESTAMPS = 2, MK_DBG_WIDE_GEMV = 4, MK_DBG_PAGE_WALK = 8, MK_DBG_DROP_SIGNAL = 16 };
+/* MK_DBG_PAGE_WALK records every attention page walk (MK_DBGK_PAGE_WALK).  MK_DBG_DROP_SIGNAL exercises the
+ * device watchdog from the host: the uploaded task list loses the completion signal of its first QKV task
+ * and dependency waits give up after 4096 polls (about 2 ms instead of about 1 s), so the step ends with
+ * every workgroup exiting normally and mk_status reporting MK_E_DEVICE (a wait that timed out). */
 enum {
   MK_DBGK_ROUTE_SEL = 1,     /* int32 [n_layers][batch][top_k]: last step's expert selection (always recorded) */
   MK_DBGK_ROUTE_GATE = 2,    /* fp32  [n_layers][batch][top_k]: its gates (always recorded) */
@@ -140,9 +166,16 @@ enum {
   MK_DBGK_COUNTERS = 5,      /* uint32 [n_counters]: final values of the last step, copied just before the kernel
                                 resets them to zero for the next step (always recorded) */
   MK_DBGK_TASK_DONE = 6,     /* uint32 [n_tasks]: completions per task in the last step (must be 1 each) */
-  MK_DBGK_TIMESTAMPS = 7     /* uint64 [n_tasks][8]: claim, dependencies met, end (100 MHz wall clock), hardware id
+  MK_DBGK_TIMESTAMPS = 7,    /* uint64 [n_tasks][8]: claim, dependencies met, end (100 MHz wall clock), hardware id
                                 (XCC id << 32 | HW_ID register), then up to 4 task-specific sub-phase marks (0 = unset);
                                 MK_DBG_TIMESTAMPS */
+  MK_DBGK_PAGE_WALK = 8,     /* uint32 [n_layers][batch][n_kv_heads][4]: per attention walk, the cache pages read, the sum
+                                over them of (logical page + 1) * physical page (mod 2^32), the positions attended
+                                (cached + new) and 1 + physical page * 16 + slot of the entry's K/V write (0 = none);
+                                MK_DBG_PAGE_WALK */
+  MK_DBGK_SLOTS = 9          /* int32 [n_layers][n_slots][32]: expert slot table (n_slots = min(n_experts, batch *
+                                top_k)): expert (-1 = unused), token count, then (token, rank, gate bits) per token of the
+                                slot in ascending token order (always recorded) */
 };
 int mk_debug_set(mk_model* m, uint32_t flags);
 /* Copies `bytes` of debug buffer `kind` to host memory; synchronises the device first.

@@ -56,13 +56,13 @@ class Step:
     clock: int = 0      # arrival-process time of the step
 
 
-def draws(n: int, lo: int = PREFIX_LO, hi: int = PREFIX_HI):
+def draws(n: int, lo: int = PREFIX_LO, hi: int = PREFIX_HI, mean_gap: float = MEAN_GAP):
     """Arrival times, prefix lengths and output lengths of sequences 0..n-1."""
     ug = synth.u01(SEED_ARRIVE, 0, 0, n)
     uo = synth.u01(SEED_OUTLEN, 0, 0, n)
     arrive = np.zeros(n, np.int64)
     for i in range(1, n):
-        arrive[i] = arrive[i - 1] + max(1, math.ceil(-MEAN_GAP * math.log1p(-float(ug[i]))))
+        arrive[i] = arrive[i - 1] + max(1, math.ceil(-mean_gap * math.log1p(-float(ug[i]))))
     out_len = np.array([max(1, math.ceil(math.log1p(-float(u)) / math.log1p(-P_END))) for u in uo], np.int64)
     prefix = synth.loguniform_ints(SEED_LEN, 2, n, lo, hi)
     return arrive, prefix, out_len
@@ -77,11 +77,13 @@ def pool_pages(hi: int = PREFIX_HI, max_batch: int = MAX_BATCH) -> int:
     return max_batch * -(-(hi + 4096) // PAGE)
 
 
-def schedule(n_steps: int, n_pages: int | None = None, lo: int = PREFIX_LO, hi: int = PREFIX_HI, max_batch: int = MAX_BATCH):
-    """The first n_steps decode steps.  Returns (steps, seqs, n_pages, max_pages_per_seq)."""
+def schedule(n_steps: int, n_pages: int | None = None, lo: int = PREFIX_LO, hi: int = PREFIX_HI, max_batch: int = MAX_BATCH,
+             mean_gap: float = MEAN_GAP):
+    """The first n_steps decode steps.  Returns (steps, seqs, n_pages, max_pages_per_seq).  mean_gap: mean
+    arrival gap in steps (64 for the workload; smaller gaps keep the batch full, for tests)."""
     n_pages = pool_pages(hi, max_batch) if n_pages is None else n_pages
     n_draw = n_steps + 64
-    arrive, prefix, out_len = draws(n_draw, lo, hi)
+    arrive, prefix, out_len = draws(n_draw, lo, hi, mean_gap)
     seqs = [Seq(i, int(arrive[i]), int(prefix[i]), int(out_len[i])) for i in range(n_draw)]
     free = list(range(n_pages - 1, -1, -1))  # stack: pop() gives page 0 first
     waiting, live, steps = [], [], []

@@ -19,7 +19,7 @@ HOST_LIB = os.path.join(_HERE, "libsynth_host.so")
 DEV_LIB = os.path.join(_HERE, "libsynth_dev.so")
 
 # Stream kinds, mirroring synth_core.h.
-EMBED, LM_HEAD, WQ, WK, WV, WO, WROUTER, WGATE, WUP, WDOWN = range(1, 11)
+EMBED, LM_HEAD, WQ, WK, WV, WO, WROUTER, WGATE, WUP, WDOWN, NORM = range(1, 12)
 KV_POS_SPAN = 1 << 20
 
 

@@ -69,7 +69,8 @@ enum {
   SYNTH_WROUTER = 7,
   SYNTH_WGATE = 8,
   SYNTH_WUP = 9,
-  SYNTH_WDOWN = 10
+  SYNTH_WDOWN = 10,
+  SYNTH_NORM = 11  /* RMSNorm gains (layer index; n_layers = the final norm) */
 };
 
 SYNTH_FN uint64_t synth_weight_stream(int kind, int layer) { return ((uint64_t)kind << 32) | (uint32_t)layer; }

@@ -9,11 +9,13 @@ pages' serving benchmarks are not used; every input here is seeded noise.
 
 Recipe (seeds): weights N(0, 0.02) seed 0; KV prefixes N(0, 1) seed 1; start
 tokens seed 2; context lengths seed 3; page shuffle seed 4; skew permutation
-seed 5; arrivals seed 6; output lengths seed 7.  RMSNorm gains are 1.0.
+seed 5; arrivals seed 6; output lengths seed 7.  RMSNorm gains are 1.0, or, for shapes with
+gain_sigma > 0 (parity cases that exercise the gains), BF16(1 + z) with z ~ N(0, gain_sigma) drawn per
+layer and for the final norm (seed 0).
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -39,6 +41,7 @@ class Shape:
     rms_eps: float = 1e-6
     rope_base: float = 10000.0
     page_size: int = PAGE
+    gain_sigma: float = 0.0  # RMSNorm gains: 1.0 when 0, else BF16(1 + N(0, gain_sigma)) per layer and final norm
 
     @property
     def qkv_rows(self):
@@ -65,6 +68,7 @@ class Shape:
 
 TINY = Shape(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, d_head=64, n_experts=8, top_k=2, d_ffn=512, vocab=4096)
 FULL = Shape(n_layers=48, d_model=2048, n_q_heads=32, n_kv_heads=4, d_head=128, n_experts=128, top_k=8, d_ffn=768, vocab=262144)
+GAIN_SIGMA = 0.1
 
 
 @dataclass
@@ -88,7 +92,13 @@ def start_tokens(shape: Shape, B: int):
 
 
 def make(name: str, steps: int | None = None) -> Workload:
-    """The named workloads: tiny, b1_8k, b8_ragged_uniform, b8_ragged_skewed, long_64k, long_128k, long_256k."""
+    """The named workloads: tiny, b1_8k, b8_ragged_uniform, b8_ragged_skewed, long_64k, long_128k, long_256k;
+    a name ending in "_gains" is the same workload with non-unit RMSNorm gains."""
+    if name.endswith("_gains"):
+        w = make(name[:-len("_gains")], steps)
+        w.name = name
+        w.shape = replace(w.shape, gain_sigma=GAIN_SIGMA)
+        return w
     if name == "tiny":
         w = Workload(name, TINY, [128], 16 if steps is None else steps, extra_pages=2)
     elif name == "tiny_ragged":
@@ -140,11 +150,24 @@ def host_expert(shape: Shape, layer: int, e: int):
 ONE_BF16 = np.uint16(0x3F80)
 
 
+def host_norm(shape: Shape, layer: int) -> np.ndarray:
+    """RMSNorm gain of layer `layer` (layer == n_layers: the final norm) as BF16 bit patterns: 1.0, or
+    BF16(1 + z) with z the generator's BF16 N(0, gain_sigma) value, the sum taken in fp32 and rounded to
+    nearest even."""
+    d = shape.d_model
+    if not shape.gain_sigma:
+        return np.full(d, ONE_BF16, np.uint16)
+    z = synth.fill_bf16_host(d, SEED_W, synth.weight_stream(synth.NORM, layer), 0, shape.gain_sigma)
+    g = (z.astype(np.uint32) << 16).view(np.float32) + np.float32(1.0)
+    u = g.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
 def host_layer(shape: Shape, layer: int):
     """Dense (non-expert) weights of one layer as uint16 arrays."""
     d, dh = shape.d_model, shape.d_head
     return dict(
-        attn_norm=np.full(d, ONE_BF16, np.uint16),
+        attn_norm=host_norm(shape, layer),
         wq=host_matrix(synth.WQ, layer, shape.n_q_heads * dh, d),
         wk=host_matrix(synth.WK, layer, shape.n_kv_heads * dh, d),
         wv=host_matrix(synth.WV, layer, shape.n_kv_heads * dh, d),
@@ -194,6 +217,13 @@ class DeviceModel:
         self.lm_head = mk(V, d)
         self.final_norm = torch.ones(d, dtype=bf, device=device)
         self.attn_norm = torch.ones(L, d, dtype=bf, device=device)
+        if s.gain_sigma:
+            def up(a):
+                return torch.from_numpy(a.view(np.int16)).to(device).view(bf)
+
+            self.final_norm.copy_(up(host_norm(s, L)))
+            for l in range(L):
+                self.attn_norm[l].copy_(up(host_norm(s, l)))
         self.wq = mk(L, s.n_q_heads * dh, d)
         self.wk = mk(L, s.n_kv_heads * dh, d)
         self.wv = mk(L, s.n_kv_heads * dh, d)

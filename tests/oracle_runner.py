@@ -45,16 +45,22 @@ class OracleRun:
     in memory; for large ones `layer_source(l)` generates a layer's dense weights on demand and experts
     are generated when selected."""
 
-    def __init__(self, w: W.Workload, pt, n_pages, keep_all=None, kv_layers=None):
+    def __init__(self, w: W.Workload, pt, n_pages, keep_all=None, lazy_kv=False, keep_kv_layers=()):
+        """lazy_kv: generate each layer's cache when the layer runs and drop it afterwards (KV values are keyed
+        by logical coordinates, so they do not depend on when they are generated); only the layers listed in
+        keep_kv_layers are kept (self.kept[l]), with the step's K/V writes.  For one-step runs of long contexts."""
         self.w = w
         s = self.shape = w.shape
         self.D = dims(s)
         self.pt = pt
         self.n_pages = n_pages
-        self.kv = W.host_kv(w, pt, n_pages, n_layers=kv_layers)  # kv_layers: only the first layers' caches
+        self.lazy_kv = lazy_kv
+        self.keep_kv_layers = set(keep_kv_layers)
+        self.kept = {}
+        self.kv = None if lazy_kv else W.host_kv(w, pt, n_pages)
         small = s.n_layers * (s.layer_attn_bytes() + s.n_experts * s.expert_bytes()) < 2e9
         self.keep_all = small if keep_all is None else keep_all
-        self.final_norm = np.full(s.d_model, W.ONE_BF16, np.uint16)
+        self.final_norm = W.host_norm(s, s.n_layers)
         self.lm_head = W.host_lm_head(s)
         self._layers = {}
         self._experts = {}
@@ -112,7 +118,14 @@ class OracleRun:
                                          f"(k-th gap {kth_gap(lg, s.top_k):.3g}, gpu-chosen logits {lg[np.asarray(gpu_sel[l][b])]})")
                 need.update(int(e) for e in sel)
             Wl = self.layer_weights(l, sorted(need))
-            x, aux = O.layer(self.D, Wl, pos, self.pt, self.kv[l], x, sel_force=force if (force >= 0).any() else None)
+            if self.lazy_kv:
+                kvl = W.host_kv(self.w, self.pt, self.n_pages, layer0=l, n_layers=1)[0]
+                if l in self.keep_kv_layers:
+                    self.kept[l] = kvl
+            else:
+                kvl = self.kv[l]
+            x, aux = O.layer(self.D, Wl, pos, self.pt, kvl, x, sel_force=force if (force >= 0).any() else None)
+            del kvl
             sels.append(aux["sel"])
             ns.append(aux["n"])
             if s.n_layers >= 24 and l % 12 == 11:  # progress of long oracle runs

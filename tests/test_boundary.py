@@ -9,13 +9,10 @@ import pytest
 
 from decode_megakernel_wg_amd import mk
 from synth import workloads as W
+from taskgraph import (OP_ATTN, OP_EMBED, OP_LMHEAD, W_ARR, W_D, W_LAYER, W_OP, W_R0, W_R1, W_SIG, W_WAIT0, complete, counter_layout,
+                       phases_of, simulate)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-
-# descriptor words (mirrors the library's layout)
-W_OP, W_LAYER, W_A, W_B, W_C, W_D, W_R0, W_R1, W_WAIT0, W_SIG, W_SIGN, W_ARR, W_ARRN, W_SIGR = 0, 1, 2, 3, 4, 5, 6, 7, 8, 16, 17, 18, 19, 20
-W_ARR2, W_ARRN2, W_RSIG, W_RSIGR = 24, 25, 26, 27
-OP_EMBED, OP_ATTN, OP_LMHEAD = 1, 4, 9
 
 
 def declared(header):
@@ -66,82 +63,6 @@ def test_batch_validation():
         mk.mk_plan_tasks(d, [-1])
 
 
-def phases_of(tasks):
-    """The launcher's phases: maximal runs of one operation and layer, in list order."""
-    phases = []
-    for t in range(len(tasks)):
-        key = (tasks[t, W_OP], tasks[t, W_LAYER])
-        if not phases or phases[-1][0] != key:
-            phases.append((key, []))
-        phases[-1][1].append(t)
-    return [p for _, p in phases]
-
-
-def simulate(tasks, n_counters, n_workers, rng):
-    """Every workgroup runs one task at a time.  One workgroup claims the list in order; two or more take
-    tasks from the phase pools in order, one at a time, moving to the next phase once a take finds the pool
-    empty.  Rounds visit the workgroups in random order; each picks its next task if it has none and runs
-    its task if the waits are met.  A round that runs nothing while tasks remain is a deadlock.  Returns
-    final counters and completion counts."""
-    phases = phases_of(tasks) if n_workers >= 2 else [list(range(len(tasks)))]
-    ctr = np.zeros(n_counters, np.int64)
-    done = np.zeros(len(tasks), np.int64)
-    taken = [0] * len(phases)
-    cur = [None] * n_workers
-    ph = [0] * n_workers
-    completed = 0
-
-    def ready(t):
-        w = tasks[t]
-        for i in range(4):
-            c, tgt = w[W_WAIT0 + 2 * i], w[W_WAIT0 + 2 * i + 1]
-            if c >= 0 and ctr[c] < tgt:
-                return False
-        return True
-
-    def pick(wk):
-        while ph[wk] < len(phases):
-            p = ph[wk]
-            if taken[p] < len(phases[p]):
-                taken[p] += 1
-                return phases[p][taken[p] - 1]
-            ph[wk] += 1
-        return None
-
-    while completed < len(tasks):
-        progressed = False
-        for wk in rng.permutation(n_workers):
-            if cur[wk] is None:
-                cur[wk] = pick(wk)
-            t = cur[wk]
-            if t is None or not ready(t):
-                continue
-            cur[wk] = None
-            done[t] += 1
-            completed += 1
-            complete(tasks[t], ctr)
-            progressed = True
-        assert progressed, f"deadlock: no workgroup can run its current task ({completed} of {len(tasks)} done)"
-    return ctr, done
-
-
-def complete(w, ctr):
-    """Counter effects of a finished task: an arrival (only the last arriver goes on), then the signal of
-    W_SIGR consecutive counters; a task that completes a residual row tile then arrives with its router
-    partial, and the last row tile releases the next layer's expert-slot counters (each receives a routing
-    value >= 1)."""
-    if w[W_ARR] >= 0:
-        ctr[w[W_ARR]] += 1
-        if ctr[w[W_ARR]] != w[W_ARRN]:
-            return
-    if w[W_SIG] >= 0:
-        ctr[w[W_SIG]:w[W_SIG] + w[W_SIGR]] += w[W_SIGN]
-    if w[W_ARR2] >= 0:
-        ctr[w[W_ARR2]] += 1
-        if ctr[w[W_ARR2]] == w[W_ARRN2]:
-            ctr[w[W_RSIG]:w[W_RSIG] + w[W_RSIGR]] += 1
-
-
 @pytest.mark.parametrize("name,B_lens", [("tiny", [128]), ("tiny", [5, 300, 17, 0]), ("full", [8192]),
                                          ("full", [1024, 30000, 4000, 70000, 2000, 9000, 1500, 12000])])
 def test_task_list_is_a_deadlock_free_topological_order(name, B_lens):
@@ -165,11 +86,14 @@ def test_task_list_is_a_deadlock_free_topological_order(name, B_lens):
             continue
         ctr, done = simulate(tasks, n_ctr, workers, rng)
         assert np.all(done == 1)
+        # every interleaving ends every counter at its planned value, and every wait's target is exactly
+        # that final value (a consumer waits for all of its producers)
+        assert np.array_equal(ctr, sim)
         for w in tasks:
             for i in range(4):
                 c, tgt = w[W_WAIT0 + 2 * i], w[W_WAIT0 + 2 * i + 1]
                 if c >= 0:
-                    assert ctr[c] == tgt or ctr[c] >= tgt
+                    assert ctr[c] == tgt, f"counter {c} ends at {ctr[c]}, a wait targets {tgt}"
 
 
 def test_dropped_producer_is_detected_by_the_simulator():
@@ -229,3 +153,56 @@ def test_task_list_has_the_regular_phase_structure(name, B_lens):
         layer_runs = runs[1 + l * npl:1 + (l + 1) * npl]
         assert [(int(tasks[r[0], W_OP]), len(r)) for r in layer_runs] == first
         assert all(int(tasks[t, W_LAYER]) == l for r in layer_runs for t in r)
+
+
+@pytest.mark.parametrize("shape,lens", [(W.TINY, [128]), (W.TINY, [5, 300, 17, 0]), (W.FULL, [8192]), (W.FULL, [100] * 8)])
+def test_counter_layout_mirror(shape, lens):
+    """The tests' copy of the counter layout gives the library's counter count, and every counter a descriptor
+    names lies in the block its role belongs to."""
+    maxp = max(lens) // 16 + 2
+    d = desc_for(shape, B=len(lens), pages=maxp, n_pages=maxp * len(lens))
+    tasks, n_ctr = mk.mk_plan_tasks(d, lens)
+    B, L = len(lens), shape.n_layers
+    n_slots = min(shape.n_experts, B * shape.top_k)
+    n_rt = shape.d_model // (128 if shape.d_model >= 1024 else 32)
+    lay = counter_layout(L, shape.n_kv_heads, B, n_slots, n_rt)
+    assert lay["total"] == n_ctr
+
+    def inside(c, block):
+        o, n = lay[block]
+        return o <= c < o + n
+
+    for w in tasks:
+        op = w[W_OP]
+        if op == 3:
+            assert inside(w[W_WAIT0], "xready") and inside(w[W_SIG], "qkv_done")
+        if op == OP_ATTN:
+            assert inside(w[W_WAIT0], "qkv_done") and inside(w[W_ARR], "attn_arrive") and inside(w[W_SIG], "attn_done")
+        if op == 5:
+            assert inside(w[W_WAIT0], "slot_ready") and inside(w[W_SIG], "up_done")
+        if op in (6, 7):
+            assert inside(w[W_ARR], "resid_arrive") and inside(w[W_SIG], "xready")
+
+
+def test_chunk_map_validation_and_planning():
+    """first_of: entries of a chunk are consecutive, in position order, and its attention splits cover only the
+    cached prefix below the chunk's first position."""
+    d = desc_for(W.TINY, B=8, pages=64, n_pages=512)
+    lens = [300, 301, 302, 303, 40, 41, 7, 500]
+    first = [0, 0, 0, 0, 4, 4, 6, 7]
+    tasks, _ = mk.mk_plan_tasks(d, lens, first)
+    plain, _ = mk.mk_plan_tasks(d, [300, 300, 300, 300, 40, 40, 7, 500])
+    # the splits depend only on the cached lengths: a chunk plans like its first entry repeated
+    assert np.array_equal(tasks, plain)
+    for bad_first, bad_lens in (([0, 0, 1, 3, 4, 4, 6, 7], lens),        # an entry whose first is not a chunk head
+                                ([0, 1, 0, 3, 4, 4, 6, 7], lens),        # a chunk interrupted by another sequence
+                                ([1, 1, 2, 3, 4, 4, 6, 7], lens),        # first after the entry
+                                ([0, 0, 0, 0, 4, 4, 6, 7], [300, 301, 303, 303, 40, 41, 7, 500]),  # positions not consecutive
+                                ([0, 0, 0, 0, 4, 4, 4, 7], lens)):       # an entry's position outside its chunk's run
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_plan_tasks(d, bad_lens, bad_first)
+        assert e.value.code == mk.MK_E_INVAL
+    # prefill from an empty context: one split per entry, covering no cached position
+    t0, _ = mk.mk_plan_tasks(d, list(range(8)), [0] * 8)
+    attn = t0[t0[:, W_OP] == OP_ATTN]
+    assert (attn[:, W_D] == 1).all()

@@ -1,23 +1,27 @@
 """GPU parity: the persistent HIP kernel (through the C ABI) against the CPU oracle on the same seeded inputs.
 
 Bar (per step and sequence): logits within relative L2 error 1e-2 (BF16 weights, fp32 accumulation; the
-kernel reaches ~1e-6); greedy tokens equal except where the oracle's top-2 logit gap is below 1e-2; routing
-identical except at oracle near-ties (k-th vs (k+1)-th logit gap < 1e-3, counted); router logits of the
-GPU's own normalised inputs reproduce the GPU's selection exactly (teacher-forced router check); every
-task completes exactly once and every counter ends at its planned value.
+kernel reaches ~1e-5); greedy tokens equal except where the oracle's top-2 logit gap is below 1e-2, with
+>= 99 % agreement; routing identical except at oracle near-ties (k-th vs (k+1)-th logit gap < 1e-3: the
+oracle follows the GPU's selection there and counts it, at most 1 % of the (layer, token) routings).
+Integer work bit-exact every step (gpu_checks): the selection is exactly the top-k of the GPU's own router
+logits and the slot table exactly its distinct experts; every page walk equals a brute-force walk of the
+page table; every task completes once and every counter ends at its planned value.  The router logits of
+the GPU's own normalised inputs agree with the oracle's router applied to them (rtol 1e-5: the GPU forms
+inv_rms * sum w x gamma, the oracle sum w n, equal up to the fp32 rounding of n).
 """
 import numpy as np
 import pytest
 import torch
 
-from oracle_runner import OracleRun, rel_l2, tie_ok, top2_gap
+from gpu_checks import check_step, kv_layers_close
+from oracle_runner import OracleRun, rel_l2, top2_gap
 from synth import workloads as W
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("cuda")]
 
 LOGIT_TOL = 1e-2
 TOKEN_GAP = 1e-2
-ROUTE_EPS = 1e-5   # teacher-forced routing: largest k-th logit gap at which the GPU may pick the other set
 
 
 def _session(w, **kw):
@@ -26,7 +30,7 @@ def _session(w, **kw):
     return Session(w, **kw)
 
 
-def run_parity(w, steps, check_router_inputs=True, grid=None):
+def run_parity(w, steps, check_router_inputs=True, grid=None, flags=0):
     from decode_megakernel_wg_amd import mk
     from oracle import oracle as O
 
@@ -34,38 +38,29 @@ def run_parity(w, steps, check_router_inputs=True, grid=None):
     sess = _session(w, pt=pt, n_pages=n_pages)
     if grid:
         sess.h.mk_set_grid(grid)
-    sess.h.mk_debug_set(mk.MK_DBG_DUMP_N)
+    sess.h.mk_debug_set(mk.MK_DBG_DUMP_N | mk.MK_DBG_PAGE_WALK | flags)
     orc = OracleRun(w, pt, n_pages)
     s = w.shape
     tokens = list(w.tokens)
     agree = 0
     worst = 0.0
-    near_ties = 0
     for step in range(steps):
         sess.step()
         sess.status()
         logits = sess.logits.cpu().numpy()
         nxt = sess.next_tokens()
         gsel = sess.h.mk_debug_read(mk.MK_DBGK_ROUTE_SEL, (s.n_layers, w.B, s.top_k), np.int32)
-        done = sess.h.mk_debug_read(mk.MK_DBGK_TASK_DONE, (sess.h.n_tasks,), np.uint32)
-        assert np.all(done == 1), f"step {step}: tasks not run exactly once: {np.nonzero(done != 1)[0][:10]}"
+        check_step(sess.h, s, sess.desc, pt, sess.seq_rows_host[step], grid=grid, plan_lens=sess.seq_rows_host[0])
         if check_router_inputs:
             n_gpu = sess.h.mk_debug_read(mk.MK_DBGK_NORM_IN, (s.n_layers, w.B, s.d_model), np.float32)
             rl_gpu = sess.h.mk_debug_read(mk.MK_DBGK_ROUTER_LOGITS, (s.n_layers, w.B, s.n_experts), np.float32)
             for l in range(s.n_layers):
                 wr = W.host_matrix(7, l, s.n_experts, s.d_model)  # router weights of layer l
                 for b in range(w.B):
-                    # The GPU forms each logit as inv_rms * sum_i w_ei * x_i * gamma_i (fp64) from the row tiles'
-                    # partials; the oracle's router takes the GPU's fp32 RMSNorm output n_i = x_i * (gamma_i *
-                    # inv_rms).  The two agree up to the fp32 rounding of n (a few 1e-8 here), so selections must be
-                    # identical except where the oracle's k-th and (k+1)-th logits are closer than ROUTE_EPS.
-                    sel, _, lg = O.router(n_gpu[l, b], wr, s.top_k, w.router_bias)
+                    _, _, lg = O.router(n_gpu[l, b], wr, s.top_k, w.router_bias)
                     assert np.allclose(lg, rl_gpu[l, b], rtol=1e-5, atol=1e-6), f"router logits differ at step {step} layer {l}"
-                    if not np.array_equal(sel, gsel[l, b]):
-                        assert tie_ok(lg, gsel[l, b], s.top_k, ROUTE_EPS), f"teacher-forced routing differs at step {step} layer {l} seq {b}"
-                        near_ties += 1
         pos = sess.seq_rows_host[step]
-        ol, onx, osel, _ = orc.step(tokens, pos, gpu_sel=gsel)
+        ol, onx, _, _ = orc.step(tokens, pos, gpu_sel=gsel)
         for b in range(w.B):
             e = rel_l2(logits[b], ol[b])
             worst = max(worst, e)
@@ -77,25 +72,38 @@ def run_parity(w, steps, check_router_inputs=True, grid=None):
             assert nxt[b] == int(np.argmax(logits[b])), "greedy token is not the argmax of the GPU's own logits"
         tokens = [int(t) for t in nxt]
     assert agree >= 0.99 * steps * w.B
-    if check_router_inputs:
-        assert near_ties <= max(1, 0.01 * steps * w.B * s.n_layers), f"{near_ties} teacher-forced near-tie routings"
-    orc.tf_near_ties = near_ties
+    assert orc.near_ties <= max(1, 0.01 * orc.route_checked), f"{orc.near_ties} routing near-ties in {orc.route_checked}"
     return sess, orc, worst
+
+
+def _check_kv(sess, orc):
+    """The KV cache the kernel wrote equals the oracle's up to BF16 rounding (kv_layers_close), and nearly all
+    of it bit for bit."""
+    from oracle import oracle as O
+
+    kv_gpu = sess.kvc.kv.view(torch.int16).cpu().numpy().view(np.uint16)
+    kv_layers_close(O.bf16_to_f32(kv_gpu), O.bf16_to_f32(orc.kv), sess.w.name)
+    assert (kv_gpu == orc.kv).mean() > 0.99
 
 
 def test_tiny_16_steps():
     w = W.make("tiny")
     sess, orc, worst = run_parity(w, w.steps)
-    print(f"tiny: worst logits rel L2 {worst:.2e}, routing near-ties {orc.near_ties}/{orc.route_checked}, "
-          f"teacher-forced near-ties {orc.tf_near_ties}")
-    # KV written by the kernel equals the oracle's cache: the new K/V are BF16 roundings of fp32 values that
-    # agree to ~1e-6, so a rounding may land one step apart (more steps only for values near zero)
-    from oracle import oracle as O
+    print(f"tiny: worst logits rel L2 {worst:.2e}, routing near-ties {orc.near_ties}/{orc.route_checked}")
+    _check_kv(sess, orc)
 
-    kv_gpu = sess.kvc.kv.view(torch.int16).cpu().numpy().view(np.uint16)
-    g32, o32 = O.bf16_to_f32(kv_gpu), O.bf16_to_f32(orc.kv)
-    assert np.allclose(g32, o32, rtol=2 ** -7, atol=1e-4), f"KV cache differs: max abs {np.abs(g32 - o32).max():.3g}"
-    assert (kv_gpu == orc.kv).mean() > 0.99
+
+def test_tiny_gains_16_steps():
+    """Non-unit RMSNorm gains (BF16 of 1 + N(0, 0.1), a different vector per layer and for the final norm):
+    the gains enter the consumers' RMSNorm staging, the router partials and the LM head's final norm."""
+    w = W.make("tiny_gains")
+    assert w.shape.gain_sigma > 0
+    sess, orc, worst = run_parity(w, w.steps)
+    print(f"tiny_gains: worst logits rel L2 {worst:.2e}")
+    _check_kv(sess, orc)
+    # the gains are not all equal, and the final norm differs from every layer's
+    fin = W.host_norm(w.shape, w.shape.n_layers)
+    assert len(np.unique(fin)) > 10 and not np.array_equal(fin, W.host_norm(w.shape, 0))
 
 
 def test_tiny_ragged_batch_shuffled_pages():
@@ -103,9 +111,13 @@ def test_tiny_ragged_batch_shuffled_pages():
     run_parity(w, w.steps)
 
 
-def test_grid_size_and_page_order_invariance():
-    from decode_megakernel_wg_amd import mk
+def test_tiny_ragged_odd_grid():
+    """The ragged batch on 7 workgroups (phase pools with few workgroups), with every integer check."""
+    w = W.make("tiny_ragged", steps=2)
+    run_parity(w, w.steps, grid=7, check_router_inputs=False)
 
+
+def test_grid_size_and_page_order_invariance():
     w = W.make("tiny", steps=2)
     pt, n_pages = W.page_tables(w)
     ref = None
@@ -181,6 +193,32 @@ def _single_kv(w, b, pt, n_pages):
     return kv
 
 
+def test_watchdog_times_out_and_recovers():
+    """A dependency that never completes, forced from the host: the uploaded list loses its first QKV task's
+    signal (MK_DBG_DROP_SIGNAL, which also cuts the wait limit to ~2 ms), so a wait gives up, the step aborts
+    with every workgroup exiting normally, and mk_status reports MK_E_DEVICE.  Cleared, the same handle then
+    reruns the step with results bit-identical to a fresh handle's."""
+    from decode_megakernel_wg_amd import mk
+
+    w = W.make("tiny", steps=1)
+    pt, n_pages = W.page_tables(w)
+    ref = _session(w, pt=pt, n_pages=n_pages)
+    ref.step()
+    ref.status()
+    want = ref.logits.cpu().numpy().copy()
+    sess = _session(w, pt=pt, n_pages=n_pages, model=ref.model)
+    sess.h.mk_debug_set(mk.MK_DBG_DROP_SIGNAL)
+    sess.step()
+    with pytest.raises(mk.MkError) as e:
+        sess.status()
+    assert e.value.code == mk.MK_E_DEVICE and "timed out" in str(e.value)
+    sess.h.mk_debug_set(0)
+    sess.rewind(0)
+    sess.step()
+    sess.status()
+    assert np.array_equal(sess.logits.cpu().numpy(), want)
+
+
 def test_device_generator_matches_host():
     from synth import synth
 
@@ -192,3 +230,7 @@ def test_device_generator_matches_host():
         assert np.array_equal(dev, host), name
     emb = m.embed.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(emb, W.host_embed(s))
+    g = W.DeviceModel(W.make("tiny_gains").shape)
+    for l in range(s.n_layers):
+        assert np.array_equal(g.attn_norm[l].view(torch.int16).cpu().numpy().view(np.uint16), W.host_norm(g.shape, l))
+    assert np.array_equal(g.final_norm.view(torch.int16).cpu().numpy().view(np.uint16), W.host_norm(g.shape, s.n_layers))
