@@ -55,6 +55,9 @@ constexpr int N_WAITS = 4;
 // of a layer share all compute units.  Phases follow the list's topological order and a workgroup enters
 // a phase only once every task of the previous one has been taken by a workgroup that runs it at once,
 // so the earliest unfinished task can always run.  One workgroup claims the list in order.
+// Expert phases (UP, DOWN) list their tiles slot by slot, the same number per slot; slots are numbered in
+// ascending expert order, so once a layer is routed (its used-slot count published) the tiles of its unused
+// slots are the tail of each expert phase, and takers leave the phase there.
 constexpr int DESC_WORDS = 32;
 
 // Tile sizes chosen by the planner (rows per task); the kernel reads r0/r1 from the descriptor.
@@ -71,7 +74,7 @@ constexpr int LM_MAX_WG = 1024;  // most workgroups a launch may have (stride of
 
 // Counter index layout for a model/batch; computed identically by planner and host launcher.
 struct CounterLayout {
-  int32_t ticket, done, xready, phase, qkv_done, router_arrive, slot_ready, attn_arrive, attn_done, up_done,
+  int32_t ticket, done, xready, phase, qkv_done, router_arrive, slot_ready, slots_used, attn_arrive, attn_done, up_done,
       resid_arrive, lm_arrive, lm_pool, total;
   int32_t n_layers, n_kv, n_slots, n_row_tiles, batch;
   void build(int L, int Hkv, int B, int slots, int nrt) {
@@ -88,6 +91,7 @@ struct CounterLayout {
     qkv_done = o; o += L * Hkv;
     router_arrive = o; o += L;
     slot_ready = o; o += L * slots;
+    slots_used = o; o += L;  // distinct experts of each layer's routing (0 until the layer is routed)
     attn_arrive = o; o += L * B * Hkv;
     attn_done = o; o += L * Hkv;
     up_done = o; o += L * slots;

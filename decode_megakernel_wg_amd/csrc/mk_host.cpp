@@ -72,6 +72,7 @@ struct mk_model {
   int32_t ph_on = 0;         // phases in use (two or more workgroups and a regular list)
   int32_t ph_npl = 0;        // phases per layer
   int32_t ph_n[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int32_t ph_op[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int32_t* staging = nullptr;  // pinned host copy of the task list
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
@@ -242,7 +243,10 @@ static void derive_phases(mk_model* m, const int32_t* q, int64_t n) {
     }
   m->ph_npl = npl;
   m->ph_n[0] = len[0];
-  for (int k = 0; k < npl; ++k) m->ph_n[1 + k] = len[1 + k];
+  for (int k = 0; k < npl; ++k) {
+    m->ph_n[1 + k] = len[1 + k];
+    m->ph_op[k] = op[1 + k];
+  }
   m->ph_on = 1;
 }
 
@@ -306,7 +310,12 @@ static int launch_step(mk_model* m, const int32_t* tokens, const int32_t* seq_le
   a.c_ticket = P.cl.ticket;
   a.ph_on = m->ph_on;
   a.ph_npl = m->ph_npl;
-  for (int i = 0; i < 8; ++i) a.ph_n[i] = m->ph_n[i];
+  for (int i = 0; i < 8; ++i) {
+    a.ph_n[i] = m->ph_n[i];
+    a.ph_op[i] = m->ph_op[i];
+  }
+  a.c_slots_used = P.cl.slots_used;
+  a.c_resid_arrive = P.cl.resid_arrive;
   a.c_phase = P.cl.phase;
   a.c_done = P.cl.done;
   a.layers = m->layers;

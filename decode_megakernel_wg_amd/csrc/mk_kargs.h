@@ -33,6 +33,9 @@ struct KArgs {
   // operation, of ph_n[1] .. ph_n[ph_npl] tasks; counter c_phase + p is phase p's pool (p = 0 embedding,
   // 1 + ph_npl * l + k).  Otherwise every workgroup claims the list in order (ticket counter c_ticket).
   int32_t ph_on, ph_npl, ph_n[8], c_phase;
+  int32_t ph_op[8];      // operation of each per-layer phase
+  // expert slots: counter of each layer's used-slot count, first residual arrival counter
+  int32_t c_slots_used, c_resid_arrive;
   // model (device)
   const LayerW* layers;
   const uint16_t* embed;

@@ -79,7 +79,8 @@ struct Lds {
   float slot_g[8];
   int slotw[SLOT_WORDS];
   int32_t desc[2][DESC_WORDS];  // current and next task descriptor
-  int pool_tile;                // attention-branch phases: the index a take returned
+  int pool_tile;                // phases: the index a take returned
+  int pool_used;                // expert phases: the layer's used-slot count seen with the take (0 = not yet routed)
   int lmq[4];                   // LM head: ring of claimed vocabulary chunks
   uint32_t wval;                // value a wait observed (expert slot words)
   int next1, flag;
@@ -432,6 +433,20 @@ __device__ __forceinline__ void route_select(KA& a, int l, int32_t slot0, Lds& S
     pubi(ent + 0, e);
     pubi(ent + 1, n);
     sv = e >= 0 ? (mask << 16) | (uint32_t)(e + 1) : 0x80000000u;
+  }
+  // Unused slots: their tasks will neither run nor arrive, so their arrivals on each row tile's residual
+  // counter are made here, and the layer's used-slot count is published for the phase takes, all before any
+  // slot is released.  Until a slot is released only O-projection tiles (at most Hkv per row tile) can have
+  // arrived, so the last arrival of a row tile is still a down-projection tile's and runs the epilogue.
+  int nu = 0;
+#pragma unroll
+  for (int wd = 0; wd < 8; ++wd) nu += __popc(S.used[wd]);
+  const int n_empty = a.n_slots - nu;
+  if (slot0 >= 0) {
+    if (n_empty > 0)
+      for (int r = tid; r < a.n_rt; r += NT)
+        __hip_atomic_fetch_add(&a.ctr[a.c_resid_arrive + l * a.n_rt + r], (uint32_t)n_empty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&a.ctr[a.c_slots_used + l], (uint32_t)nu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // publish the entries, then release the slots (one counter each, value = routing)
   drain_stores();
@@ -1084,8 +1099,9 @@ __device__ __forceinline__ void task_up(KA& a, Desc w, int t, Lds& S) {
       const float h = gv / (1.0f + expf(-gv)) * uv;
       pub(a.h + ((int64_t)s * B + j) * F + r0 + r, h);
     }
+    signal(a, w[W_SIG], w[W_SIGN]);
   }
-  signal(a, w[W_SIG], w[W_SIGN]);
+  // an unused slot's tiles signal nothing: only the same slot's down-projection tiles wait on them
 }
 
 template <class C>
@@ -1115,8 +1131,9 @@ __device__ __forceinline__ void task_down(KA& a, Desc w, int t, Lds& S) {
           __syncthreads();
         },
         [&](int r, int j, float v) { pub(a.ypart + ((int64_t)S.slot_b[j] * a.k + S.slot_j[j]) * d + r0 + r, S.slot_g[j] * v); }, S);
+    resid_chain(a, w, S);
   }
-  resid_chain(a, w, S);
+  // an unused slot's arrival on the row tile was made by the routing workgroup
 }
 
 // LM head, the kernel's closing phase (not a task): once a workgroup's task phases are exhausted it takes
@@ -2132,15 +2149,20 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
         int start = ph == 0 ? 0 : a.ph_n[0] + l * per_layer;
         for (int j = 0; j < k; ++j) start += a.ph_n[1 + j];
         const int cnt = ph == 0 ? a.ph_n[0] : a.ph_n[1 + k];
+        // expert phases list their tiles slot by slot (cnt / n_slots per slot) and slots are numbered in
+        // ascending expert order, so once the layer is routed the tiles of unused slots are the pool's tail
+        const bool moe = ph > 0 && (a.ph_op[k] == OP_UP || a.ph_op[k] == OP_DOWN);
         if (tid == 0) S.pool_tile = (int)__hip_atomic_fetch_add(&a.ctr[a.c_phase + ph], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 1) S.pool_used = moe ? (int)__hip_atomic_load(&a.ctr[a.c_slots_used + l], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
         __syncthreads();
         const int tk = __builtin_amdgcn_readfirstlane(S.pool_tile);
+        const int nu = __builtin_amdgcn_readfirstlane(S.pool_used);
         __syncthreads();  // read by every wave before the next take overwrites it
-        if (tk < cnt) {
+        if (tk < cnt && (nu == 0 || tk < nu * (cnt / a.n_slots))) {
           pos = start + tk;
           break;
         }
-        ++ph;  // every task of this phase is taken
+        ++ph;  // every task of this phase is taken, or only unused slots' tiles are left
       }
       if (pos < 0) break;
       fetch_desc(a, pos, S.desc[cur]);

@@ -23,7 +23,8 @@ def counter_layout(L, Hkv, B, n_slots, n_rt):
     o = 0
     lay = {}
     for name, size in (("ticket", 32), ("done", 32), ("xready", L + 1), ("phase", 1 + 5 * L), ("qkv_done", L * Hkv),
-                       ("router_arrive", L), ("slot_ready", L * n_slots), ("attn_arrive", L * B * Hkv), ("attn_done", L * Hkv),
+                       ("router_arrive", L), ("slot_ready", L * n_slots), ("slots_used", L), ("attn_arrive", L * B * Hkv),
+                       ("attn_done", L * Hkv),
                        ("up_done", L * n_slots), ("resid_arrive", L * n_rt), ("lm_arrive", 1), ("lm_pool", 1)):
         lay[name] = (o, size)
         o += size
@@ -115,25 +116,44 @@ def in_order(tasks, n_counters):
     return ctr
 
 
-def check_device_counters(got, tasks, n_counters, lay, grid, vocab, slot_values):
+def check_device_counters(got, tasks, n_counters, lay, grid, vocab, slot_values, n_slots):
     """The device's final counters of a step (MK_DBGK_COUNTERS) against the plan, exactly:
     - every dependency, arrival and readiness counter equals its planned final value (the in-order
-      simulation of the list);
+      simulation of the list), except that the up-projection counter of an unused expert slot stays 0 (its
+      tiles signal nothing); a row tile's residual counter still ends at Hkv + n_slots (the routing
+      workgroup arrives for the unused slots);
     - expert-slot counters hold their slot's routing (expert + 1 in bits 0..15, token mask in bits 16..23;
-      an unused slot 0x80000000), `slot_values` computed from the slot table;
+      an unused slot 0x80000000), `slot_values` computed from the slot table, and each layer's used-slot
+      counter the number of used slots;
     - each phase pool was taken (phase size + grid) times: every task once, then one empty take per
-      workgroup (one workgroup: the in-order ticket passed the end of the list instead); the kernel's exit counter and the LM head's arrival counter equal the grid; the LM head's
-      chunk pool was claimed at least once per vocabulary chunk; with phases, the in-order ticket is unused."""
+      workgroup; an expert phase ends between (its used slots' tiles + grid) and (phase size + grid), since
+      takers leave it once the layer is routed and only unused slots' tiles remain (one workgroup: the
+      in-order ticket passed the end of the list instead);
+    - the kernel's exit counter and the LM head's arrival counter equal the grid; the LM head's chunk pool was
+      claimed at least once per vocabulary chunk; with phases, the in-order ticket is unused."""
     got = np.asarray(got, np.int64)
     exp = in_order(tasks, n_counters)
     s0, ns = lay["slot_ready"]
     exp[s0:s0 + ns] = slot_values
+    L = ns // n_slots
+    used = np.asarray(slot_values).reshape(L, n_slots) != UNUSED_SLOT
+    u0, _ = lay["slots_used"]
+    exp[u0:u0 + L] = used.sum(1)
+    d0, _ = lay["up_done"]
+    exp[d0:d0 + L * n_slots][~used.ravel()] = 0
     p0, npc = lay["phase"]
     runs = phases_of(tasks)
     assert len(runs) <= npc
     if grid >= 2:
         for p, r in enumerate(runs):
-            exp[p0 + p] = len(r) + grid
+            op = tasks[r[0], W_OP]
+            if op in (OP_UP, OP_DOWN):
+                l = tasks[r[0], W_LAYER]
+                lo = int(used[l].sum()) * (len(r) // n_slots) + grid
+                assert lo <= got[p0 + p] <= len(r) + grid, f"expert phase {p}: {got[p0 + p]} takes, outside [{lo}, {len(r) + grid}]"
+                exp[p0 + p] = got[p0 + p]
+            else:
+                exp[p0 + p] = len(r) + grid
     else:  # one workgroup claims the list in order: the ticket passes the end of the list
         tk = lay["ticket"][0]
         assert len(tasks) <= got[tk] <= len(tasks) + 3, f"ticket {got[tk]} for {len(tasks)} tasks"
@@ -146,3 +166,15 @@ def check_device_counters(got, tasks, n_counters, lay, grid, vocab, slot_values)
     exp[lm] = got[lm]
     bad = np.nonzero(got[:n_counters] != exp)[0]
     assert len(bad) == 0, f"counters differ from the plan at {bad[:8].tolist()}: device {got[bad[:8]].tolist()} plan {exp[bad[:8]].tolist()}"
+
+
+def tasks_ran(done, tasks, slot_values, n_slots):
+    """Completion counts of a step: every task once, except the expert tiles of unused slots, which run at most
+    once (a workgroup that took one before its layer was routed runs it as an empty task)."""
+    done = np.asarray(done)
+    unused = np.zeros(len(tasks), bool)
+    sv = np.asarray(slot_values).reshape(-1, n_slots)
+    moe = (tasks[:, W_OP] == OP_UP) | (tasks[:, W_OP] == OP_DOWN)
+    unused[moe] = sv[tasks[moe, W_LAYER], tasks[moe, W_A]] == UNUSED_SLOT
+    assert np.all(done[~unused] == 1), f"tasks not run exactly once: {np.nonzero((done != 1) & ~unused)[0][:10]}"
+    assert np.all(done[unused] <= 1), "an unused slot's tile ran twice"
