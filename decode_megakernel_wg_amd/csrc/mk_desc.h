@@ -10,22 +10,21 @@ namespace mk {
 
 enum Op : int32_t {
   OP_EMBED = 1,   // x[b][rows] = embed[token_b][rows]; partial sum of squares of the rows  -> XREADY[0]
-  OP_ROUTER = 2,  // (reserved: router logits are partials of the residual row tiles; the last tile routes)
   OP_QKV = 3,     // rows [r0, r1) of KV group g's fused [q heads; k; v] projection     -> QKV_DONE[l][g]
   OP_ATTN = 4,    // split s of (sequence b, KV group g): partial softmax(qK^T)V; last arriver combines -> ATTN_DONE[l][g]
   OP_UP = 5,      // gate+up rows [r0, r1) of expert slot s, SwiGLU (waits SLOT_READY)     -> UP_DONE[l][s]
   OP_OPROJ = 6,   // rows [r0, r1) of Wo restricted to group g's columns; residual epilogue (see below)
-  OP_DOWN = 7,    // rows [r0, r1) of expert slot s's down projection, times the gate; residual epilogue
-  OP_RESID = 8,   // (reserved: the residual add is the epilogue of the last O-proj / down task of a row tile)
-  OP_LMHEAD = 9,  // (reserved: the LM head runs as the kernel's closing phase over a shared chunk pool)
-  OP_COUNT = 10
+  OP_DOWN = 7     // rows [r0, r1) of expert slot s's down projection, times the gate; residual epilogue
 };
+// The router is not a task (the last residual row tile of a layer routes the next), nor is the residual add
+// (the epilogue of a row tile's last O-proj or down-projection task), nor the LM head (the kernel's closing
+// phase over a shared chunk pool).
 
 // Descriptor words.
 enum Word : int {
   W_OP = 0,
   W_LAYER = 1,
-  W_A = 2,  // EMBED/RESID: row tile; QKV/OPROJ: KV group; UP/DOWN: slot; ATTN: sequence; LMHEAD: tile
+  W_A = 2,  // EMBED: row tile; QKV/OPROJ: KV group; UP/DOWN: slot; ATTN: sequence
   W_B = 3,  // ATTN: KV group
   W_C = 4,  // ATTN: split index
   W_D = 5,  // ATTN: split count
@@ -36,8 +35,7 @@ enum Word : int {
   W_SIGN = 17,  // increment
   W_ARR = 18,   // arrival counter for the last-arriver epilogue (-1 = none)
   W_ARRN = 19,  // arrivals expected
-  W_SIGR = 20,  // counters signalled: [W_SIG, W_SIG + W_SIGR) (router: one per expert slot, the value
-                // written there is the slot's routing, at least 1)
+  W_SIGR = 20,  // counters signalled: [W_SIG, W_SIG + W_SIGR) (1 for every task of this planner)
   W_RT = 22,    // residual row tile of OPROJ / DOWN / EMBED tasks
   W_ARR2 = 24,  // row-tile tasks: arrival counter of the next layer's router partials (-1 = none: last layer)
   W_ARRN2 = 25, // arrivals expected there (row tiles)

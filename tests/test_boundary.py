@@ -9,7 +9,7 @@ import pytest
 
 from decode_megakernel_wg_amd import mk
 from synth import workloads as W
-from taskgraph import (OP_ATTN, OP_EMBED, OP_LMHEAD, W_ARR, W_D, W_LAYER, W_OP, W_R0, W_R1, W_SIG, W_WAIT0, complete, counter_layout,
+from taskgraph import (OP_ATTN, OP_EMBED, W_ARR, W_D, W_LAYER, W_OP, W_R0, W_R1, W_SIG, W_WAIT0, complete, counter_layout,
                        phases_of, simulate)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -110,7 +110,8 @@ def test_task_counts_full_model():
     d = desc_for(W.FULL, B=1, pages=600, n_pages=600)
     tasks, _ = mk.mk_plan_tasks(d, [8192])
     ops = np.bincount(tasks[:, W_OP], minlength=10)
-    assert ops[OP_LMHEAD] == 0   # the LM head is the kernel's closing phase, not tasks
+    # the LM head, the router and the residual add are not tasks
+    assert set(np.unique(tasks[:, W_OP]).tolist()) == {1, 3, 4, 5, 6, 7}
     # about 96 splits per layer: 8192 cached positions x 4 KV groups / 96 = 341 -> 384 positions (3 chunks of
     # 128) per split, 22 splits per KV group; the last split of each (sequence, group) takes the rest (128
     # cached positions) and the new token
@@ -178,6 +179,8 @@ def test_counter_layout_mirror(shape, lens):
             assert inside(w[W_WAIT0], "xready") and inside(w[W_SIG], "qkv_done")
         if op == OP_ATTN:
             assert inside(w[W_WAIT0], "qkv_done") and inside(w[W_ARR], "attn_arrive") and inside(w[W_SIG], "attn_done")
+        if op == 6:
+            assert inside(w[W_WAIT0], "attn_done")
         if op == 5:
             assert inside(w[W_WAIT0], "slot_ready") and inside(w[W_SIG], "up_done")
         if op in (6, 7):
