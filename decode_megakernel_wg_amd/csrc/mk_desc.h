@@ -70,7 +70,9 @@ constexpr int ATTN_MAX_SPLITS = 256;
 constexpr int SLOT_WORDS = 32;
 constexpr int LM_MAX_WG = 1024;  // most workgroups a launch may have (stride of the LM head's per-workgroup bests)  // routing table entry per expert slot: expert, token count, (token, rank, gate) x 8
 
-// Counter index layout for a model/batch; computed identically by planner and host launcher.
+// Counter index layout for a model/batch; computed identically by planner and host launcher.  Counter c lives
+// at word c * CTR_STRIDE of the counter array (one 128-byte line per counter).
+constexpr int CTR_STRIDE = 32;
 struct CounterLayout {
   int32_t ticket, done, xready, phase, qkv_done, router_arrive, slot_ready, slots_used, attn_arrive, attn_done, up_done,
       resid_arrive, lm_arrive, lm_pool, total;

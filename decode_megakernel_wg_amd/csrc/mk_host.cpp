@@ -173,7 +173,7 @@ int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out
   for (int i = 0; i < dh / 2; ++i) invf[i] = std::pow((double)desc->rope_base, -2.0 * i / dh);
 
   if ((rc = m->alloc(&m->layers, L)) || (rc = m->alloc(&m->router_bias, E)) || (rc = m->alloc(&m->inv_freq, dh / 2)) ||
-      (rc = m->alloc(&m->tasks, (size_t)m->max_tasks * mk::DESC_WORDS)) || (rc = m->alloc(&m->ctr, m->max_counters)) ||
+      (rc = m->alloc(&m->tasks, (size_t)m->max_tasks * mk::DESC_WORDS)) || (rc = m->alloc(&m->ctr, (size_t)m->max_counters * mk::CTR_STRIDE)) ||
       (rc = m->alloc(&m->err, 8)) || (rc = m->alloc(&m->x, (size_t)maxB * d)) || (rc = m->alloc(&m->ssq, (size_t)maxB * t.n_rt)) ||
       (rc = m->alloc(&m->rope_cs, (size_t)maxB * dh)) || (rc = m->alloc(&m->qkv, (size_t)maxB * Hkv * (grp + 2) * dh)) ||
       (rc = m->alloc(&m->apart, (size_t)maxB * Hkv * mk::ATTN_MAX_SPLITS * grp * (dh + 2))) ||
@@ -389,7 +389,7 @@ int mk_status(mk_model* m, void* stream) {
   const uint32_t c = e[mk::ERR_CODE];
   std::string msg = std::string("device fault: ") + (c < 6 ? names[c] : "unknown") + " (task " + std::to_string(e[mk::ERR_TASK]) + ")";
   HIPCHK(hipMemset(m->err, 0, sizeof(e)));
-  HIPCHK(hipMemset(m->ctr, 0, sizeof(uint32_t) * m->max_counters));
+  HIPCHK(hipMemset(m->ctr, 0, sizeof(uint32_t) * m->max_counters * mk::CTR_STRIDE));
   return fail(MK_E_DEVICE, msg);
 }
 

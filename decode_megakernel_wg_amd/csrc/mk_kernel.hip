@@ -159,6 +159,10 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(rdl(v, 0), rdl(v, 16)), fmaxf(rdl(v, 32), rdl(v, 48)));
 }
 
+// Counter c.  Counters lie one 128-byte line apart: every workgroup polls and adds to them, and counters that
+// share a line (the phase pools, a layer's readiness counters) would serialize each other's atomics.
+__device__ __forceinline__ uint32_t* ctr_at(KA& a, int64_t c) { return a.ctr + c * CTR_STRIDE; }
+
 __device__ __forceinline__ void raise_error(KA& a, uint32_t code, int task) {
   if (atomicCAS(&a.err[ERR_CODE], 0u, code) == 0u) atomicExch(&a.err[ERR_TASK], (uint32_t)task);
   __hip_atomic_store(&a.err[ERR_ABORT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -170,7 +174,7 @@ __device__ __forceinline__ void raise_error(KA& a, uint32_t code, int task) {
 __device__ __forceinline__ uint32_t spin_ge(KA& a, int32_t c, int32_t target, int task) {
   if (c < 0) return 0u;
   uint32_t n = 0, v;
-  while ((v = __hip_atomic_load(&a.ctr[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < (uint32_t)target) {
+  while ((v = __hip_atomic_load(ctr_at(a, c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < (uint32_t)target) {
     if ((++n & 63) == 0) {
       if (__hip_atomic_load(&a.err[ERR_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return 0u;
       if (n > a.spin_limit) {
@@ -215,7 +219,7 @@ __device__ __forceinline__ uint32_t wait_value(KA& a, Desc w, int i, int task, L
 __device__ __forceinline__ void signal(KA& a, int32_t c, int32_t n) {
   drain_stores();
   __syncthreads();
-  if (tidx() == 0 && c >= 0) __hip_atomic_fetch_add(&a.ctr[c], (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tidx() == 0 && c >= 0) __hip_atomic_fetch_add(ctr_at(a, c), (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Arrive on a last-arriver counter; returns true (to every thread) in the workgroup that arrives last.
@@ -223,7 +227,7 @@ __device__ __forceinline__ bool arrive_last(KA& a, int32_t c, int32_t n, Lds& S)
   drain_stores();
   __syncthreads();
   if (tidx() == 0) {
-    uint32_t old = __hip_atomic_fetch_add(&a.ctr[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t old = __hip_atomic_fetch_add(ctr_at(a, c), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     S.flag = (old == (uint32_t)(n - 1));
     if (S.flag) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
@@ -445,13 +449,13 @@ __device__ __forceinline__ void route_select(KA& a, int l, int32_t slot0, Lds& S
   if (slot0 >= 0) {
     if (n_empty > 0)
       for (int r = tid; r < a.n_rt; r += NT)
-        __hip_atomic_fetch_add(&a.ctr[a.c_resid_arrive + l * a.n_rt + r], (uint32_t)n_empty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid == 0) __hip_atomic_store(&a.ctr[a.c_slots_used + l], (uint32_t)nu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(ctr_at(a, a.c_resid_arrive + l * a.n_rt + r), (uint32_t)n_empty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(ctr_at(a, a.c_slots_used + l), (uint32_t)nu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // publish the entries, then release the slots (one counter each, value = routing)
   drain_stores();
   __syncthreads();
-  if (tid < a.n_slots && slot0 >= 0) __hip_atomic_store(&a.ctr[slot0 + tid], sv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid < a.n_slots && slot0 >= 0) __hip_atomic_store(ctr_at(a, slot0 + tid), sv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Residual rows [r0, r1): x += sum over KV groups of the O-projection partials + sum over the k selections
@@ -1155,7 +1159,7 @@ __device__ __forceinline__ void lm_phase(KA& a, Lds& S) {
   const NormGain gn = norm_gain(a.final_norm, d);
   if (tidx() == 0)
     for (int k = 0; k < ahead; ++k)
-      S.lmq[k] = (int)__hip_atomic_fetch_add(&a.ctr[a.c_lm_pool], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      S.lmq[k] = (int)__hip_atomic_fetch_add(ctr_at(a, a.c_lm_pool), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   auto load = [&](MBuf& buf, int q) {
     const int k = q / np, p = q - k * np;
@@ -1194,7 +1198,7 @@ __device__ __forceinline__ void lm_phase(KA& a, Lds& S) {
           if (tidx() == 0) S.lmq[(k - 1 + ahead) % LMQ] = (int)pend;
           __syncthreads();
         }
-        if (tidx() == 0) pend = __hip_atomic_fetch_add(&a.ctr[a.c_lm_pool], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tidx() == 0) pend = __hip_atomic_fetch_add(ctr_at(a, a.c_lm_pool), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         macc_zero(acc);
       }
       const int id = S.lmq[k % LMQ];
@@ -2089,15 +2093,15 @@ __device__ __forceinline__ void exit_step(KA& a, Lds& S) {
   const int tid = tidx();
   __syncthreads();
   if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&a.ctr[a.c_done], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(ctr_at(a, a.c_done), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     S.flag = (old == gridDim.x - 1);
     if (S.flag) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
   if (S.flag) {
     if (a.ctr_snapshot)
-      for (int i = tid; i < a.n_counters; i += NT) a.ctr_snapshot[i] = a.ctr[i];
-    for (int i = tid; i < a.n_counters; i += NT) __hip_atomic_store(&a.ctr[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = tid; i < a.n_counters; i += NT) a.ctr_snapshot[i] = *ctr_at(a, i);
+    for (int i = tid; i < a.n_counters; i += NT) __hip_atomic_store(ctr_at(a, i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -2126,12 +2130,12 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
   if (tid == 0) {
     S.xb_layer = 0;
     S.route_layer = 0;
-    if (!phases) S.next1 = (int)__hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!phases) S.next1 = (int)__hip_atomic_fetch_add(ctr_at(a, ticket), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   int i = phases ? count : S.next1;
   if (i < count) fetch_desc(a, base + i, S.desc[0]);
-  if (tid == 0 && !phases) S.next1 = (int)__hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0 && !phases) S.next1 = (int)__hip_atomic_fetch_add(ctr_at(a, ticket), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   drain_stores();
   __syncthreads();
   const int npl = a.ph_npl, nph = 1 + npl * a.L;
@@ -2152,8 +2156,8 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
         // expert phases list their tiles slot by slot (cnt / n_slots per slot) and slots are numbered in
         // ascending expert order, so once the layer is routed the tiles of unused slots are the pool's tail
         const bool moe = ph > 0 && (a.ph_op[k] == OP_UP || a.ph_op[k] == OP_DOWN);
-        if (tid == 0) S.pool_tile = (int)__hip_atomic_fetch_add(&a.ctr[a.c_phase + ph], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (tid == 1) S.pool_used = moe ? (int)__hip_atomic_load(&a.ctr[a.c_slots_used + l], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        if (tid == 0) S.pool_tile = (int)__hip_atomic_fetch_add(ctr_at(a, a.c_phase + ph), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 1) S.pool_used = moe ? (int)__hip_atomic_load(ctr_at(a, a.c_slots_used + l), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
         __syncthreads();
         const int tk = __builtin_amdgcn_readfirstlane(S.pool_tile);
         const int nu = __builtin_amdgcn_readfirstlane(S.pool_used);
@@ -2173,7 +2177,7 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
       i1 = S.next1;
       __syncthreads();
       if (i1 < count) fetch_desc(a, base + i1, S.desc[cur ^ 1]);
-      if (tid == 0) i2 = __hip_atomic_fetch_add(&a.ctr[ticket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) i2 = __hip_atomic_fetch_add(ctr_at(a, ticket), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     const Desc w{S.desc[cur]};
     run_task<C>(a0, w, w[W_SEQ], S);
