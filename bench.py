@@ -78,7 +78,7 @@ def unique_experts_per_layer(sess):
     return [len(np.unique(sel[l])) for l in range(s.n_layers)]
 
 
-def run_gpu(workload, steps, warmup, model=None):
+def run_gpu(workload, steps, warmup, model=None, gemv="mfma"):
     import numpy as np
     import torch
 
@@ -93,6 +93,10 @@ def run_gpu(workload, steps, warmup, model=None):
         model = W.DeviceModel(w.shape)
     log(f"generating KV prefixes {w.ctx}")
     sess = Session(w, model=model)
+    if gemv == "valu":  # GEMV tiles on the VALU instead of the matrix cores (batch 1; engine comparison)
+        from decode_megakernel_wg_amd import mk
+
+        sess.h.mk_debug_set(mk.MK_DBG_VALU_GEMV)
     torch.cuda.synchronize()
     log(f"setup {time.time() - t0:.1f} s; warmup {warmup} steps")
     for _ in range(warmup):
@@ -290,6 +294,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="b1_8k", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gemv", choices=("mfma", "valu"), default="mfma",
+                    help="engine of the GEMV tiles at batch 1: matrix cores (default) or VALU, for comparing the two")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
@@ -303,7 +309,7 @@ def main():
 
     if args.workload == "continuous":
         return main_continuous(args)
-    r = run_gpu(args.workload, args.steps, args.warmup)
+    r = run_gpu(args.workload, args.steps, args.warmup, gemv=args.gemv)
     w = r["w"]
     achieved = r["avg_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
     sol_tok_s = R.sol_tokens_per_s(r["avg_bytes"], w.B)
@@ -322,6 +328,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}", "global_batch": w.B,
                    "seq_len": int(max(w.ctx)), "parallelism": "single GPU, persistent megakernel"},
+        "gemv_engine": args.gemv if w.B == 1 else "mfma",
         "sol_tok_s": round(sol_tok_s, 1),
         "pct_of_sol": round(100 * r["tok_s"] / sol_tok_s, 2),
         "sol_bytes_per_step": int(r["avg_bytes"]),

@@ -13,7 +13,7 @@
 #include "mk_kargs.h"
 #include "mk_plan.h"
 
-extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int kclass, int grid, int wide, hipStream_t stream);
+extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int kclass, int grid, int mode, hipStream_t stream);
 extern "C" int mk_kernel_class(int d_head, int group, int d_model, int d_ffn);
 
 namespace {
@@ -281,7 +281,7 @@ static int launch_step(mk_model* m, const int32_t* tokens, const int32_t* seq_le
     m->upload_pending = true;
     m->dirty = false;
   }
-  if (m->task_done) HIPCHK(hipMemsetAsync(m->task_done, 0, sizeof(uint32_t) * P.n_tasks(), s));
+  if (m->task_done && (m->dbg & MK_DBG_COUNT_TASKS)) HIPCHK(hipMemsetAsync(m->task_done, 0, sizeof(uint32_t) * P.n_tasks(), s));
   if (m->ts && (m->dbg & MK_DBG_TIMESTAMPS)) HIPCHK(hipMemsetAsync(m->ts, 0, sizeof(uint64_t) * 8 * P.n_tasks(), s));
   if (m->pagewalk && (m->dbg & MK_DBG_PAGE_WALK))
     HIPCHK(hipMemsetAsync(m->pagewalk, 0, sizeof(uint32_t) * 4 * m->desc.n_layers * P.B * m->desc.n_kv_heads, s));
@@ -351,12 +351,12 @@ static int launch_step(mk_model* m, const int32_t* tokens, const int32_t* seq_le
   a.lmbest_i = m->lmbest_i;
   a.next_tok = m->next_tok;
   a.dump_n = (m->dbg & MK_DBG_DUMP_N) ? m->dump_n : nullptr;
-  a.task_done = m->task_done;
+  a.task_done = (m->dbg & MK_DBG_COUNT_TASKS) ? m->task_done : nullptr;
   a.ts = (m->dbg & MK_DBG_TIMESTAMPS) ? m->ts : nullptr;
   a.ctr_snapshot = m->ctr_snapshot;
   a.pagewalk = (m->dbg & MK_DBG_PAGE_WALK) ? m->pagewalk : nullptr;
   a.spin_limit = (m->dbg & MK_DBG_DROP_SIGNAL) ? (1u << 12) : (1u << 21);
-  HIPCHK(mk_launch_persistent(&a, m->kclass, m->grid, (m->dbg & MK_DBG_WIDE_GEMV) ? 1 : 0, s));
+  HIPCHK(mk_launch_persistent(&a, m->kclass, m->grid, (m->dbg & MK_DBG_WIDE_GEMV) ? 1 : (m->dbg & MK_DBG_VALU_GEMV) ? 2 : 0, s));
   m->stepped = true;
   return MK_OK;
 }
@@ -399,7 +399,7 @@ int mk_debug_set(mk_model* m, uint32_t flags) {
     int rc = m->alloc(&m->dump_n, (size_t)m->desc.n_layers * m->desc.max_batch * m->desc.d_model);
     if (rc) return rc;
   }
-  if (!m->task_done) {
+  if ((flags & MK_DBG_COUNT_TASKS) && !m->task_done) {
     int rc = m->alloc(&m->task_done, (size_t)m->max_tasks);
     if (rc) return rc;
   }
@@ -435,7 +435,7 @@ int mk_debug_read(mk_model* m, int kind, void* host_dst, int64_t bytes) {
       break;
     case MK_DBGK_COUNTERS: src = m->ctr_snapshot; avail = (int64_t)m->plan.cl.total * 4; break;
     case MK_DBGK_TASK_DONE:
-      if (!m->task_done) return fail(MK_E_STATE, "mk_debug_set has not been called");
+      if (!(m->dbg & MK_DBG_COUNT_TASKS)) return fail(MK_E_STATE, "MK_DBG_COUNT_TASKS is not enabled");
       src = m->task_done;
       avail = m->plan.n_tasks() * 4;
       break;

@@ -46,7 +46,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 template <int DH_, int GRP_, int NVD_, int NVF_, int NVO_, int NB_>
 struct Cfg {
   static constexpr int DH = DH_, GRP = GRP_, NVD = NVD_, NVF = NVF_, NVO = NVO_;
-  static constexpr int NB = NB_;  // batch class of the matrix-core GEMV: at most 2, or at most 8 tokens
+  // batch class of the GEMV tiles: at most 2 tokens (2) or at most 8 (8) on the matrix cores, or one token with the
+  // VALU dot-product engine in the GEMV tiles (1; everything else as class 2)
+  static constexpr int NB = NB_;
 };
 // Global-address-space views: loads through them are global_load (vmcnt only), never flat loads,
 // which would also count against lgkmcnt and make every LDS wait wait for in-flight weight loads.
@@ -881,6 +883,90 @@ __device__ __forceinline__ void split_x(int nb, int K, Lds& S) {
   lds_sync();
 }
 
+// VALU engine of the GEMV tiles (batch class 1: one token; selected by MK_DBG_VALU_GEMV to compare the two
+// engines on the same loads): lane l's 16-byte weight chunk of quad q and K block kb (the row-quad layout
+// above) times the 8 activations of the same chunk, as fp32 FMAs into one partial per quad; the activations
+// are the BF16 hi + lo parts added back in fp32 (exact: the same operand the matrix cores see).
+struct VAcc {
+  float v[4];  // [quad]
+};
+template <int KB, int KB0 = 0>
+__device__ __forceinline__ void mgv_compute_kb(const MBuf& buf, VAcc& acc, const MGeo& g, int pass, Lds& S) {
+  const int wave = tidx() >> 6, lane = tidx() & 63;
+  const int rb = wave / g.ks, kp = wave - rb * g.ks;
+  if (rb >= g.rbn) return;
+  const int c = mg_col(g, kp, pass, lane) + 128 * KB0;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    __builtin_amdgcn_sched_barrier(0);  // one K block's operands live at a time (no hoisting across blocks)
+    const u4 hv = lds16(S.xb + xb_off(0, 0) + c + 128 * kb), lv = lds16(S.xb + xb_off(0, 1) + c + 128 * kb);
+    const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w}, lw[4] = {lv.x, lv.y, lv.z, lv.w};
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf_lo(hw[i]) + bf_lo(lw[i]);
+      x[2 * i + 1] = bf_hi(hw[i]) + bf_hi(lw[i]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u4 wv = buf.v[4 * (KB0 + kb) + q];
+      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc.v[q] = fmaf(bf_lo(ww[i]), x[2 * i], acc.v[q]);
+        acc.v[q] = fmaf(bf_hi(ww[i]), x[2 * i + 1], acc.v[q]);
+      }
+    }
+  }
+}
+__device__ __forceinline__ void mgv_compute_any(const MBuf& buf, VAcc& acc, const MGeo& g, int pass, Lds& S) {
+  const int left = g.nkb - 4 * pass;
+  if (left >= 4) {
+    mgv_compute_kb<4>(buf, acc, g, pass, S);
+  } else if (left >= 2) {
+    mgv_compute_kb<2>(buf, acc, g, pass, S);
+    if (left == 3) mgv_compute_kb<1, 2>(buf, acc, g, pass, S);
+  } else {
+    mgv_compute_kb<1>(buf, acc, g, pass, S);
+  }
+}
+// Row 4q + rr of the row block (rr = (lane % 16) / 4) is spread over the 16 lanes with that rr (lane % 4 and
+// lane / 16 free): added across them (two DPP steps, two lane swaps), then the K-slice partials of the block
+// in a fixed order through LDS; lanes 0, 4, 8, 12 hand (row, token 0, value) to out().
+template <class Out>
+__device__ __forceinline__ void mgv_finish(const VAcc& acc, const MGeo& g, Out& out, Lds& S) {
+  const int wave = tidx() >> 6, lane = tidx() & 63;
+  const int rb = wave / g.ks, kp = wave - rb * g.ks;
+  float r[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float v = acc.v[q];
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    r[q] = v;
+  }
+  const bool lead = rb < g.rbn && lane < 16 && (lane & 3) == 0;
+  if (g.ks > 1) {
+    float* red = S.pt;  // [NW][4 quads][4 rows]
+    if (lead)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) red[(wave * 4 + q) * 4 + (lane >> 2)] = r[q];
+    __syncthreads();
+    if (kp == 0 && lead)
+      for (int p = 1; p < g.ks; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] += red[((wave + p) * 4 + q) * 4 + (lane >> 2)];
+  }
+  if (kp == 0 && lead)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = rb * 16 + 4 * q + (lane >> 2);
+      if (row < g.nrows) out(row, 0, r[q]);
+    }
+}
+
 // Prefetch, wait, stage, stream.  The first `ahead` passes of the tile (16 KB per wave each) are requested
 // before the dependency wait [wait0, wait1), so weights stream while the inputs are still being produced;
 // afterwards pass p+1 is requested before pass p is computed.  A tile that stages its inputs only after
@@ -898,16 +984,30 @@ __device__ __forceinline__ void mgemv_task(KA& a, Desc w, int t, const RowPtr& W
   if (SPLIT) split_x(nb, K, S);
   if (ahead == 1 && g.np > 1) mg_load(b1, W, g, 1);
   mark(a, t, 0);
-  MAcc acc;
-  macc_zero(acc);
-  for (int p = 0; p < g.np; p += 2) {
-    mg_compute_any<NB>(b0, acc, g, p, nb, S);
-    if (p + 2 < g.np) mg_load(b0, W, g, p + 2);
-    if (p + 1 >= g.np) break;
-    mg_compute_any<NB>(b1, acc, g, p + 1, nb, S);
-    if (p + 3 < g.np) mg_load(b1, W, g, p + 3);
+  if constexpr (NB == 1) {  // one token (the class is launched for batches of 1 only)
+    VAcc acc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc.v[q] = 0.f;
+    for (int p = 0; p < g.np; p += 2) {
+      mgv_compute_any(b0, acc, g, p, S);
+      if (p + 2 < g.np) mg_load(b0, W, g, p + 2);
+      if (p + 1 >= g.np) break;
+      mgv_compute_any(b1, acc, g, p + 1, S);
+      if (p + 3 < g.np) mg_load(b1, W, g, p + 3);
+    }
+    mgv_finish(acc, g, out, S);
+  } else {
+    MAcc acc;
+    macc_zero(acc);
+    for (int p = 0; p < g.np; p += 2) {
+      mg_compute_any<NB>(b0, acc, g, p, nb, S);
+      if (p + 2 < g.np) mg_load(b0, W, g, p + 2);
+      if (p + 1 >= g.np) break;
+      mg_compute_any<NB>(b1, acc, g, p + 1, nb, S);
+      if (p + 3 < g.np) mg_load(b1, W, g, p + 3);
+    }
+    mg_finish<NB>(acc, g, nb, out, S);
   }
-  mg_finish<NB>(acc, g, nb, out, S);
   mark(a, t, 1);
 }
 
@@ -2200,8 +2300,10 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
 // classes (at most 2 tokens: one MFMA per weight block; at most 8: hi and lo MFMAs for each group of 4).
 using CfgFull2 = mk::Cfg<128, 8, 4, 2, 2, 2>;  // d_head 128, group 8, d_model <= 2048, d_ffn <= 1024, group*d_head = 1024
 using CfgFull8 = mk::Cfg<128, 8, 4, 2, 2, 8>;
+using CfgFull1 = mk::Cfg<128, 8, 4, 2, 2, 1>;  // one token, VALU GEMV tiles
 using CfgTiny2 = mk::Cfg<64, 2, 1, 1, 1, 2>;   // d_head 64, group 2, d_model <= 512, d_ffn <= 512, group*d_head = 128
 using CfgTiny8 = mk::Cfg<64, 2, 1, 1, 1, 8>;
+using CfgTiny1 = mk::Cfg<64, 2, 1, 1, 1, 1>;
 
 extern "C" int mk_kernel_class(int d_head, int group, int d_model, int d_ffn) {
   if (d_head == 128 && group == 8 && d_model <= 64 * 8 * CfgFull2::NVD && d_ffn <= 64 * 8 * CfgFull2::NVF) return 1;
@@ -2209,10 +2311,14 @@ extern "C" int mk_kernel_class(int d_head, int group, int d_model, int d_ffn) {
   return 0;
 }
 
-extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int kclass, int grid, int wide, hipStream_t stream) {
-  const bool small = a->B <= 2 && !wide;
-  if (kclass == 1 && small) hipLaunchKernelGGL(mk::mk_persistent<CfgFull2>, dim3(grid), dim3(mk::NT), 0, stream, *a);
+// mode 0: batch class by batch size; 1: the 8-token class at every batch size; 2: the VALU GEMV class at batch 1
+// (larger batches as mode 0).
+extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int kclass, int grid, int mode, hipStream_t stream) {
+  const bool small = a->B <= 2 && mode != 1, valu = a->B == 1 && mode == 2;
+  if (kclass == 1 && valu) hipLaunchKernelGGL(mk::mk_persistent<CfgFull1>, dim3(grid), dim3(mk::NT), 0, stream, *a);
+  else if (kclass == 1 && small) hipLaunchKernelGGL(mk::mk_persistent<CfgFull2>, dim3(grid), dim3(mk::NT), 0, stream, *a);
   else if (kclass == 1) hipLaunchKernelGGL(mk::mk_persistent<CfgFull8>, dim3(grid), dim3(mk::NT), 0, stream, *a);
+  else if (kclass == 2 && valu) hipLaunchKernelGGL(mk::mk_persistent<CfgTiny1>, dim3(grid), dim3(mk::NT), 0, stream, *a);
   else if (kclass == 2 && small) hipLaunchKernelGGL(mk::mk_persistent<CfgTiny2>, dim3(grid), dim3(mk::NT), 0, stream, *a);
   else if (kclass == 2) hipLaunchKernelGGL(mk::mk_persistent<CfgTiny8>, dim3(grid), dim3(mk::NT), 0, stream, *a);
   else return hipErrorInvalidValue;

@@ -153,7 +153,12 @@ int mk_status(mk_model* m, void* stream);
  * batches of 1-2 sequences with the matrix-core arithmetic of batches of 3-8 (hi and lo activation parts in
  * separate instructions accumulating into one sum), so that a sequence's results then equal, bit for bit,
  * its results inside a larger batch; without it the two batch classes agree to rounding only. */
-enum { MK_DBG_DUMP_N = 1, MK_DBG_TIMESTAMPS = 2, MK_DBG_WIDE_GEMV = 4, MK_DBG_PAGE_WALK = 8, MK_DBG_DROP_SIGNAL = 16 };
+enum { MK_DBG_DUMP_N = 1, MK_DBG_TIMESTAMPS = 2, MK_DBG_WIDE_GEMV = 4, MK_DBG_PAGE_WALK = 8, MK_DBG_DROP_SIGNAL = 16,
+       MK_DBG_VALU_GEMV = 32, MK_DBG_COUNT_TASKS = 64 };
+/* MK_DBG_COUNT_TASKS counts every task's completions (MK_DBGK_TASK_DONE). */
+/* MK_DBG_VALU_GEMV runs the GEMV tiles of a batch of one sequence on the VALU (fp32 FMAs on the same loads and
+ * the same hi + lo activations) instead of the matrix cores, to compare the two engines; results agree to
+ * rounding.  MK_DBG_WIDE_GEMV takes precedence. */
 /* MK_DBG_PAGE_WALK records every attention page walk (MK_DBGK_PAGE_WALK).  MK_DBG_DROP_SIGNAL exercises the
  * device watchdog from the host: the uploaded task list loses the completion signal of its first QKV task
  * and dependency waits give up after 4096 polls (about 2 ms instead of about 1 s), so the step ends with
@@ -165,7 +170,7 @@ enum {
   MK_DBGK_NORM_IN = 4,       /* fp32  [n_layers][batch][d_model]: each layer's RMSNorm output (MK_DBG_DUMP_N) */
   MK_DBGK_COUNTERS = 5,      /* uint32 [n_counters]: final values of the last step, copied just before the kernel
                                 resets them to zero for the next step (always recorded) */
-  MK_DBGK_TASK_DONE = 6,     /* uint32 [n_tasks]: completions per task in the last step (must be 1 each) */
+  MK_DBGK_TASK_DONE = 6,     /* uint32 [n_tasks]: completions per task in the last step (MK_DBG_COUNT_TASKS) */
   MK_DBGK_TIMESTAMPS = 7,    /* uint64 [n_tasks][8]: claim, dependencies met, end (100 MHz wall clock), hardware id
                                 (XCC id << 32 | HW_ID register), then up to 4 task-specific sub-phase marks (0 = unset);
                                 MK_DBG_TIMESTAMPS */

@@ -31,7 +31,7 @@ def _run(shape, n_steps, n_pages=None, **kw):
     from oracle import oracle as O
 
     sess = ContinuousSession(shape, n_steps, n_pages=n_pages, **kw)
-    sess.h.mk_debug_set(mk.MK_DBG_PAGE_WALK)  # per-task completion counts and page walks
+    sess.h.mk_debug_set(mk.MK_DBG_PAGE_WALK | mk.MK_DBG_COUNT_TASKS)  # page walks and per-task completion counts
     w = W.Workload("continuous", shape, [], n_steps)
     orc = OracleRun(w, np.zeros((0, sess.max_pages), np.int32), sess.n_pages, keep_all=None)
     s = shape

@@ -88,7 +88,7 @@ def _teacher_forced_router(sess, w):
             assert np.allclose(lg, rl[l, b], rtol=1e-5, atol=1e-6), f"{w.name}: router logits differ at layer {l} seq {b}"
 
 
-def _run(name, steps, teacher_forced_step=None, lazy=False):
+def _run(name, steps, teacher_forced_step=None, lazy=False, extra_flags=0):
     from decode_megakernel_wg_amd import mk
     from decode_megakernel_wg_amd.session import Session
 
@@ -101,7 +101,7 @@ def _run(name, steps, teacher_forced_step=None, lazy=False):
     tokens = list(w.tokens)
     agree, worst = 0, 0.0
     for step in range(steps):
-        flags = mk.MK_DBG_PAGE_WALK | (mk.MK_DBG_DUMP_N if step == teacher_forced_step else 0)
+        flags = mk.MK_DBG_PAGE_WALK | mk.MK_DBG_COUNT_TASKS | extra_flags | (mk.MK_DBG_DUMP_N if step == teacher_forced_step else 0)
         sess.h.mk_debug_set(flags)
         sess.step()
         sess.status()
@@ -119,6 +119,14 @@ def _run(name, steps, teacher_forced_step=None, lazy=False):
 @pytest.mark.timeout(900)
 def test_full_b1_8k():
     _run("b1_8k", steps=16, teacher_forced_step=1)
+
+
+@pytest.mark.timeout(600)
+def test_full_b1_8k_valu_gemv():
+    """The VALU engine of the GEMV tiles at batch 1 (MK_DBG_VALU_GEMV), same bar."""
+    from decode_megakernel_wg_amd import mk
+
+    _run("b1_8k", steps=2, teacher_forced_step=0, extra_flags=mk.MK_DBG_VALU_GEMV)
 
 
 @pytest.mark.timeout(600)

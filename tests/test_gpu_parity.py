@@ -38,7 +38,7 @@ def run_parity(w, steps, check_router_inputs=True, grid=None, flags=0):
     sess = _session(w, pt=pt, n_pages=n_pages)
     if grid:
         sess.h.mk_set_grid(grid)
-    sess.h.mk_debug_set(mk.MK_DBG_DUMP_N | mk.MK_DBG_PAGE_WALK | flags)
+    sess.h.mk_debug_set(mk.MK_DBG_DUMP_N | mk.MK_DBG_PAGE_WALK | mk.MK_DBG_COUNT_TASKS | flags)
     orc = OracleRun(w, pt, n_pages)
     s = w.shape
     tokens = list(w.tokens)
@@ -90,6 +90,16 @@ def test_tiny_16_steps():
     w = W.make("tiny")
     sess, orc, worst = run_parity(w, w.steps)
     print(f"tiny: worst logits rel L2 {worst:.2e}, routing near-ties {orc.near_ties}/{orc.route_checked}")
+    _check_kv(sess, orc)
+
+
+def test_tiny_valu_gemv():
+    """The VALU engine of the GEMV tiles (MK_DBG_VALU_GEMV, batch 1) against the oracle, same bar."""
+    from decode_megakernel_wg_amd import mk
+
+    w = W.make("tiny", steps=6)
+    sess, orc, worst = run_parity(w, w.steps, flags=mk.MK_DBG_VALU_GEMV)
+    print(f"tiny, VALU GEMV: worst logits rel L2 {worst:.2e}")
     _check_kv(sess, orc)
 
 

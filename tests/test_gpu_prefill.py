@@ -54,7 +54,7 @@ class Seqs:
                        wo=m.wo, w_router=m.w_router, w_gate=m.w_gate, w_up=m.w_up, w_down=m.w_down)
         self.desc = mk.make_desc(s, 8, self.max_pages, self.n_pages)
         self.h = mk.Model(self.desc, weights)
-        self.h.mk_debug_set(mk.MK_DBG_PAGE_WALK)
+        self.h.mk_debug_set(mk.MK_DBG_PAGE_WALK | mk.MK_DBG_COUNT_TASKS)
         self.logits = torch.empty(8, s.vocab, dtype=torch.float32, device="cuda")
         self.orc = OracleRun(W.Workload("prefill", s, list(prefixes), 1), self.rows, self.n_pages)
         self.worst = 0.0
