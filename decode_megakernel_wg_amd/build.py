@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmk.so")
-SOURCES = ["mk_kernel.hip", "mk_host.cpp", "mk_plan.cpp"]
+SOURCES = ["mk_kernel.hip", "mk_static.hip", "mk_host.cpp", "mk_plan.cpp"]
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
                # packed fp32 instructions are kept out of the generated code on purpose

@@ -11,6 +11,7 @@
 #include "../../include/mk.h"
 #include "mk_desc.h"
 #include "mk_kargs.h"
+#include "mk_internal.h"
 #include "mk_plan.h"
 
 extern "C" hipError_t mk_launch_persistent(const mk::KArgs* a, int kclass, int grid, int mode, hipStream_t stream);
@@ -266,13 +267,65 @@ static void lay_out_queues(mk_model* m) {
   m->uploaded_grid = m->grid;
 }
 
+// The kernel's working scratch for the step planned in P, carved in one block from `base` (256-byte aligned
+// pieces) into the argument block; returns the bytes it needs.  Used by the allocation-free step, whose block
+// is the library's static scratch; the counters come first.
+static size_t carve_scratch(const mk_model* m, const mk::Plan& P, uint8_t* base, mk::KArgs* a) {
+  const mk_model_desc& D = m->desc;
+  const size_t B = P.B, d = D.d_model, dh = D.d_head, Hq = D.n_q_heads, Hkv = D.n_kv_heads, grp = Hq / Hkv;
+  const size_t stride = *std::max_element(P.splits.begin(), P.splits.end());
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    uint8_t* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  uint8_t* ctr = take((size_t)P.cl.total * mk::CTR_STRIDE * 4);
+  uint8_t* x = take(B * d * 4);
+  uint8_t* ssq = take(B * P.t.n_rt * 4);
+  uint8_t* rope = take(B * dh * 4);
+  uint8_t* qkv = take(B * Hkv * (grp + 2) * dh * 4);
+  uint8_t* apart = take(B * Hkv * stride * grp * (dh + 2) * 4);
+  uint8_t* attn_o = take(B * Hq * dh * 4);
+  uint8_t* opart = take(Hkv * B * d * 4);
+  uint8_t* rpart = take((size_t)P.t.n_rt * B * D.n_experts * 8);
+  uint8_t* slots = take((size_t)D.n_layers * P.n_slots * mk::SLOT_WORDS * 4);
+  uint8_t* h = take((size_t)P.n_slots * B * D.d_ffn * 4);
+  uint8_t* ypart = take(B * D.top_k * d * 4);
+  uint8_t* lmv = take(B * mk::LM_MAX_WG * 4);
+  uint8_t* lmi = take(B * mk::LM_MAX_WG * 4);
+  if (a) {
+    a->ctr = (uint32_t*)ctr;
+    a->x = (float*)x;
+    a->ssq = (float*)ssq;
+    a->rope_cs = (float*)rope;
+    a->qkv = (float*)qkv;
+    a->apart = (float*)apart;
+    a->attn_o = (float*)attn_o;
+    a->opart = (float*)opart;
+    a->rpart = (double*)rpart;
+    a->slots = (int32_t*)slots;
+    a->h = (float*)h;
+    a->ypart = (float*)ypart;
+    a->lmbest_v = (float*)lmv;
+    a->lmbest_i = (int32_t*)lmi;
+  }
+  return off;
+}
+
 static int launch_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* first_of, const int32_t* page_tables,
-                       void* kv_pages, float* logits_out, void* stream) {
+                       void* kv_pages, float* logits_out, void* stream, const mk::ScratchOverride* so = nullptr) {
   if (!m) return fail(MK_E_INVAL, "null handle");
   if (!m->have_plan) return fail(MK_E_STATE, "mk_build_tasks has not been called");
   if (!tokens || !seq_lens || !page_tables || !kv_pages || !logits_out) return fail(MK_E_INVAL, "null step pointer");
   hipStream_t s = (hipStream_t)stream;
   const mk::Plan& P = m->plan;
+  if (so) {  // the step must fit the given scratch before anything is enqueued
+    const size_t need = carve_scratch(m, P, nullptr, nullptr);
+    if (need > so->cap)
+      return fail(MK_E_RANGE, "the step needs " + std::to_string(need) + " bytes of scratch; the static scratch holds " +
+                                  std::to_string(so->cap));
+  }
   if (m->dirty || m->uploaded_grid != m->grid) {
     if (m->upload_pending) HIPCHK(hipEventSynchronize(m->upload_done));  // staging may still feed the previous copy
     lay_out_queues(m);
@@ -338,6 +391,7 @@ static int launch_step(mk_model* m, const int32_t* tokens, const int32_t* seq_le
   a.rope_cs = m->rope_cs;
   a.qkv = m->qkv;
   a.apart = m->apart;
+  a.apart_stride = *std::max_element(P.splits.begin(), P.splits.end());
   a.attn_o = m->attn_o;
   a.opart = m->opart;
   a.rlogits = m->rlogits;
@@ -355,6 +409,11 @@ static int launch_step(mk_model* m, const int32_t* tokens, const int32_t* seq_le
   a.ts = (m->dbg & MK_DBG_TIMESTAMPS) ? m->ts : nullptr;
   a.ctr_snapshot = m->ctr_snapshot;
   a.pagewalk = (m->dbg & MK_DBG_PAGE_WALK) ? m->pagewalk : nullptr;
+  if (so) {  // working scratch from the given block; its counters start at zero
+    carve_scratch(m, P, so->base, &a);
+    so->zero(a.ctr, (int64_t)P.cl.total * mk::CTR_STRIDE, s);
+    HIPCHK(hipGetLastError());
+  }
   a.spin_limit = (m->dbg & MK_DBG_DROP_SIGNAL) ? (1u << 12) : (1u << 21);
   HIPCHK(mk_launch_persistent(&a, m->kclass, m->grid, (m->dbg & MK_DBG_WIDE_GEMV) ? 1 : (m->dbg & MK_DBG_VALU_GEMV) ? 2 : 0, s));
   m->stepped = true;
@@ -365,6 +424,19 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
                    float* logits_out, void* stream) {
   return launch_step(m, tokens, seq_lens, nullptr, page_tables, kv_pages, logits_out, stream);
 }
+
+}  // extern "C"
+
+namespace mk {
+int launch_step_scratch(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* page_tables, void* kv_pages,
+                        float* logits_out, void* stream, const ScratchOverride* so) {
+  return launch_step(m, tokens, seq_lens, nullptr, page_tables, kv_pages, logits_out, stream, so);
+}
+int handle_device(const mk_model* m) { return m ? m->device : -1; }
+int set_error(int code, const char* msg) { return fail(code, msg); }
+}  // namespace mk
+
+extern "C" {
 
 int mk_mixed_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* first_of, const int32_t* page_tables,
                   void* kv_pages, float* logits_out, void* stream) {

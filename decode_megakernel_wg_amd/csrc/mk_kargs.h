@@ -60,7 +60,8 @@ struct KArgs {
   float* ssq;        // [B][n_rt] partial sums of squares of x per row tile
   float* rope_cs;    // [B][dh/2][2] cos, sin of the new position
   float* qkv;        // [B][Hkv][(grp+2)*dh] projections (q heads of the group, then k, then v)
-  float* apart;      // [B][Hkv][ATTN_MAX_SPLITS][grp][dh+2] attention split partials (o, m, l)
+  float* apart;      // [B][Hkv][apart_stride][grp][dh+2] attention split partials (o, m, l)
+  int32_t apart_stride;  // most attention splits of any sequence in the task list (at most ATTN_MAX_SPLITS)
   float* attn_o;     // [B][Hq*dh] merged attention output
   float* opart;      // [Hkv][B][d] O-projection partial per KV group
   float* rlogits;    // [L][B][E] router logits

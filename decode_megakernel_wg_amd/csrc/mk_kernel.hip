@@ -1455,7 +1455,8 @@ __device__ __forceinline__ void attn_merge(KA& a, Desc w, int t, int b, int g, i
   const int Hkv = a.Hkv;
   if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) {
     mark(a, t, 3);
-    const float* p0 = a.apart + (((int64_t)b * Hkv + g) * ATTN_MAX_SPLITS) * GRP * (DH + 2);
+    const float* p0 = a.apart + (((int64_t)b * Hkv + g) * a.apart_stride) * GRP * (DH + 2);
+    nsplit = min(nsplit, a.apart_stride);
     float* wsc = S.xs;                               // [GRP][nsplit] running max, then weights exp(m_s - M)
     float* lsc = S.xs + GRP * ATTN_MAX_SPLITS;       // [GRP][nsplit] running sums
     float* lsum = S.xs + 2 * GRP * ATTN_MAX_SPLITS;  // [GRP]
@@ -1773,7 +1774,8 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
       }
     }
   }
-  float* part = a.apart + ((((int64_t)b * Hkv + g) * ATTN_MAX_SPLITS + s) * GRP) * (DH + 2);
+  if (nsplit > a.apart_stride && tid == 0) raise_error(a, ERRC_SEQLEN, t);  // a list planned for another stride
+  float* part = a.apart + ((((int64_t)b * Hkv + g) * a.apart_stride + min(s, a.apart_stride - 1)) * GRP) * (DH + 2);
   // reduce the per-thread partial outputs over positions: lanes of one slice within the wave, then the
   // waves in order through LDS
 #pragma unroll
@@ -2136,7 +2138,8 @@ __device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
       }
     }
   }
-  float* part = a.apart + ((((int64_t)b * Hkv + g) * ATTN_MAX_SPLITS + s) * GRP) * (DH + 2);
+  if (nsplit > a.apart_stride && tid == 0) raise_error(a, ERRC_SEQLEN, t);  // a list planned for another stride
+  float* part = a.apart + ((((int64_t)b * Hkv + g) * a.apart_stride + min(s, a.apart_stride - 1)) * GRP) * (DH + 2);
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int i = tid + k * NT, h = i / DH, dd = i - h * DH;

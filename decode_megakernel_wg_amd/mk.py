@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmk.so")
 
 MK_ABI_VERSION = 2
 MK_DESC_WORDS = 32
+MK_STATIC_SCRATCH_BYTES = 16 << 20
 MK_OK, MK_E_INVAL, MK_E_UNSUPPORTED, MK_E_NOMEM, MK_E_HIP, MK_E_STATE, MK_E_RANGE, MK_E_DEVICE = 0, -1, -2, -3, -4, -5, -6, -7
 MK_DBG_DUMP_N = 1
 MK_DBG_TIMESTAMPS = 2
@@ -28,7 +29,7 @@ MK_DBGK_ROUTE_SEL, MK_DBGK_ROUTE_GATE, MK_DBGK_ROUTER_LOGITS, MK_DBGK_NORM_IN, M
 MK_DBGK_TIMESTAMPS = 7
 MK_DBGK_PAGE_WALK = 8
 MK_DBGK_SLOTS = 9
-EXPORTS = ("mk_load_model", "mk_build_tasks", "mk_decode_step", "mk_mixed_step", "mk_next_tokens", "mk_status", "mk_debug_set", "mk_debug_read",
+EXPORTS = ("mk_load_model", "mk_build_tasks", "mk_decode_step", "mk_mixed_step", "mk_decode_step_static", "mk_next_tokens", "mk_status", "mk_debug_set", "mk_debug_read",
            "mk_set_grid", "mk_free_model", "mk_last_error", "mk_plan_tasks")
 
 
@@ -69,6 +70,7 @@ def lib():
         L.mk_build_tasks.argtypes = [vp, vp, vp, i64, C.POINTER(i64)]
         L.mk_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp]
         L.mk_mixed_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+        L.mk_decode_step_static.argtypes = [vp, vp, vp, vp, vp, vp, vp]
         L.mk_next_tokens.argtypes = [vp, C.POINTER(vp)]
         L.mk_status.argtypes = [vp, vp]
         L.mk_debug_set.argtypes = [vp, C.c_uint32]
@@ -179,6 +181,10 @@ class Model:
     def mk_decode_step(self, tokens, seq_lens, page_tables, kv_pages, logits_out, stream=None):
         _check(lib().mk_decode_step(self.h, _ptr(tokens), _ptr(seq_lens), _ptr(page_tables), _ptr(kv_pages), _ptr(logits_out),
                                     _stream(stream)))
+
+    def mk_decode_step_static(self, tokens, seq_lens, page_tables, kv_pages, logits_out, stream=None):
+        _check(lib().mk_decode_step_static(self.h, _ptr(tokens), _ptr(seq_lens), _ptr(page_tables), _ptr(kv_pages),
+                                           _ptr(logits_out), _stream(stream)))
 
     def mk_mixed_step(self, tokens, seq_lens, first_of, page_tables, kv_pages, logits_out, stream=None):
         _check(lib().mk_mixed_step(self.h, _ptr(tokens), _ptr(seq_lens), _ptr(first_of), _ptr(page_tables), _ptr(kv_pages),

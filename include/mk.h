@@ -141,6 +141,25 @@ int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, 
 int mk_mixed_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* first_of, const int32_t* page_tables,
                   void* kv_pages, float* logits_out, void* stream);
 
+/* Allocation-free decode step, for callers that cannot allocate device memory while they step (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  The same step as mk_decode_step on
+ * the same handle and arguments, with the same results, but the kernel's working scratch (counters,
+ * activations, attention partials, router partials, expert slot table and states, LM-head bests) comes from
+ * the library's static device scratch of MK_STATIC_SCRATCH_BYTES instead of the handle's buffers.  Each
+ * device holds its own copy of that scratch from the library's load until the process ends.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine): it enqueues a zero fill of the
+ * scratch's counters (a kernel, not a memset), the task list's upload when mk_build_tasks ran since the last
+ * step (into the handle's buffer), and the step.  The current device must be the handle's.  Every call on one
+ * device uses that device's one scratch, which keeps the last call's contents: calls that overlap on one device
+ * (several streams or handles) race.  The handle's routing records, final counter values and greedy tokens are
+ * written as by mk_decode_step; its expert slot table (MK_DBGK_SLOTS) is not.
+ * Errors: as mk_decode_step; MK_E_RANGE (nothing enqueued) if the planned step needs more than
+ * MK_STATIC_SCRATCH_BYTES (the message gives both sizes); MK_E_STATE if the current device is not the
+ * handle's; MK_E_HIP if the scratch's device address cannot be obtained. */
+#define MK_STATIC_SCRATCH_BYTES (16u << 20)
+int mk_decode_step_static(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* page_tables, void* kv_pages,
+                          float* logits_out, void* stream);
+
 /* Device buffer int32 [max_batch] holding the last step's greedy tokens (argmax, lowest index on ties);
  * it may be passed straight back as the next step's `tokens`.  Owned by the handle. */
 int mk_next_tokens(mk_model* m, int32_t** dev_ptr);
