@@ -1,6 +1,6 @@
 """Decode throughput of the persistent megakernel on one MI355X, and its fraction of HBM speed-of-light.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload b1_8k] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload b1_8k] [--no-cpu-baseline] [--gemv mfma|valu]
 
 A step is one decode step (one launch of the persistent kernel over the whole model) for the
 workload's batch; inputs (weights, KV cache, page tables, lengths) are resident in HBM before the
@@ -13,6 +13,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -235,10 +236,31 @@ def cpu_baseline_continuous(min_seconds=10.0, max_steps=16):
         n += 1
         ntok += B
         log(f"oracle step {n}: timed {timed:.2f} s")
-    return {"value": round(ntok / timed, 4), "unit": "tok/s", "cores": O.num_threads(), "kind": "oracle",
+    return {"value": round(ntok / timed, 4), "unit": "tok/s", "cores": O.num_threads(), "kind": "oracle", **host_info(),
             "sample": f"the continuous-batching schedule's first {n} steps ({ntok} tokens, live batch "
                       f"{min(len(st.sids) for st in steps[:n])}-{max(len(st.sids) for st in steps[:n])}); fp64-accumulating C oracle "
                       f"with OpenMP; {timed:.2f} s of timed CPU work; prefix writes and host weight generation excluded"}
+
+
+def host_info():
+    """CPU model, sockets, logical CPUs and RAM of the host (lscpu, /proc/meminfo)."""
+    info = {}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() in ("Model name", "Socket(s)", "CPU(s)"):
+                info[k.strip()] = v.strip()
+    except Exception:  # noqa: BLE001 - reporting only
+        pass
+    try:
+        with open("/proc/meminfo") as fh:
+            kb = int(fh.readline().split()[1])
+        info["ram_gib"] = round(kb / 2 ** 20, 1)
+    except Exception:  # noqa: BLE001
+        pass
+    return {"cpu_model": info.get("Model name"), "sockets": info.get("Socket(s)"), "logical_cpus": info.get("CPU(s)"),
+            "ram_gib": info.get("ram_gib")}
 
 
 def cpu_baseline(workload, min_seconds=10.0, max_steps=16):
@@ -282,7 +304,7 @@ def cpu_baseline(workload, min_seconds=10.0, max_steps=16):
         steps += 1
         log(f"oracle step {steps}: timed {timed:.2f} s")
     cores = O.num_threads()
-    return {"value": round(steps * w.B / timed, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+    return {"value": round(steps * w.B / timed, 4), "unit": "tok/s", "cores": cores, "kind": "oracle", **host_info(),
             "sample": f"{steps} consecutive greedy decode steps of {workload} (all {s.n_layers} layers + LM head, batch {w.B}); "
                       f"fp64-accumulating C oracle with OpenMP; {timed:.2f} s of timed CPU work; host weight generation excluded"}
 
