@@ -100,7 +100,13 @@ typedef struct mk_model mk_model;
 /* Create a handle: validates the shape, records the weight pointers, allocates the handle's own
  * device scratch (counters, fp32 activations, partials, routing and debug buffers) and sizes the
  * grid to one workgroup per compute unit of the current device.
- * Errors: MK_E_INVAL, MK_E_UNSUPPORTED, MK_E_NOMEM, MK_E_HIP. */
+ * Errors: MK_E_INVAL, MK_E_UNSUPPORTED, MK_E_NOMEM, MK_E_HIP.
+ * Passage: agenticcommons.xyz "Cohere North Mini Code megakernel serving engine", section 三個實際的加速來源, item 1
+ * (the parallel transformer layer: attention and the MoE feed-forward both read one RMSNorm of the residual
+ * stream, joined by a fused residual add) and section 為什麼 decode 慢 (a sparse MoE model whose active weights
+ * stream from HBM once per step, in BF16); aimodeling.com "Cohere megakernel engine: one CUDA file, 1.58x vLLM
+ * on H100", section "Caveats and takeaways" (BF16, batches of at most 8).
+ */
 int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out);
 
 /* Build the step's task list on the host (deterministic, no device work): fixed-size descriptors of
@@ -109,7 +115,13 @@ int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out
  * lengths; split bounds are recomputed on the device from the step's seq_lens, so a list stays valid
  * while lengths grow.  tasks_out (nullable, host) receives a copy when cap >= the task count;
  * *n_tasks always receives the count.
- * Errors: MK_E_INVAL (batch outside 1..max_batch, negative length, null batch), MK_E_RANGE (cap too small). */
+ * Errors: MK_E_INVAL (batch outside 1..max_batch, negative length, null batch), MK_E_RANGE (cap too small).
+ * Passage: agenticcommons.xyz "Cohere North Mini Code megakernel serving engine", section Megakernel 的運作方式
+ * (the step as a list of tasks in global memory, one operation on one tile each); aimodeling.com "Cohere
+ * megakernel engine: one CUDA file, 1.58x vLLM on H100", section "One persistent kernel for the whole decode
+ * step" (a task waits only for its own producers, e.g. an O-projection tile for its KV group's attention) and
+ * section "Caveats and takeaways" (fixed descriptors of 32 int32 words).
+ */
 int mk_build_tasks(mk_model* m, const mk_batch* batch, int32_t* tasks_out, int64_t cap, int64_t* n_tasks);
 
 /* Enqueue one decode step on `stream` (a hipStream_t; NULL = default stream); asynchronous.
@@ -121,7 +133,14 @@ int mk_build_tasks(mk_model* m, const mk_batch* batch, int32_t* tasks_out, int64
  *  logits_out  device fp32  [B][vocab]
  * B is the batch of the last mk_build_tasks.  The greedy next tokens go to the buffer of mk_next_tokens.
  * Errors before launch: MK_E_STATE (no task list), MK_E_INVAL (null pointer), MK_E_HIP.  Faults found by the
- * kernel (token or page out of range, a dependency wait that timed out) are reported by mk_status. */
+ * kernel (token or page out of range, a dependency wait that timed out) are reported by mk_status.
+ * Passage: agenticcommons.xyz "Cohere North Mini Code megakernel serving engine", section Megakernel 的運作方式
+ * (one resident workgroup per compute unit takes tasks from the list; completions increment counters that
+ * consumers spin on) and section 三個實際的加速來源 (tile tasks in place of kernel waves, per-producer dependencies,
+ * weights loaded before the activations they meet); aimodeling.com "Cohere megakernel engine: one CUDA file,
+ * 1.58x vLLM on H100", section "From demo to a full serving system" (paged attention over ragged sequence
+ * lengths).
+ */
 int mk_decode_step(mk_model* m, const int32_t* tokens, const int32_t* seq_lens, const int32_t* page_tables, void* kv_pages,
                    float* logits_out, void* stream);
 
@@ -161,11 +180,19 @@ int mk_decode_step_static(mk_model* m, const int32_t* tokens, const int32_t* seq
                           float* logits_out, void* stream);
 
 /* Device buffer int32 [max_batch] holding the last step's greedy tokens (argmax, lowest index on ties);
- * it may be passed straight back as the next step's `tokens`.  Owned by the handle. */
+ * it may be passed straight back as the next step's `tokens`.  Owned by the handle.
+ * Passage: aimodeling.com "Cohere megakernel engine: one CUDA file, 1.58x vLLM on H100", section "From demo to
+ * a full serving system" (continuous batching: each step's output tokens are the next step's inputs).  The
+ * pages do not name the sampling rule; greedy decoding is the plainest reading of a decode-only throughput
+ * test.
+ */
 int mk_next_tokens(mk_model* m, int32_t** dev_ptr);
 
 /* Synchronise `stream`, then return MK_OK or MK_E_DEVICE if the kernel raised a fault since the last
- * call (the fault word is cleared and the handle's counters are reset). */
+ * call (the fault word is cleared and the handle's counters are reset).
+ * Passage: none on the pages, which do not say what happens when a dependency is never met; every wait here is
+ * bounded, and a fault ends the step with every workgroup exiting normally.
+ */
 int mk_status(mk_model* m, void* stream);
 
 /* Debug switches (bit flags, MK_DBG_*) and read-back of the handle's debug buffers.  MK_DBG_WIDE_GEMV runs
@@ -201,6 +228,12 @@ enum {
                                 top_k)): expert (-1 = unused), token count, then (token, rank, gate bits) per token of the
                                 slot in ascending token order (always recorded) */
 };
+/*
+ * Passage: none on the pages; the debug records make the step's integer work checkable: the task graph's
+ * counters (agenticcommons.xyz "Cohere North Mini Code megakernel serving engine", section Megakernel 的運作方式),
+ * the routing and expert slot table (section 三個實際的加速來源, item 1) and the page walks (aimodeling.com "Cohere
+ * megakernel engine: one CUDA file, 1.58x vLLM on H100", section "From demo to a full serving system").
+ */
 int mk_debug_set(mk_model* m, uint32_t flags);
 /* Copies `bytes` of debug buffer `kind` to host memory; synchronises the device first.
  * Errors: MK_E_INVAL (unknown kind), MK_E_STATE (kind not enabled), MK_E_RANGE (bytes larger than the buffer). */
@@ -210,7 +243,10 @@ int mk_debug_read(mk_model* m, int kind, void* host_dst, int64_t bytes);
  * do not depend on it (every reduction has a fixed order); it exists for testing and tuning.  Takes effect at
  * the next mk_decode_step, which lays the task list out for this grid (phase pools for two or more
  * workgroups, one in-order claim sequence for one).
- * Errors: MK_E_INVAL (null handle, n_workgroups outside 0..1024). */
+ * Errors: MK_E_INVAL (null handle, n_workgroups outside 0..1024).
+ * Passage: agenticcommons.xyz "Cohere North Mini Code megakernel serving engine", section 三個實際的加速來源, item 1
+ * (tile tasks spread over whichever compute units are free, so no work is tied to a wave of the grid).
+ */
 int mk_set_grid(mk_model* m, int32_t n_workgroups);
 
 /* Release the handle and its device memory (after the stream's work has finished). */
@@ -222,7 +258,9 @@ const char* mk_last_error(void);
 /* Pure host planning, for tools and tests (no device needed): the task list mk_build_tasks would emit
  * for `desc` and `batch`, in topological order (the order the phases follow).  n_tasks receives the
  * task count, n_counters (nullable) the counter count; tasks_out may be null to query the sizes.
- * Errors: MK_E_INVAL (bad shape or batch), MK_E_RANGE (cap smaller than the task count). */
+ * Errors: MK_E_INVAL (bad shape or batch), MK_E_RANGE (cap smaller than the task count).
+ * Passage: as mk_build_tasks.
+ */
 int mk_plan_tasks(const mk_model_desc* desc, const mk_batch* batch, int32_t* tasks_out, int64_t cap, int64_t* n_tasks,
                   int32_t* n_counters);
 
