@@ -48,12 +48,13 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload):
+def counter_traffic(workload, gemv="mfma"):
     """Calibrated HBM bytes per launch of the persistent kernel from the committed counter summary of this
-    workload, or None when there is none or it was taken on other kernel sources."""
+    workload (and GEMV engine), or None when there is none or it was taken on other kernel sources."""
     import re
 
-    path = os.path.join(ROOT, "profiles", f"mk_persistent_{workload}_hbm_counters.md")
+    suffix = "" if gemv == "mfma" else f"_{gemv}"
+    path = os.path.join(ROOT, "profiles", f"mk_persistent_{workload}_hbm_counters{suffix}.md")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -356,7 +357,7 @@ def main():
         "sol_bytes_per_step": int(r["avg_bytes"]),
         "unique_experts_per_layer": int(round(sum(r["uniq"]) / len(r["uniq"]))),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
-                     "frac": round(achieved / 8000.0, 4), "traffic": counter_traffic(args.workload)},
+                     "frac": round(achieved / 8000.0, 4), "traffic": counter_traffic(args.workload, args.gemv)},
     }
     if not args.no_cpu_baseline:
         del r
