@@ -44,18 +44,18 @@ enum Word : int {
   W_SEQ = 31    // task index (debug)
 };
 constexpr int N_WAITS = 4;
-// Scheduling.  With two or more workgroups the list runs as phases: the embedding tiles, then per layer
-// each maximal run of one operation (QKV tiles, attention splits, expert up-projection tiles,
-// O-projection tiles, expert down-projection tiles).  Each phase is a pool that every workgroup takes
-// tasks from one at a time (an atomic counter; nothing is claimed ahead), moving on to the next phase
-// once a take finds the pool empty.  A phase's tasks thus go to whichever workgroups are free, one each,
-// instead of queueing behind busy workgroups that hold tickets, and the attention and expert branches
-// of a layer share all compute units.  Phases follow the list's topological order and a workgroup enters
-// a phase only once every task of the previous one has been taken by a workgroup that runs it at once,
-// so the earliest unfinished task can always run.  One workgroup claims the list in order.
-// Expert phases (UP, DOWN) list their tiles slot by slot, the same number per slot; slots are numbered in
+// Scheduling.  The list is one pool: every workgroup takes the next untaken task in list order through one
+// atomic counter (the ticket), runs it, and takes again; nothing is claimed ahead, so a task goes to
+// whichever workgroup is free first and the attention and expert branches of a layer share all compute
+// units.  Every take but each workgroup's last returns a task (no take comes back from an exhausted pool
+// part-way through the list).  The list is topological and a task is taken only by a workgroup that runs it
+// at once, so the earliest unfinished task can always run.
+// Phases (maximal runs of one operation within a layer: the embedding tiles, then per layer QKV tiles,
+// attention splits, expert up-projection tiles, O-projection tiles, expert down-projection tiles) classify
+// a take.  Expert phases list their tiles slot by slot, the same number per slot; slots are numbered in
 // ascending expert order, so once a layer is routed (its used-slot count published) the tiles of its unused
-// slots are the tail of each expert phase, and takers leave the phase there.
+// slots are the tail of each expert phase, and the workgroup that meets that tail first moves the ticket past
+// it.
 constexpr int DESC_WORDS = 32;
 
 // Tile sizes chosen by the planner (rows per task); the kernel reads r0/r1 from the descriptor.
@@ -74,7 +74,7 @@ constexpr int LM_MAX_WG = 1024;  // most workgroups a launch may have (stride of
 // at word c * CTR_STRIDE of the counter array (one 128-byte line per counter).
 constexpr int CTR_STRIDE = 32;
 struct CounterLayout {
-  int32_t ticket, done, xready, phase, qkv_done, router_arrive, slot_ready, slots_used, attn_arrive, attn_done, up_done,
+  int32_t ticket, done, xready, qkv_done, router_arrive, slot_ready, slots_used, attn_arrive, attn_done, up_done,
       resid_arrive, lm_arrive, lm_pool, total;
   int32_t n_layers, n_kv, n_slots, n_row_tiles, batch;
   void build(int L, int Hkv, int B, int slots, int nrt) {
@@ -84,10 +84,9 @@ struct CounterLayout {
     n_row_tiles = nrt;
     batch = B;
     int32_t o = 0;
-    ticket = o; o += 32;     // own cache line (claim order with one workgroup)
+    ticket = o; o += 32;     // next untaken task of the list
     done = o; o += 32;
     xready = o; o += L + 1;
-    phase = o; o += 1 + 5 * L;  // next untaken task of each phase
     qkv_done = o; o += L * Hkv;
     router_arrive = o; o += L;
     slot_ready = o; o += L * slots;

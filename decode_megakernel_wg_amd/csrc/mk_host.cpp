@@ -70,7 +70,7 @@ struct mk_model {
   mk::Plan plan;
   bool have_plan = false, dirty = false;
   int uploaded_grid = -1;    // grid the device task array was laid out for
-  int32_t ph_on = 0;         // phases in use (two or more workgroups and a regular list)
+  int32_t ph_on = 0;         // the list is regular: its phase table is valid
   int32_t ph_npl = 0;        // phases per layer
   int32_t ph_n[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int32_t ph_op[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -218,9 +218,10 @@ int mk_build_tasks(mk_model* m, const mk_batch* batch, int32_t* tasks_out, int64
   return MK_OK;
 }
 
-// Phases of the list: maximal runs of one operation and layer.  They are used when the list is the
+// Phases of the list: maximal runs of one operation and layer.  The table is valid when the list is the
 // embedding tiles followed, layer by layer, by the same sequence of runs with the same sizes (at most 7 per
-// layer); otherwise the workgroups claim the list in order.
+// layer); the kernel then passes over the expert tiles of unused slots (otherwise it runs them as empty
+// tasks).
 static void derive_phases(mk_model* m, const int32_t* q, int64_t n) {
   m->ph_on = 0;
   const int L = m->desc.n_layers;
@@ -251,8 +252,8 @@ static void derive_phases(mk_model* m, const int32_t* q, int64_t n) {
   m->ph_on = 1;
 }
 
-// Copy the task list to the pinned staging buffer (list order) and derive its phases for grids of two or
-// more workgroups.  MK_DBG_DROP_SIGNAL removes the completion signal of the first QKV task (watchdog test).
+// Copy the task list to the pinned staging buffer (list order) and derive its phase table.
+// MK_DBG_DROP_SIGNAL removes the completion signal of the first QKV task (watchdog test).
 static void lay_out_queues(mk_model* m) {
   const mk::Plan& P = m->plan;
   std::memcpy(m->staging, P.desc.data(), P.desc.size() * sizeof(int32_t));
@@ -262,8 +263,7 @@ static void lay_out_queues(mk_model* m) {
         m->staging[i * mk::DESC_WORDS + mk::W_SIG] = -1;
         break;
       }
-  m->ph_on = 0;
-  if (m->grid >= 2) derive_phases(m, m->staging, P.n_tasks());
+  derive_phases(m, m->staging, P.n_tasks());
   m->uploaded_grid = m->grid;
 }
 
@@ -369,7 +369,6 @@ static int launch_step(mk_model* m, const int32_t* tokens, const int32_t* seq_le
   }
   a.c_slots_used = P.cl.slots_used;
   a.c_resid_arrive = P.cl.resid_arrive;
-  a.c_phase = P.cl.phase;
   a.c_done = P.cl.done;
   a.layers = m->layers;
   a.embed = m->embed;

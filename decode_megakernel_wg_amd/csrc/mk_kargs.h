@@ -29,10 +29,10 @@ struct KArgs {
   float eps;
   int32_t n_tasks, n_counters, c_ticket, c_done;
   int32_t c_lm_pool, c_lm_arrive, c_xfinal;  // LM head: chunk pool, arrivals, readiness of the final residual stream
-  // phases (when ph_on): the list is the embedding tiles (ph_n[0]), then per layer ph_npl runs of one
-  // operation, of ph_n[1] .. ph_n[ph_npl] tasks; counter c_phase + p is phase p's pool (p = 0 embedding,
-  // 1 + ph_npl * l + k).  Otherwise every workgroup claims the list in order (ticket counter c_ticket).
-  int32_t ph_on, ph_npl, ph_n[8], c_phase;
+  // phase table (when ph_on): the list is the embedding tiles (ph_n[0]), then per layer ph_npl runs of one
+  // operation, of ph_n[1] .. ph_n[ph_npl] tasks, the same in every layer; it classifies a take (expert tiles
+  // of unused slots).  Every workgroup takes the list in order through the ticket counter c_ticket.
+  int32_t ph_on, ph_npl, ph_n[8];
   int32_t ph_op[8];      // operation of each per-layer phase
   // expert slots: counter of each layer's used-slot count, first residual arrival counter
   int32_t c_slots_used, c_resid_arrive;

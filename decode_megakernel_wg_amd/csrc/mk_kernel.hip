@@ -4,9 +4,8 @@
 // Megakernel 的運作方式 and 三個實際的加速來源; aimodeling.com "Cohere megakernel engine: one CUDA file,
 // 1.58x vLLM on H100", section "One persistent kernel for the whole decode step"):
 //  * one 512-thread workgroup per compute unit stays resident for the whole step and takes tasks (one
-//    operation on one tile) from a task list in global memory, in list order: the list runs as phases
-//    (runs of one operation within a layer), each a pool that free workgroups take tasks from one at a
-//    time through an atomic counter, so a phase spreads over whichever compute units are free;
+//    operation on one tile) from a task list in global memory, one at a time, in list order, through one
+//    atomic counter, so each task goes to whichever compute unit is free first;
 //  * dependencies are global counters: a finished task increments its counter, a task that needs an
 //    input spins on the producer's counter (no grid barrier, no kernel boundary);
 //  * weight tiles (immutable) and old KV pages are loaded into registers BEFORE the task waits for its
@@ -80,12 +79,12 @@ struct Lds {
   int slot_e, slot_n, slot_b[8], slot_j[8];
   float slot_g[8];
   int slotw[SLOT_WORDS];
-  int32_t desc[2][DESC_WORDS];  // current and next task descriptor
-  int pool_tile;                // phases: the index a take returned
-  int pool_used;                // expert phases: the layer's used-slot count seen with the take (0 = not yet routed)
+  int32_t desc[DESC_WORDS];     // the task's descriptor
+  int pool_tile;                // the index a take returned (the ticket's value before a maximum)
+  int pool_used;                // a layer's used-slot count read with a take (0 = not yet routed)
   int lmq[4];                   // LM head: ring of claimed vocabulary chunks
   uint32_t wval;                // value a wait observed (expert slot words)
-  int next1, flag;
+  int flag;
   int xb_layer;  // l + 1 while xb holds layer l's normalised input of every token (split); 0 otherwise
   int route_layer;  // l + 1 while sel / used hold layer l's routing; 0 otherwise
 };
@@ -2225,74 +2224,84 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KArgs args) {
   __shared__ Lds S;
   const int tid = tidx();
   KA& a = *a0;
-  const int base = 0, count = a.n_tasks, ticket = a.c_ticket;
-  // phases: take tasks from phase ph's pool until it is empty, then ph + 1
-  const bool phases = a.ph_on;
-  // claim order (no phases): first task claimed and fetched synchronously; then two claims and one
-  // descriptor kept ahead
+  const int count = a.n_tasks;
   if (tid == 0) {
     S.xb_layer = 0;
     S.route_layer = 0;
-    if (!phases) S.next1 = (int)__hip_atomic_fetch_add(ctr_at(a, ticket), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  int i = phases ? count : S.next1;
-  if (i < count) fetch_desc(a, base + i, S.desc[0]);
-  if (tid == 0 && !phases) S.next1 = (int)__hip_atomic_fetch_add(ctr_at(a, ticket), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  drain_stores();
-  __syncthreads();
-  const int npl = a.ph_npl, nph = 1 + npl * a.L;
+  // The list is one pool: every take (an atomic on the ticket counter) returns the next untaken task in
+  // list order, so a task goes to whichever workgroup is free first and no take comes back empty before the
+  // list's end.  Expert tiles of a batch above one are classified with the list's phase table: a tile found
+  // (with its descriptor, once its layer is routed) to belong to an unused slot starts the unused tail of its
+  // phase, and the ticket is moved past the phase in one step (an atomic maximum).  No task of that tail is
+  // handed out any more; the phase's next task is this workgroup's if the maximum found the ticket at or
+  // below it.
+  const bool skip_unused = a.ph_on && a.B > 1;
+  const int n0 = a.ph_n[0], npl = a.ph_npl;
   int per_layer = 0;
   for (int k = 0; k < npl; ++k) per_layer += a.ph_n[1 + k];
-  int ph = 0;
-  int cur = 0;
+  int nu_l = 0, nu_v = 0;  // used-slot count nu_v of layer nu_l - 1, once seen (it never changes after)
   for (;;) {
-    int i1 = 0;
-    uint32_t i2 = 0;
-    if (phases) {
-      int pos = -1;
-      while (ph < nph) {
-        const int l = ph == 0 ? 0 : (ph - 1) / npl, k = ph == 0 ? 0 : ph - 1 - npl * l;
-        int start = ph == 0 ? 0 : a.ph_n[0] + l * per_layer;
-        for (int j = 0; j < k; ++j) start += a.ph_n[1 + j];
-        const int cnt = ph == 0 ? a.ph_n[0] : a.ph_n[1 + k];
-        // expert phases list their tiles slot by slot (cnt / n_slots per slot) and slots are numbered in
-        // ascending expert order, so once the layer is routed the tiles of unused slots are the pool's tail
-        const bool moe = ph > 0 && (a.ph_op[k] == OP_UP || a.ph_op[k] == OP_DOWN);
-        if (tid == 0) S.pool_tile = (int)__hip_atomic_fetch_add(ctr_at(a, a.c_phase + ph), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (tid == 1) S.pool_used = moe ? (int)__hip_atomic_load(ctr_at(a, a.c_slots_used + l), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-        __syncthreads();
-        const int tk = __builtin_amdgcn_readfirstlane(S.pool_tile);
-        const int nu = __builtin_amdgcn_readfirstlane(S.pool_used);
-        __syncthreads();  // read by every wave before the next take overwrites it
-        if (tk < cnt && (nu == 0 || tk < nu * (cnt / a.n_slots))) {
-          pos = start + tk;
+    int pos = -1;
+    for (;;) {
+      if (tid == 0) S.pool_tile = (int)__hip_atomic_fetch_add(ctr_at(a, a.c_ticket), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      int tk = __builtin_amdgcn_readfirstlane(S.pool_tile);
+      __syncthreads();  // read by every wave before the next take overwrites it
+      while (tk < count) {
+        fetch_desc(a, tk, S.desc);
+        if (!skip_unused || tk < n0) {
+          pos = tk;
           break;
         }
-        ++ph;  // every task of this phase is taken, or only unused slots' tiles are left
+        // phase k of layer l, offset off within it, first task after it pend
+        const int l = (tk - n0) / per_layer;
+        int off = tk - n0 - l * per_layer, k = 0, pend = n0 + l * per_layer;
+        while (k < npl - 1 && off >= a.ph_n[1 + k]) {
+          off -= a.ph_n[1 + k];
+          pend += a.ph_n[1 + k++];
+        }
+        const int cnt = a.ph_n[1 + k];
+        pend += cnt;
+        const bool moe = a.ph_op[k] == OP_UP || a.ph_op[k] == OP_DOWN;
+        const bool known = nu_l == l + 1;
+        if (moe && !known && tid == 1)
+          S.pool_used = (int)__hip_atomic_load(ctr_at(a, a.c_slots_used + l), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        drain_stores();
+        __syncthreads();
+        int nu = 0;
+        if (moe) {
+          nu = known ? nu_v : __builtin_amdgcn_readfirstlane(S.pool_used);
+          if (nu > 0) {
+            nu_l = l + 1;
+            nu_v = nu;
+          }
+        }
+        __syncthreads();
+        // expert phases list their tiles slot by slot, cnt / n_slots per slot, slots in ascending expert
+        // order: once the layer is routed, the tiles of its unused slots are the phase's tail
+        if (!moe || nu == 0 || off < nu * (cnt / a.n_slots)) {
+          pos = tk;
+          break;
+        }
+        const int target = pend < count ? pend + 1 : count;
+        if (tid == 0) S.pool_tile = (int)__hip_atomic_fetch_max(ctr_at(a, a.c_ticket), (uint32_t)target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int old = __builtin_amdgcn_readfirstlane(S.pool_tile);
+        __syncthreads();
+        if (pend >= count || old > pend) break;  // the next task was taken by another workgroup: take again
+        tk = pend;
       }
-      if (pos < 0) break;
-      fetch_desc(a, pos, S.desc[cur]);
-      drain_stores();
-      __syncthreads();
-    } else {
-      if (i >= count) break;
-      i1 = S.next1;
-      __syncthreads();
-      if (i1 < count) fetch_desc(a, base + i1, S.desc[cur ^ 1]);
-      if (tid == 0) i2 = __hip_atomic_fetch_add(ctr_at(a, ticket), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (pos >= 0 || tk >= count) break;
     }
-    const Desc w{S.desc[cur]};
+    if (pos < 0) break;
+    drain_stores();  // the descriptor has landed in LDS
+    __syncthreads();
+    const Desc w{S.desc};
     run_task<C>(a0, w, w[W_SEQ], S);
-    drain_stores();  // the next descriptor has landed in LDS, the claim has returned
-    if (phases) {
-      __syncthreads();  // every wave is done with the descriptor
-    } else {
-      if (tid == 0) S.next1 = (int)i2;
-      __syncthreads();
-      i = i1;
-      cur ^= 1;
-    }
+    drain_stores();
+    __syncthreads();  // every wave is done with the descriptor
   }
   lm_phase<C>(*(KA*)a0, S);
   exit_step(a, S);

@@ -241,8 +241,7 @@ int mk_debug_read(mk_model* m, int kind, void* host_dst, int64_t bytes);
 
 /* Override the grid: n_workgroups persistent workgroups (0 = one per compute unit, at most 1024).  Results
  * do not depend on it (every reduction has a fixed order); it exists for testing and tuning.  Takes effect at
- * the next mk_decode_step, which lays the task list out for this grid (phase pools for two or more
- * workgroups, one in-order claim sequence for one).
+ * the next mk_decode_step (every grid takes the same list in order through one counter).
  * Errors: MK_E_INVAL (null handle, n_workgroups outside 0..1024).
  * Passage: agenticcommons.xyz "Cohere North Mini Code megakernel serving engine", section 三個實際的加速來源, item 1
  * (tile tasks spread over whichever compute units are free, so no work is tied to a wave of the grid).
@@ -256,7 +255,7 @@ int mk_free_model(mk_model* m);
 const char* mk_last_error(void);
 
 /* Pure host planning, for tools and tests (no device needed): the task list mk_build_tasks would emit
- * for `desc` and `batch`, in topological order (the order the phases follow).  n_tasks receives the
+ * for `desc` and `batch`, in topological order (the order the workgroups take it in).  n_tasks receives the
  * task count, n_counters (nullable) the counter count; tasks_out may be null to query the sizes.
  * Errors: MK_E_INVAL (bad shape or batch), MK_E_RANGE (cap smaller than the task count).
  * Passage: as mk_build_tasks.

@@ -136,9 +136,10 @@ def test_task_counts_full_model():
 @pytest.mark.parametrize("name,B_lens", [("tiny", [128]), ("tiny", [5, 300, 17, 0]), ("full", [8192]),
                                          ("full", [1024, 30000, 4000, 70000, 2000, 9000, 1500, 12000])])
 def test_task_list_has_the_regular_phase_structure(name, B_lens):
-    """The launcher runs the list as phases only when it is the embedding tiles followed, layer by layer, by
-    the same sequence of operation runs with the same sizes (otherwise it falls back to in-order claims):
-    every planned list must have that structure."""
+    """The kernel classifies its takes by the list's phase table (and passes over the expert tiles of unused
+    slots) only when the list is the embedding tiles followed, layer by layer, by the same sequence of
+    operation runs with the same sizes (otherwise it runs those tiles as empty tasks): every planned list
+    must have that structure."""
     shape = W.TINY if name == "tiny" else W.FULL
     maxp = max(B_lens) // 16 + 2
     d = desc_for(shape, B=len(B_lens), pages=maxp, n_pages=maxp * len(B_lens))
