@@ -66,6 +66,12 @@ def counter_traffic(workload, gemv="mfma"):
     return int(t.group(1))
 
 
+def percentile(xs, q):
+    """q-th percentile of the per-step times (nearest rank)."""
+    v = sorted(xs)
+    return v[min(len(v) - 1, max(0, -(-q * len(v) // 100) - 1))]
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -186,7 +192,7 @@ def run_gpu_continuous(steps, warmup):
         raise RuntimeError("pipelined pass ended on other tokens than the step-by-step pass")
     log(f"pass 2: {wall:.3f} s wall, {fill_s:.3f} s of prefix writes")
     log(f"kernel time per step: pass 1 {sum(kern) / steps:.3f} ms, pass 2 {1e3 * sum(kern2) / steps:.3f} ms")
-    return dict(sess=sess, wall_s=wall - fill_s, kernel_s=sum(kern2), bytes=sum(nbytes), tokens=ntok,
+    return dict(sess=sess, wall_s=wall - fill_s, kernel_s=sum(kern2), kernel_ms=[1e3 * k for k in kern2], bytes=sum(nbytes), tokens=ntok,
                 batch_sizes=[len(st.sids) for st in sess.steps[:steps]], max_ctx=int(max(max(st.pos) for st in sess.steps[:steps])))
 
 
@@ -355,6 +361,8 @@ def main():
         "sol_tok_s": round(sol_tok_s, 1),
         "pct_of_sol": round(100 * r["tok_s"] / sol_tok_s, 2),
         "sol_bytes_per_step": int(r["avg_bytes"]),
+        "step_ms_p50": round(percentile(r["per_step_ms"], 50), 4),
+        "step_ms_p99": round(percentile(r["per_step_ms"], 99), 4),
         "unique_experts_per_layer": int(round(sum(r["uniq"]) / len(r["uniq"]))),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(achieved / 8000.0, 4), "traffic": counter_traffic(args.workload, args.gemv)},
@@ -393,6 +401,8 @@ def main_continuous(args):
         "pct_of_sol": round(100 * sol_s / r["wall_s"], 2),
         "sol_bytes_per_step": int(r["bytes"] / args.steps),
         "kernel_ms_per_step": round(1e3 * r["kernel_s"] / args.steps, 4),
+        "kernel_ms_p50": round(percentile(r["kernel_ms"], 50), 4),
+        "kernel_ms_p99": round(percentile(r["kernel_ms"], 99), 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(achieved / 8000.0, 4), "traffic": counter_traffic("continuous")},
     }

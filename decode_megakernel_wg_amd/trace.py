@@ -58,17 +58,20 @@ def summarize(w, tasks, ts, plain_ms, traced_ms):
     op = tasks[:, 0]
     layer = tasks[:, 1]
     claim, met, end = ts[:, 0], ts[:, 1], ts[:, 2]
-    t_first = claim.min()
-    span_us = (end.max() - t_first) * TICK_US
+    # tasks that ran (the expert tiles of slots a layer leaves unused are passed over and record nothing)
+    ran = end > 0
+    t_first = claim[ran].min()
+    span_us = (end[ran].max() - t_first) * TICK_US
     L = w.shape.n_layers
-    lines = [f"workload `{w.name}`, batch {w.B}, {len(tasks)} tasks", "",
+    lines = [f"workload `{w.name}`, batch {w.B}, {len(tasks)} tasks, {int(ran.sum())} of them run (the others are "
+             "expert tiles of unused slots, passed over)", "",
              f"step without timestamps {plain_ms * 1e3:.1f} us; with timestamps {traced_ms * 1e3:.1f} us; "
              f"span of the recorded tasks {span_us:.1f} us (the LM head's closing phase follows the last task)", ""]
     # layer input complete: the earliest moment a QKV tile of the layer saw all row tiles of its input
     # (their waits end when the last row tile's residual epilogue has counted itself)
     t0 = np.zeros(L, np.int64)
     for l in range(L):
-        m = (op == 3) & (layer == l)
+        m = (op == 3) & (layer == l) & ran
         t0[l] = met[m][met[m] > 0].min()
     per = np.diff(t0) * TICK_US
     lines += [f"layer period (input complete to next input complete), median over layers 1..{L - 2}: "
@@ -80,9 +83,9 @@ def summarize(w, tasks, ts, plain_ms, traced_ms):
     for o in (3, 4, 5, 6, 7):
         rows = {"claim": [], "met": [], "end": [], "cl_max": [], "met_max": [], "end_max": []}
         marks = [[] for _ in range(4)]
-        cnt = 0
+        cnt = 0  # tasks of the kind that ran in a layer (the last layer seen)
         for l in mid:
-            m = (op == o) & (layer == l)
+            m = (op == o) & (layer == l) & ran
             if not m.any():
                 continue
             cnt = int(m.sum())
@@ -113,11 +116,11 @@ def summarize(w, tasks, ts, plain_ms, traced_ms):
               "staged, m1 = cached positions done, m2 = partials published, m3 = merge started (last split only)."]
     # per compute unit: time in task bodies (waits met), in waits, outside tasks, over the recorded span
     cu = (ts[:, 3] >> 32) * 65536 + ((ts[:, 3] >> 8) & 0xFFFF)
-    keys = np.unique(cu)
+    keys = np.unique(cu[ran])
     wait_f, body_f, out_f = [], [], []
-    span = end.max() - t_first
+    span = end[ran].max() - t_first
     for k in keys:
-        m = cu == k
+        m = (cu == k) & ran
         c, mt, e = claim[m], met[m], end[m]
         mt = np.where(mt > 0, mt, c)
         wait = (mt - c).sum()
