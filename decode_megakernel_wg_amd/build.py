@@ -30,5 +30,24 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(HERE, "hop_probe.hip")
+PROBE = os.path.join(HERE, "hop_probe")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The measurement program hop_probe.hip (synchronisation and streaming costs; not part of the decode path)."""
+    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    cmd = ["hipcc", *flags, PROBE_SRC, "-o", PROBE + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        errs = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{errs}")
+    os.replace(PROBE + ".tmp", PROBE)
+    return PROBE
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_probe(verbose=True)

@@ -4,6 +4,7 @@ python -m decode_megakernel_wg_amd.profiling trace WORKLOAD [--steps 32] [--gemv
 python -m decode_megakernel_wg_amd.profiling hbm WORKLOAD [--gemv mfma|valu]      FETCH_SIZE and WRITE_SIZE, calibrated
 python -m decode_megakernel_wg_amd.profiling counters WORKLOAD                     LDS bank conflicts, busy CUs, occupancy, MFMA
 python -m decode_megakernel_wg_amd.profiling timeline WORKLOAD                     per-task timestamp pass (trace.py)
+python -m decode_megakernel_wg_amd.profiling probe                                 synchronisation / streaming costs (hop_probe)
 
 Each pass runs `rocprofv3 ... -- python3 bench.py --workload WORKLOAD ... --no-cpu-baseline` as a child process
 under a time limit of its own, from /tmp, with the raw output under OUT (default gpurun_out/rocprof), and
@@ -227,17 +228,35 @@ def do_timeline(a, out):
     return f"mk_persistent_{a.workload}_timeline", lines
 
 
+def do_probe(a, out):
+    """Run the measurement program hop_probe (built in-tree by build.build_probe) and keep its tables."""
+    prog = os.path.join(HERE, "hop_probe")
+    if not os.path.exists(prog):
+        raise RuntimeError("hop_probe is not built (decode_megakernel_wg_amd.build.build_probe)")
+    log = os.path.join(out, "hop_probe.log")
+    run([prog], 240, log)
+    with open(log) as fh:
+        body = [l.rstrip("\n") for l in fh if l.strip() != "done"]
+    lines = header("Synchronisation and streaming costs on this part (hop_probe)",
+                   ["decode_megakernel_wg_amd/hop_probe   (built from decode_megakernel_wg_amd/hop_probe.hip by build.build_probe)"],
+                   "A standalone program, not the decode kernel: one dependency hop between workgroups on different XCDs "
+                   "(counter protocol against a flag in the data), int64 atomic additions against plain stores, and "
+                   "re-reads of a buffer that fits the last-level cache.  Wall-clock ticks at 100 MHz; HIP events.")
+    return "mk_probe_sync_and_streaming", lines + body
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=("trace", "hbm", "counters", "timeline"))
-    ap.add_argument("workload")
+    ap.add_argument("what", choices=("trace", "hbm", "counters", "timeline", "probe"))
+    ap.add_argument("workload", nargs="?", default="b1_8k")
     ap.add_argument("--steps", type=int, default=32)
     ap.add_argument("--gemv", choices=("mfma", "valu"), default="mfma")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
     a = ap.parse_args()
     out = os.path.abspath(a.out)
     os.makedirs(os.path.join(out, "summaries"), exist_ok=True)
-    name, lines = {"trace": do_trace, "hbm": do_hbm, "counters": do_counters, "timeline": do_timeline}[a.what](a, out)
+    name, lines = {"trace": do_trace, "hbm": do_hbm, "counters": do_counters, "timeline": do_timeline,
+                   "probe": do_probe}[a.what](a, out)
     path = os.path.join(out, "summaries", name + ".md")
     with open(path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
