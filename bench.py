@@ -29,6 +29,9 @@ WORKLOAD_TEXT = {
     "long_64k": "same 48-layer model, batch 1, 65536 prior positions, split-KV attention",
     "long_128k": "same 48-layer model, batch 1, 131072 prior positions, split-KV attention",
     "long_256k": "same 48-layer model, batch 1, 262144 prior positions, split-KV attention",
+    "tp2_b1_8k": "one GPU's share of the same model under 2-way tensor parallelism (16 q heads / 2 KV heads x 128, "
+                 "128 experts top-8 with d_ffn 384, vocab 131072, d_model 2048, 48 layers), batch 1, 8192 prior KV positions; "
+                 "the per-layer exchanges between the two GPUs are not part of this single-GPU run",
     "continuous": "same 48-layer model under continuous batching: arrivals every ~64 steps (exponential gaps), "
                   "geometric output lengths (mean 256), prefixes log-uniform in [512, 65536], LIFO page free list, "
                   "live batch 1-8, task list rebuilt every step on the host while the previous step runs",

@@ -68,6 +68,11 @@ class Shape:
 
 TINY = Shape(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, d_head=64, n_experts=8, top_k=2, d_ffn=512, vocab=4096)
 FULL = Shape(n_layers=48, d_model=2048, n_q_heads=32, n_kv_heads=4, d_head=128, n_experts=128, top_k=8, d_ffn=768, vocab=262144)
+# One GPU's share of FULL under 2-way tensor parallelism (half the query and KV heads, half of every expert's
+# d_ffn, half the vocabulary; d_model, layers, experts and top-k unchanged): the kernel a GPU would run between
+# the per-layer exchanges.  Its synthetic weights come from the same generator (same distributions), drawn for
+# this shape.
+TP2 = Shape(n_layers=48, d_model=2048, n_q_heads=16, n_kv_heads=2, d_head=128, n_experts=128, top_k=8, d_ffn=384, vocab=131072)
 GAIN_SIGMA = 0.1
 
 
@@ -92,8 +97,9 @@ def start_tokens(shape: Shape, B: int):
 
 
 def make(name: str, steps: int | None = None) -> Workload:
-    """The named workloads: tiny, b1_8k, b8_ragged_uniform, b8_ragged_skewed, long_64k, long_128k, long_256k;
-    a name ending in "_gains" is the same workload with non-unit RMSNorm gains."""
+    """The named workloads: tiny, b1_8k, b8_ragged_uniform, b8_ragged_skewed, long_64k, long_128k, long_256k,
+    tp2_b1_8k (b1_8k on one GPU's share of the model under 2-way tensor parallelism); a name ending in "_gains"
+    is the same workload with non-unit RMSNorm gains."""
     if name.endswith("_gains"):
         w = make(name[:-len("_gains")], steps)
         w.name = name
@@ -106,6 +112,8 @@ def make(name: str, steps: int | None = None) -> Workload:
                      shuffle_pages=True, extra_pages=3)
     elif name == "b1_8k":
         w = Workload(name, FULL, [8192], 128 if steps is None else steps)
+    elif name == "tp2_b1_8k":
+        w = Workload(name, TP2, [8192], 128 if steps is None else steps)
     elif name in ("b8_ragged_uniform", "b8_ragged_skewed"):
         ctx = [int(v) for v in synth.loguniform_ints(SEED_LEN, 0, 8, 1024, 32768)]
         bias = synth.skew_bias(SEED_PERM, FULL.n_experts, 1.5) if name.endswith("skewed") else None

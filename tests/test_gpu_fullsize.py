@@ -130,6 +130,13 @@ def test_full_b1_8k_valu_gemv():
 
 
 @pytest.mark.timeout(600)
+def test_full_tp2_shard_b1_8k():
+    """One GPU's share of the model under 2-way tensor parallelism (16 q / 2 KV heads, d_ffn 384, vocab 131072):
+    the same kernel classes at the shard's shape, same bar."""
+    _run("tp2_b1_8k", steps=4, teacher_forced_step=0)
+
+
+@pytest.mark.timeout(600)
 def test_full_b1_8k_gains():
     """Non-unit RMSNorm gains at full size (every layer's gain and the final norm's differ)."""
     _run("b1_8k_gains", steps=3, teacher_forced_step=0)
