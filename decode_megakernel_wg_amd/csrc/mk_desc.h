@@ -12,9 +12,11 @@ enum Op : int32_t {
   OP_EMBED = 1,   // x[b][rows] = embed[token_b][rows]; partial sum of squares of the rows  -> XREADY[0]
   OP_QKV = 3,     // rows [r0, r1) of KV group g's fused [q heads; k; v] projection     -> QKV_DONE[l][g]
   OP_ATTN = 4,    // split s of (sequence b, KV group g): partial softmax(qK^T)V; last arriver combines -> ATTN_DONE[l][g]
+                  // (with merge tasks: every split counts itself into ATTN_ARRIVE[l][b][g] instead)
   OP_UP = 5,      // gate+up rows [r0, r1) of expert slot s, SwiGLU (waits SLOT_READY)     -> UP_DONE[l][s]
   OP_OPROJ = 6,   // rows [r0, r1) of Wo restricted to group g's columns; residual epilogue (see below)
-  OP_DOWN = 7     // rows [r0, r1) of expert slot s's down projection, times the gate; residual epilogue
+  OP_DOWN = 7,    // rows [r0, r1) of expert slot s's down projection, times the gate; residual epilogue
+  OP_MERGE = 8    // heads [h0, h0 + nh) of (sequence b, KV group g): log-sum-exp merge of the splits -> ATTN_DONE[l][g]
 };
 // The router is not a task (the last residual row tile of a layer routes the next), nor is the residual add
 // (the epilogue of a row tile's last O-proj or down-projection task), nor the LM head (the kernel's closing
@@ -24,10 +26,10 @@ enum Op : int32_t {
 enum Word : int {
   W_OP = 0,
   W_LAYER = 1,
-  W_A = 2,  // EMBED: row tile; QKV/OPROJ: KV group; UP/DOWN: slot; ATTN: sequence
-  W_B = 3,  // ATTN: KV group
-  W_C = 4,  // ATTN: split index
-  W_D = 5,  // ATTN: split count
+  W_A = 2,  // EMBED: row tile; QKV/OPROJ: KV group; UP/DOWN: slot; ATTN, MERGE: sequence
+  W_B = 3,  // ATTN, MERGE: KV group
+  W_C = 4,  // ATTN: split index; MERGE: first head of the group it merges
+  W_D = 5,  // ATTN, MERGE: split count
   W_R0 = 6,
   W_R1 = 7,
   W_WAIT0 = 8,  // 4 waits of (counter, target): words 8..15; counter -1 = none
@@ -67,6 +69,16 @@ constexpr int ATTN_MAX_SPLIT_POS = 4096;  // most positions per split the planne
 constexpr int ATTN_MAX_SPLIT_PAGES = 512;  // pages one split may cover (its page list is staged in LDS; the
                                            // last split of a sequence also takes the growth since planning)
 constexpr int ATTN_MAX_SPLITS = 256;
+// Long contexts merge their splits in separate tasks: from ATTN_MERGE_MIN_SPLITS splits of one sequence on,
+// the partials of every (sequence, KV group) are merged by up to ATTN_MERGE_TASKS tasks, one per head of the
+// group (at most), instead of by the split that arrives last.  One workgroup reads other workgroups' fresh
+// partials at only about 10 GB/s (measured), so a last-arriver merge of about 48 splits (200 KB) takes about
+// 10 us; one head per task reads an eighth of it, at the cost of one more hop.
+constexpr int ATTN_MERGE_MIN_SPLITS = 33;
+constexpr int ATTN_MERGE_TASKS = 8;
+// A merge task stages its heads' rows of every split ((d_head + 2) floats each) in LDS; a plan whose rows
+// exceed the area uses the last-arriver merge.
+constexpr int ATTN_MERGE_STAGE_FLOATS = 16640;  // 128 splits x 1 head x (128 + 2) floats
 constexpr int SLOT_WORDS = 32;
 constexpr int LM_MAX_WG = 1024;  // most workgroups a launch may have (stride of the LM head's per-workgroup bests)  // routing table entry per expert slot: expert, token count, (token, rank, gate) x 8
 

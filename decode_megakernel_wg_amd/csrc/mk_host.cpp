@@ -155,6 +155,7 @@ int mk_load_model(const mk_model_desc* desc, const mk_weights* w, mk_model** out
   cl.build(L, Hkv, maxB, m->max_slots, t.n_rt);
   m->max_counters = cl.total;
   m->max_tasks = (int64_t)t.n_rt + (int64_t)L * (t.n_router + Hkv * t.n_qkv_per_group + (int64_t)Hkv * maxB * mk::ATTN_MAX_SPLITS +
+                                                 (int64_t)Hkv * maxB * grp +  /* merge tasks: at most one per head */
                                                  (int64_t)m->max_slots * n_up_max + Hkv * t.n_rt + (int64_t)m->max_slots * t.n_rt + t.n_rt) +
                  t.n_lm;
 
@@ -206,7 +207,7 @@ int mk_build_tasks(mk_model* m, const mk_batch* batch, int32_t* tasks_out, int64
   if (!m || !n_tasks) return fail(MK_E_INVAL, "null handle or n_tasks");
   std::string msg;
   mk::Plan P;
-  int rc = mk::plan_step(&m->desc, batch, &P, &msg);
+  int rc = mk::plan_step(&m->desc, batch, &P, &msg, (m->dbg & MK_DBG_MERGE_TASKS) != 0);
   if (rc) return fail(rc, msg);
   *n_tasks = P.n_tasks();
   if (P.n_tasks() > m->max_tasks) return fail(MK_E_INVAL, "task list larger than the handle's bound");

@@ -1447,11 +1447,16 @@ __device__ __forceinline__ uint32_t* walk_rec(KA& a, int l, int b, int g) {
   return a.pagewalk ? a.pagewalk + (((int64_t)l * a.B + b) * a.Hkv + g) * 4 : nullptr;
 }
 
-// The last split of (b, g) to finish merges all splits (log-sum-exp) and publishes the group's output.
+// The last split of (b, g) to finish merges all splits (log-sum-exp) and publishes the group's output.  In
+// a plan with merge tasks (no arrival counter) the split only counts its published partial.
 template <int DH, int GRP>
 __device__ __forceinline__ void attn_merge(KA& a, Desc w, int t, int b, int g, int nsplit, Lds& S) {
   const int tid = tidx(), wave = tid >> 6, lane = tid & 63;
   const int Hkv = a.Hkv;
+  if (w[W_ARR] < 0) {
+    signal(a, w[W_SIG], w[W_SIGN]);
+    return;
+  }
   if (arrive_last(a, w[W_ARR], w[W_ARRN], S)) {
     mark(a, t, 3);
     const float* p0 = a.apart + (((int64_t)b * Hkv + g) * a.apart_stride) * GRP * (DH + 2);
@@ -1514,6 +1519,74 @@ __device__ __forceinline__ void attn_merge(KA& a, Desc w, int t, int b, int g, i
     if (has1) pub(a.attn_o + (int64_t)b * a.Hq * DH + ((int64_t)g * GRP + h1) * DH + d1, o1 / lsum[h1]);
     signal(a, w[W_SIG], w[W_SIGN]);
   }
+}
+
+// MERGE task: heads [h0, h0 + nh) of (sequence b, KV group g), once every split of (b, g) has published its
+// partial.  The arithmetic is the last-arriver merge's, operation for operation (per head: the maximum, the
+// weights and their sum on one wave; per output: the splits added in order, then one division), so both
+// give the same bits; a long context's partials (about 200 KB per group) are then read by several
+// workgroups instead of one.  The slice of every split (nh rows of o, maximum and sum) is copied straight
+// into LDS in one round trip, 16 bytes per lane (4 where a slice is not a whole number of 16-byte chunks).
+template <int DH, int GRP>
+__device__ __forceinline__ void task_merge(KA& a, Desc w, int t, Lds& S) {
+  const int tid = tidx(), wave = tid >> 6, lane = tid & 63;
+  const int b = w[W_A], g = w[W_B], h0 = w[W_C], nh = w[W_R0];
+  const int nsplit = min((int)w[W_D], a.apart_stride);
+  constexpr int ROWF = DH + 2;            // floats per head row of a partial: o, running max, running sum
+  constexpr int CHB = ROWF % 4 == 0 ? 16 : 4;  // bytes per direct load
+  const int row = nh * ROWF;              // floats of one split's slice (contiguous in the partials)
+  static_assert(sizeof(S.xb) / 4 >= ATTN_MERGE_STAGE_FLOATS, "the merge staging area holds what the planner allows");
+  if (nh < 1 || h0 < 0 || h0 + nh > GRP || nh * DH > NT || nsplit * row > ATTN_MERGE_STAGE_FLOATS) {
+    if (tid == 0) raise_error(a, ERRC_OPCODE, t);
+    return;
+  }
+  wait_deps(a, w, 0, N_WAITS, t);
+  mark(a, t, 0);
+  const float* p0 = a.apart + (((int64_t)b * a.Hkv + g) * a.apart_stride) * GRP * ROWF;
+  float* st = reinterpret_cast<float*>(S.xb);  // [nsplit][nh][ROWF]
+  if (tid == 0) S.xb_layer = 0;                 // the staged GEMV input is overwritten
+  {
+    constexpr int CF = CHB / 4;                 // floats per chunk
+    const int per = row / CF, n = nsplit * per;
+    for (int c0 = wave * 64; c0 < n; c0 += NT) {
+      const int c = c0 + lane;
+      if (c < n) {
+        const int q = c / per, k = c - q * per;
+        const auto src = (const __attribute__((address_space(1))) void*)(p0 + ((int64_t)q * GRP + h0) * ROWF + k * CF);
+        const auto dst = (__attribute__((address_space(3))) void*)(st + (int64_t)c0 * CF);
+        if constexpr (CHB == 16) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+        else __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+      }
+    }
+  }
+  drain_stores();
+  __syncthreads();
+  float* wsc = S.xs;                               // [nh][nsplit] weights exp(m_s - M)
+  float* lsum = S.xs + GRP * ATTN_MAX_SPLITS;      // [nh]
+  if (wave < nh) {
+    const int h = wave;
+    float M = -INFINITY;
+    for (int q = lane; q < nsplit; q += 64) M = fmaxf(M, st[q * row + h * ROWF + DH]);
+    M = wave_max(M);
+    float Ls = 0.f;
+    for (int q = lane; q < nsplit; q += 64) {
+      const float mq = st[q * row + h * ROWF + DH];
+      const float wq = mq == -INFINITY ? 0.f : expf(mq - M);
+      wsc[h * nsplit + q] = wq;
+      Ls = fmaf(st[q * row + h * ROWF + DH + 1], wq, Ls);
+    }
+    Ls = wave_sum(Ls);
+    if (lane == 0) lsum[h] = Ls;
+  }
+  __syncthreads();
+  mark(a, t, 1);
+  if (tid < nh * DH) {
+    const int hl = tid / DH, d = tid - hl * DH;
+    float o = 0.f;
+    for (int q = 0; q < nsplit; ++q) o = fmaf(st[q * row + hl * ROWF + d], wsc[hl * nsplit + q], o);
+    pub(a.attn_o + (int64_t)b * a.Hq * DH + ((int64_t)g * GRP + h0 + hl) * DH + d, o / lsum[hl]);
+  }
+  signal(a, w[W_SIG], w[W_SIGN]);
 }
 
 // d_head 64 (the tiny shape; d_head 128 runs attn_split_w below): split s of (sequence b, KV group g)
@@ -2183,6 +2256,7 @@ __device__ __forceinline__ void run_task(KA* a0, Desc w, int t, Lds& S) {
     case OP_UP: task_up<C>(a, w, t, S); break;
     case OP_OPROJ: task_oproj<C>(a, w, t, S); break;
     case OP_DOWN: task_down<C>(a, w, t, S); break;
+    case OP_MERGE: task_merge<C::DH, C::GRP>(a, w, t, S); break;
     default:
       if (tid == 0) raise_error(a, ERRC_OPCODE, t);
   }

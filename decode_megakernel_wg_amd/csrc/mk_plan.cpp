@@ -4,8 +4,8 @@
 // task list: each task is one operation on one tile, and dependencies are counters, not kernel
 // boundaries (agenticcommons.xyz "Cohere North Mini Code megakernel serving engine", section
 // Megakernel 的運作方式).  The list is the embedding row tiles, then per layer
-//   QKV tiles, ATTN splits, expert UP tiles, OPROJ tiles, expert DOWN tiles
-// (the router is the residual epilogue's last row tile, the residual add the epilogue of the last O-proj or
+//   QKV tiles, ATTN splits, expert UP tiles, [MERGE tasks,] OPROJ tiles, expert DOWN tiles
+// (MERGE tasks only for long contexts, whose split-KV partials are merged in parallel; the router is the residual epilogue's last row tile, the residual add the epilogue of the last O-proj or
 // down-projection task of a row tile, and the LM head the kernel's closing phase: none of them is a task).
 // Workgroups take the next layer's QKV, attention and up-projection tiles and start their weight (and old
 // K/V) loads while the current layer's tail still runs (same page, section 三個實際的加速來源, item 3), the
@@ -147,7 +147,7 @@ void resid_epilogue(int32_t* w, const CounterLayout& cl, const Tiling& t, int l,
 }
 }  // namespace
 
-int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::string* msg) {
+int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::string* msg, bool force_merge) {
   int rc = validate_desc(d, msg);
   if (rc) return rc;
   if (!batch || !batch->seq_lens) {
@@ -201,9 +201,16 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
     const int64_t s = (std::max<int64_t>(cached[b], 1) + split_pos - 1) / split_pos;
     P->splits[b] = (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, ATTN_MAX_SPLITS));
   }
+  // merge tasks: when a sequence has many splits (long contexts), or when asked for (tests); each stages its
+  // heads' rows of every split of its sequence in LDS, so a slice takes fewer heads as the splits grow
+  const int grp = d->n_q_heads / Hkv;
+  const int max_splits = *std::max_element(P->splits.begin(), P->splits.end());
+  int n_merge = std::min(ATTN_MERGE_TASKS, grp);  // merge tasks per (sequence, KV group): grp is a power of two
+  while (n_merge < grp && (int64_t)max_splits * (grp / n_merge) * (d->d_head + 2) > ATTN_MERGE_STAGE_FLOATS) n_merge *= 2;
+  P->merge = (force_merge || max_splits >= ATTN_MERGE_MIN_SPLITS) &&
+             (int64_t)max_splits * (grp / n_merge) * (d->d_head + 2) <= ATTN_MERGE_STAGE_FLOATS;
   P->desc.clear();
   Emitter em{&P->desc};
-  const int grp = d->n_q_heads / Hkv;
 
   for (int r = 0; r < t.n_rt; ++r) {
     int32_t* w = em.add(OP_EMBED, 0);
@@ -237,9 +244,27 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
             w[W_D] = P->splits[b];
             w[W_R0] = (int32_t)split_pos;  // cached positions per split (the last one takes the rest)
             set_wait(w, 0, cl.qkv_done + l * Hkv + g, t.n_qkv_per_group);
-            set_sig(w, cl.attn_done + l * Hkv + g);  // issued only by the split that arrives last
-            w[W_ARR] = cl.attn_arrive + (l * B + b) * Hkv + g;
-            w[W_ARRN] = P->splits[b];
+            if (P->merge) {
+              set_sig(w, cl.attn_arrive + (l * B + b) * Hkv + g);  // counted; merged by the MERGE tasks
+            } else {
+              set_sig(w, cl.attn_done + l * Hkv + g);  // issued only by the split that arrives last
+              w[W_ARR] = cl.attn_arrive + (l * B + b) * Hkv + g;
+              w[W_ARRN] = P->splits[b];
+            }
+          }
+    };
+    auto emit_merge = [&] {
+      for (int g = 0; g < Hkv; ++g)
+        for (int b = 0; b < B; ++b)
+          for (int m = 0; m < n_merge; ++m) {
+            int32_t* w = em.add(OP_MERGE, l);
+            w[W_A] = b;
+            w[W_B] = g;
+            w[W_C] = m * (grp / n_merge);  // first head of the slice
+            w[W_D] = P->splits[b];
+            w[W_R0] = grp / n_merge;       // heads of the slice
+            set_wait(w, 0, cl.attn_arrive + (l * B + b) * Hkv + g, P->splits[b]);
+            set_sig(w, cl.attn_done + l * Hkv + g);
           }
     };
     auto emit_up = [&] {
@@ -262,7 +287,7 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
           w[W_A] = g;
           w[W_R0] = r * t.rt;
           w[W_R1] = (r + 1) * t.rt;
-          set_wait(w, 0, cl.attn_done + l * Hkv + g, B);
+          set_wait(w, 0, cl.attn_done + l * Hkv + g, P->merge ? B * n_merge : B);
           resid_epilogue(w, cl, t, l, r, Hkv + P->n_slots);
         }
     };
@@ -278,16 +303,17 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
           resid_epilogue(w, cl, t, l, r, Hkv + P->n_slots);
         }
     };
-    // per layer: QKV tiles, attention splits, expert up-projection tiles, O-projection tiles, expert
-    // down-projection tiles (topological; as phases, the attention splits are taken first so that their
-    // old K/V stream while the QKV tiles run, and measured faster than the up-projections first)
+    // per layer: QKV tiles, attention splits, expert up-projection tiles, (merge tasks,) O-projection tiles,
+    // expert down-projection tiles (topological; as phases, the attention splits are taken first so that
+    // their old K/V stream while the QKV tiles run, and measured faster than the up-projections first; the
+    // merge tasks follow the up-projection tiles, which are taken about when the splits' partials land)
     emit_qkv();
     emit_attn();
     emit_up();
+    if (P->merge) emit_merge();
     emit_oproj();
     emit_down();
   }
-  (void)grp;
   return MK_OK;
 }
 

@@ -25,6 +25,7 @@ struct Plan {
   Tiling t{};
   CounterLayout cl{};
   std::vector<int32_t> splits;  // attention splits per sequence
+  bool merge = false;           // split-KV partials merged by MERGE tasks (else by each group's last split)
   std::vector<int32_t> desc;    // n_tasks * DESC_WORDS
   int64_t n_tasks() const { return (int64_t)desc.size() / DESC_WORDS; }
 };
@@ -33,6 +34,7 @@ struct Plan {
 int validate_desc(const mk_model_desc* d, std::string* msg);
 // Tile sizes for a batch of `batch` sequences (only the expert up-projection tiles depend on it).
 Tiling choose_tiling(const mk_model_desc* d, int batch);
-int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* out, std::string* msg);
+// force_merge: merge tasks whatever the split counts (otherwise only from ATTN_MERGE_MIN_SPLITS splits on).
+int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* out, std::string* msg, bool force_merge = false);
 
 }  // namespace mk

@@ -25,6 +25,7 @@ MK_DBG_PAGE_WALK = 8
 MK_DBG_DROP_SIGNAL = 16
 MK_DBG_VALU_GEMV = 32
 MK_DBG_COUNT_TASKS = 64
+MK_DBG_MERGE_TASKS = 128
 MK_DBGK_ROUTE_SEL, MK_DBGK_ROUTE_GATE, MK_DBGK_ROUTER_LOGITS, MK_DBGK_NORM_IN, MK_DBGK_COUNTERS, MK_DBGK_TASK_DONE = 1, 2, 3, 4, 5, 6
 MK_DBGK_TIMESTAMPS = 7
 MK_DBGK_PAGE_WALK = 8

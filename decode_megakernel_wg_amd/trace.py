@@ -20,7 +20,7 @@ import time
 
 import numpy as np
 
-OPS = {1: "EMBED", 3: "QKV", 4: "ATTN", 5: "UP", 6: "OPROJ", 7: "DOWN"}
+OPS = {1: "EMBED", 3: "QKV", 4: "ATTN", 5: "UP", 6: "OPROJ", 7: "DOWN", 8: "MERGE"}
 TICK_US = 0.01  # 100 MHz
 
 
@@ -80,7 +80,7 @@ def summarize(w, tasks, ts, plain_ms, traced_ms):
               "marks after the waits (median) |",
               "|---|---|---|---|---|---|"]
     mid = range(1, L - 1)
-    for o in (3, 4, 5, 6, 7):
+    for o in (3, 4, 5, 8, 6, 7):
         rows = {"claim": [], "met": [], "end": [], "cl_max": [], "met_max": [], "end_max": []}
         marks = [[] for _ in range(4)]
         cnt = 0  # tasks of the kind that ran in a layer (the last layer seen)
@@ -113,7 +113,8 @@ def summarize(w, tasks, ts, plain_ms, traced_ms):
                          f"{md['end']:+.1f}, {md['end_max']:+.1f} | {mtxt} |")
     lines += ["", "Times in us relative to the layer's input being complete (negative: before it).  Marks: GEMV tiles "
               "m0 = inputs staged, m1 = tile computed, m2 (UP) = expert weights requested; attention m0 = queries "
-              "staged, m1 = cached positions done, m2 = partials published, m3 = merge started (last split only)."]
+              "staged, m1 = cached positions done, m2 = partials published, m3 = merge started (last split only, when no "
+              "merge tasks); merge tasks m0 = waits ended, m1 = the splits' weights formed (partials landed)."]
     # per compute unit: time in task bodies (waits met), in waits, outside tasks, over the recorded span
     cu = (ts[:, 3] >> 32) * 65536 + ((ts[:, 3] >> 8) & 0xFFFF)
     keys = np.unique(cu[ran])

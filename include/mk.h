@@ -200,7 +200,12 @@ int mk_status(mk_model* m, void* stream);
  * separate instructions accumulating into one sum), so that a sequence's results then equal, bit for bit,
  * its results inside a larger batch; without it the two batch classes agree to rounding only. */
 enum { MK_DBG_DUMP_N = 1, MK_DBG_TIMESTAMPS = 2, MK_DBG_WIDE_GEMV = 4, MK_DBG_PAGE_WALK = 8, MK_DBG_DROP_SIGNAL = 16,
-       MK_DBG_VALU_GEMV = 32, MK_DBG_COUNT_TASKS = 64 };
+       MK_DBG_VALU_GEMV = 32, MK_DBG_COUNT_TASKS = 64, MK_DBG_MERGE_TASKS = 128 };
+/* MK_DBG_MERGE_TASKS makes the following mk_build_tasks plan merge tasks whatever the split counts.  By default
+ * the split-KV partials of a (sequence, KV group) are merged by the split that arrives last, and only a plan
+ * with a sequence of 33 splits or more (long contexts) merges them in separate tasks, one per head of each
+ * (sequence, KV group) (none when a sequence has more than 128 splits at d_head 128).  Both give the same
+ * results, bit for bit. */
 /* MK_DBG_COUNT_TASKS counts every task's completions (MK_DBGK_TASK_DONE). */
 /* MK_DBG_VALU_GEMV runs the GEMV tiles of a batch of one sequence on the VALU (fp32 FMAs on the same loads and
  * the same hi + lo activations) instead of the matrix cores, to compare the two engines; results agree to
@@ -255,7 +260,7 @@ int mk_free_model(mk_model* m);
 const char* mk_last_error(void);
 
 /* Pure host planning, for tools and tests (no device needed): the task list mk_build_tasks would emit
- * for `desc` and `batch`, in topological order (the order the workgroups take it in).  n_tasks receives the
+ * for `desc` and `batch` (without MK_DBG_MERGE_TASKS), in topological order (the order the workgroups take it in).  n_tasks receives the
  * task count, n_counters (nullable) the counter count; tasks_out may be null to query the sizes.
  * Errors: MK_E_INVAL (bad shape or batch), MK_E_RANGE (cap smaller than the task count).
  * Passage: as mk_build_tasks.

@@ -97,7 +97,7 @@ def start_tokens(shape: Shape, B: int):
 
 
 def make(name: str, steps: int | None = None) -> Workload:
-    """The named workloads: tiny, b1_8k, b8_ragged_uniform, b8_ragged_skewed, long_64k, long_128k, long_256k,
+    """The named workloads: tiny, tiny_ragged, tiny_long, b1_8k, b8_ragged_uniform, b8_ragged_skewed, long_64k, long_128k, long_256k,
     tp2_b1_8k (b1_8k on one GPU's share of the model under 2-way tensor parallelism); a name ending in "_gains"
     is the same workload with non-unit RMSNorm gains."""
     if name.endswith("_gains"):
@@ -107,6 +107,8 @@ def make(name: str, steps: int | None = None) -> Workload:
         return w
     if name == "tiny":
         w = Workload(name, TINY, [128], 16 if steps is None else steps, extra_pages=2)
+    elif name == "tiny_long":  # enough positions for the planner's merge tasks (43 splits of 384 per KV group)
+        w = Workload(name, TINY, [16384], 4 if steps is None else steps, extra_pages=2)
     elif name == "tiny_ragged":
         w = Workload(name, TINY, [int(v) for v in synth.loguniform_ints(SEED_LEN, 0, 8, 16, 512)], 16 if steps is None else steps,
                      shuffle_pages=True, extra_pages=3)

@@ -79,11 +79,14 @@ def check_page_walks(h, shape, pt, lens, first_of=None):
                 assert np.array_equal(rec[l, b, g], want), f"layer {l} entry {b} KV group {g}: walk {rec[l, b, g]} want {want}"
 
 
-def check_task_graph(h, shape, desc, lens, grid, slot_values, first_of=None):
-    """lens / first_of: those the handle's task list was built with (a list stays valid while lengths grow)."""
+def check_task_graph(h, shape, desc, lens, grid, slot_values, first_of=None, tasks=None):
+    """lens / first_of: those the handle's task list was built with (a list stays valid while lengths grow);
+    tasks: the handle's own list when it was planned with a debug switch that changes it (default: the list
+    mk_plan_tasks gives for lens)."""
     from decode_megakernel_wg_amd import mk
 
-    tasks, n_ctr = mk.mk_plan_tasks(desc, lens, first_of)
+    planned, n_ctr = mk.mk_plan_tasks(desc, lens, first_of)
+    tasks = planned if tasks is None else tasks
     B = len(lens)
     n_slots = min(shape.n_experts, B * shape.top_k)
     done = h.mk_debug_read(mk.MK_DBGK_TASK_DONE, (len(tasks),), np.uint32)
@@ -100,15 +103,16 @@ def device_grid():
     return min(torch.cuda.get_device_properties(0).multi_processor_count, 1024)
 
 
-def check_step(h, shape, desc, pt, lens, grid=None, first_of=None, walks=True, plan_lens=None):
+def check_step(h, shape, desc, pt, lens, grid=None, first_of=None, walks=True, plan_lens=None, tasks=None):
     """All of the above for the step just run (the handle must have MK_DBG_PAGE_WALK set when walks);
-    plan_lens: the lengths the task list was built with (default: this step's)."""
+    plan_lens: the lengths the task list was built with (default: this step's); tasks: the handle's list
+    (check_task_graph)."""
     B = len(lens)
     slot_values = check_routing(h, shape, B)
     if walks:
         check_page_walks(h, shape, pt, lens, first_of)
     check_task_graph(h, shape, desc, lens if plan_lens is None else plan_lens, device_grid() if grid is None else grid, slot_values,
-                     first_of)
+                     first_of, tasks)
 
 
 KV_DRIFT_FIRST = 1e-5

@@ -13,7 +13,7 @@ import numpy as np
 
 W_OP, W_LAYER, W_A, W_B, W_C, W_D, W_R0, W_R1, W_WAIT0, W_SIG, W_SIGN, W_ARR, W_ARRN, W_SIGR = 0, 1, 2, 3, 4, 5, 6, 7, 8, 16, 17, 18, 19, 20
 W_RT, W_ARR2, W_ARRN2, W_RSIG, W_RSIGR = 22, 24, 25, 26, 27
-OP_EMBED, OP_QKV, OP_ATTN, OP_UP, OP_OPROJ, OP_DOWN = 1, 3, 4, 5, 6, 7
+OP_EMBED, OP_QKV, OP_ATTN, OP_UP, OP_OPROJ, OP_DOWN, OP_MERGE = 1, 3, 4, 5, 6, 7, 8
 UNUSED_SLOT = 0x80000000
 
 

@@ -9,7 +9,7 @@ import pytest
 
 from decode_megakernel_wg_amd import mk
 from synth import workloads as W
-from taskgraph import (OP_ATTN, OP_EMBED, W_ARR, W_D, W_LAYER, W_OP, W_R0, W_R1, W_SIG, W_WAIT0, complete, counter_layout,
+from taskgraph import (OP_ATTN, OP_EMBED, OP_MERGE, W_ARR, W_C, W_D, W_LAYER, W_OP, W_R0, W_R1, W_SIG, W_WAIT0, complete, counter_layout,
                        phases_of, simulate)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -63,7 +63,8 @@ def test_batch_validation():
         mk.mk_plan_tasks(d, [-1])
 
 
-@pytest.mark.parametrize("name,B_lens", [("tiny", [128]), ("tiny", [5, 300, 17, 0]), ("full", [8192]),
+@pytest.mark.parametrize("name,B_lens", [("tiny", [128]), ("tiny", [5, 300, 17, 0]), ("tiny", [16384]), ("full", [8192]),
+                                         ("full", [65536]),
                                          ("full", [1024, 30000, 4000, 70000, 2000, 9000, 1500, 12000])])
 def test_task_list_is_a_deadlock_free_topological_order(name, B_lens):
     shape = W.TINY if name == "tiny" else W.FULL
@@ -124,6 +125,23 @@ def test_task_counts_full_model():
         tl, _ = mk.mk_plan_tasks(dl, [ctx])
         al = tl[(tl[:, W_OP] == 4) & (tl[:, 1] == 0)]
         assert (al[:, W_R0] == pos).all() and len(al) == 4 * -(-ctx // pos)
+    # merge tasks from 33 splits of one sequence on (long contexts): one per head of each (sequence, KV group), after
+    # the up-projection tiles; the splits then only count themselves, and each O-projection tile waits for its
+    # group's eight merges
+    assert ops[8] == 0
+    for ctx in (65536, 131072, 262144):
+        dl = desc_for(W.FULL, B=1, pages=ctx // 16 + 64, n_pages=ctx // 16 + 64)
+        tl, _ = mk.mk_plan_tasks(dl, [ctx])
+        m0 = tl[(tl[:, W_OP] == 8) & (tl[:, 1] == 0)]
+        a0 = tl[(tl[:, W_OP] == 4) & (tl[:, 1] == 0)]
+        ns = len(a0) // 4
+        assert len(m0) == 32 and sorted(m0[:, W_C].tolist()) == sorted(list(range(8)) * 4)
+        assert (m0[:, W_R0] == 1).all() and (m0[:, W_D] == ns).all() and (a0[:, W_ARR] == -1).all()
+        assert (ctx, ns) in ((65536, 47), (131072, 49), (262144, 64))
+        o0 = tl[(tl[:, W_OP] == 6) & (tl[:, 1] == 0)]
+        assert (o0[:, W_WAIT0 + 1] == 8).all()
+        runs = [int(tl[r[0], W_OP]) for r in phases_of(tl)[1:7]]
+        assert runs == [3, 4, 5, 8, 6, 7]
     # expert up-projection tiles: 48 gate + 48 up rows at batches of 1-2 (16 tiles per expert), 64 + 64 above
     up = tasks[tasks[:, W_OP] == 5]
     assert ops[5] == 48 * 8 * 16 and ((up[:, W_R1] - up[:, W_R0]) == 48).all()
@@ -133,7 +151,8 @@ def test_task_counts_full_model():
     assert ((up8[:, W_R1] - up8[:, W_R0]) == 64).all() and len(up8) == 48 * 64 * 12
 
 
-@pytest.mark.parametrize("name,B_lens", [("tiny", [128]), ("tiny", [5, 300, 17, 0]), ("full", [8192]),
+@pytest.mark.parametrize("name,B_lens", [("tiny", [128]), ("tiny", [5, 300, 17, 0]), ("tiny", [16384]), ("full", [8192]),
+                                         ("full", [65536]),
                                          ("full", [1024, 30000, 4000, 70000, 2000, 9000, 1500, 12000])])
 def test_task_list_has_the_regular_phase_structure(name, B_lens):
     """The kernel classifies its takes by the list's phase table (and passes over the expert tiles of unused
@@ -157,7 +176,8 @@ def test_task_list_has_the_regular_phase_structure(name, B_lens):
         assert all(int(tasks[t, W_LAYER]) == l for r in layer_runs for t in r)
 
 
-@pytest.mark.parametrize("shape,lens", [(W.TINY, [128]), (W.TINY, [5, 300, 17, 0]), (W.FULL, [8192]), (W.FULL, [100] * 8)])
+@pytest.mark.parametrize("shape,lens", [(W.TINY, [128]), (W.TINY, [5, 300, 17, 0]), (W.TINY, [16384]), (W.FULL, [8192]),
+                                        (W.FULL, [100] * 8)])
 def test_counter_layout_mirror(shape, lens):
     """The tests' copy of the counter layout gives the library's counter count, and every counter a descriptor
     names lies in the block its role belongs to."""
@@ -178,8 +198,12 @@ def test_counter_layout_mirror(shape, lens):
         op = w[W_OP]
         if op == 3:
             assert inside(w[W_WAIT0], "xready") and inside(w[W_SIG], "qkv_done")
-        if op == OP_ATTN:
+        if op == OP_ATTN and w[W_ARR] >= 0:
             assert inside(w[W_WAIT0], "qkv_done") and inside(w[W_ARR], "attn_arrive") and inside(w[W_SIG], "attn_done")
+        if op == OP_ATTN and w[W_ARR] < 0:  # merged by merge tasks: the split only counts itself
+            assert inside(w[W_WAIT0], "qkv_done") and inside(w[W_SIG], "attn_arrive")
+        if op == OP_MERGE:
+            assert inside(w[W_WAIT0], "attn_arrive") and inside(w[W_SIG], "attn_done")
         if op == 6:
             assert inside(w[W_WAIT0], "attn_done")
         if op == 5:

@@ -184,3 +184,35 @@ def test_full_grid_and_page_order_invariance():
         torch.cuda.empty_cache()
     for r in results[1:]:
         assert np.array_equal(r[0], results[0][0]) and np.array_equal(r[1], results[0][1]) and np.array_equal(r[2], results[0][2])
+
+
+@pytest.mark.timeout(600)
+def test_full_merge_tasks_bit_identical():
+    """b8 skewed (ragged contexts, 1 to 14 splits per sequence): the split-KV partials merged by separate merge
+    tasks over slices of each group's heads (MK_DBG_MERGE_TASKS; staged in LDS 16 bytes per lane at d_head 128)
+    give the last-arriver merge's logits, tokens and new K/V bit for bit."""
+    from decode_megakernel_wg_amd import mk
+    from decode_megakernel_wg_amd.session import Session
+
+    w = W.make("b8_ragged_skewed", steps=2)
+    pt, n_pages = W.page_tables(w)
+    model = W.DeviceModel(w.shape)
+    results = []
+    for flags in (0, mk.MK_DBG_MERGE_TASKS):
+        sess = Session(w, model=model, pt=pt, n_pages=n_pages)
+        sess.h.mk_debug_set(flags | mk.MK_DBG_PAGE_WALK | mk.MK_DBG_COUNT_TASKS)
+        tasks = sess.h.mk_build_tasks(sess.seq_rows_host[0], want_tasks=True)
+        assert ((tasks[:, 0] == 8).sum() > 0) == bool(flags)
+        out = []
+        for step in range(w.steps):
+            sess.step()
+            sess.status()
+            check_step(sess.h, w.shape, sess.desc, pt, sess.seq_rows_host[step], plan_lens=sess.seq_rows_host[0], tasks=tasks)
+            new_kv = np.stack([np.stack([_gpu_kv_at(sess, l, b, int(sess.seq_rows_host[step][b])) for b in range(w.B)])
+                               for l in (0, w.shape.n_layers - 1)])
+            out.append((sess.logits.cpu().numpy().copy(), sess.next_tokens().copy(), new_kv))
+        results.append(out)
+        del sess
+        torch.cuda.empty_cache()
+    for a, b in zip(results[0], results[1]):
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])

@@ -127,6 +127,43 @@ def test_tiny_ragged_odd_grid():
     run_parity(w, w.steps, grid=7, check_router_inputs=False)
 
 
+def test_tiny_long_context_merge_tasks():
+    """A context long enough for the planner's merge tasks (16384 positions: 43 splits per KV group, each
+    (sequence, group) merged by separate tasks over slices of its heads) against the oracle."""
+    from decode_megakernel_wg_amd import mk
+
+    w = W.make("tiny_long")
+    d = _session(w).desc
+    tasks, _ = mk.mk_plan_tasks(d, w.ctx)
+    assert (tasks[:, 0] == 8).sum() == w.shape.n_layers * w.shape.n_kv_heads * 2
+    sess, orc, worst = run_parity(w, w.steps)
+    print(f"tiny_long: worst logits rel L2 {worst:.2e}")
+    _check_kv(sess, orc)
+
+
+def test_tiny_merge_tasks_bit_identical():
+    """Merge tasks forced at short contexts (MK_DBG_MERGE_TASKS) give the last-arriver merge's results bit for
+    bit, on a ragged batch with shuffled pages, with every integer check against the handle's own list."""
+    from decode_megakernel_wg_amd import mk
+
+    w = W.make("tiny_ragged", steps=3)
+    pt, n_pages = W.page_tables(w)
+    outs = []
+    for flags in (0, mk.MK_DBG_MERGE_TASKS):
+        sess = _session(w, pt=pt, n_pages=n_pages)
+        sess.h.mk_debug_set(mk.MK_DBG_PAGE_WALK | mk.MK_DBG_COUNT_TASKS | flags)
+        tasks = sess.h.mk_build_tasks(sess.seq_rows_host[0], want_tasks=True)
+        assert ((tasks[:, 0] == 8).sum() > 0) == bool(flags)
+        logits = []
+        for step in range(w.steps):
+            sess.step()
+            sess.status()
+            check_step(sess.h, w.shape, sess.desc, pt, sess.seq_rows_host[step], plan_lens=sess.seq_rows_host[0], tasks=tasks)
+            logits.append(sess.logits.cpu().numpy().copy())
+        outs.append(np.stack(logits))
+    assert np.array_equal(outs[0], outs[1])
+
+
 def test_grid_size_and_page_order_invariance():
     w = W.make("tiny", steps=2)
     pt, n_pages = W.page_tables(w)
