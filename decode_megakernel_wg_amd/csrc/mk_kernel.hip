@@ -1527,8 +1527,10 @@ __device__ __forceinline__ void attn_merge(KA& a, Desc w, int t, int b, int g, i
 // give the same bits; a long context's partials (about 200 KB per group) are then read by several
 // workgroups instead of one.  The slice of every split (nh rows of o, maximum and sum) is copied straight
 // into LDS in one round trip, 16 bytes per lane (4 where a slice is not a whole number of 16-byte chunks).
+// Not inlined: inlined, it changed the register allocation of the 8-token class elsewhere (more spills;
+// batch 8 about 8 % slower, measured), and it runs a few times per layer at most.
 template <int DH, int GRP>
-__device__ __forceinline__ void task_merge(KA& a, Desc w, int t, Lds& S) {
+__device__ __attribute__((noinline)) void task_merge(KA& a, Desc w, int t, Lds& S) {
   const int tid = tidx(), wave = tid >> 6, lane = tid & 63;
   const int b = w[W_A], g = w[W_B], h0 = w[W_C], nh = w[W_R0];
   const int nsplit = min((int)w[W_D], a.apart_stride);
