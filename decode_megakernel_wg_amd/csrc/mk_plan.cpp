@@ -194,9 +194,14 @@ int plan_step(const mk_model_desc* d, const mk_batch* batch, Plan* P, std::strin
   auto round128 = [](int64_t v) { return (v + 64) / 128 * 128; };
   int64_t split_pos = std::max<int64_t>(ATTN_SPLIT_POS, round128((total * Hkv + ATTN_TARGET_TASKS / 2) / ATTN_TARGET_TASKS));
   // long contexts: about ATTN_LONG_TASKS splits (three quarters of the compute units), each of thousands
-  // of positions, which keeps the merges short and every wave streaming many blocks
-  if (split_pos > ATTN_LONG_MIN_POS)
-    split_pos = std::max<int64_t>(ATTN_LONG_MIN_POS, std::min<int64_t>(round128((total * Hkv + ATTN_LONG_TASKS / 2) / ATTN_LONG_TASKS), ATTN_MAX_SPLIT_POS));
+  // of positions, which keeps the merges short and every wave streaming many blocks; from
+  // ATTN_LONGER_MIN_POS positions per split on, about ATTN_LONGER_TASKS splits (the splits that start after
+  // the QKV tiles then cost less than the shorter splits save)
+  if (split_pos > ATTN_LONG_MIN_POS) {
+    int64_t sp = round128((total * Hkv + ATTN_LONG_TASKS / 2) / ATTN_LONG_TASKS);
+    if (sp >= ATTN_LONGER_MIN_POS) sp = round128((total * Hkv + ATTN_LONGER_TASKS / 2) / ATTN_LONGER_TASKS);
+    split_pos = std::max<int64_t>(ATTN_LONG_MIN_POS, std::min<int64_t>(sp, ATTN_MAX_SPLIT_POS));
+  }
   for (int b = 0; b < B; ++b) {
     const int64_t s = (std::max<int64_t>(cached[b], 1) + split_pos - 1) / split_pos;
     P->splits[b] = (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, ATTN_MAX_SPLITS));
