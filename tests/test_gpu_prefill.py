@@ -31,7 +31,7 @@ class Seqs:
     """Sequences with seeded prefixes in one paged KV pool on the device, their page-table rows, a handle, and
     the oracle over the same pool."""
 
-    def __init__(self, shape, prefixes, room, model=None):
+    def __init__(self, shape, prefixes, room, model=None, flags=0):
         from decode_megakernel_wg_amd import mk
 
         self.shape = s = shape
@@ -54,7 +54,8 @@ class Seqs:
                        wo=m.wo, w_router=m.w_router, w_gate=m.w_gate, w_up=m.w_up, w_down=m.w_down)
         self.desc = mk.make_desc(s, 8, self.max_pages, self.n_pages)
         self.h = mk.Model(self.desc, weights)
-        self.h.mk_debug_set(mk.MK_DBG_PAGE_WALK | mk.MK_DBG_COUNT_TASKS)
+        self.h.mk_debug_set(mk.MK_DBG_PAGE_WALK | mk.MK_DBG_COUNT_TASKS | flags)
+        self.own_list = bool(flags & mk.MK_DBG_MERGE_TASKS)  # the handle's list differs from mk_plan_tasks'
         self.logits = torch.empty(8, s.vocab, dtype=torch.float32, device="cuda")
         self.orc = OracleRun(W.Workload("prefill", s, list(prefixes), 1), self.rows, self.n_pages)
         self.worst = 0.0
@@ -74,7 +75,8 @@ class Seqs:
                 first[b] = first[b - 1]
         rows = self.rows[[q for q, _ in entries]]
         chunked = (first != np.arange(B)).any()
-        self.h.mk_build_tasks(lens, first_of=first if chunked else None)
+        tasks = self.h.mk_build_tasks(lens, want_tasks=self.own_list, first_of=first if chunked else None)
+        self.last_tasks = tasks
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()  # noqa: E731
         tok_d, len_d, first_d, rows_d = dev(tokens), dev(lens), dev(first), dev(rows)
         if chunked:
@@ -84,7 +86,8 @@ class Seqs:
         self.h.mk_status()
         logits = self.logits[:B].cpu().numpy()
         nxt = mk.read_device(self.h.mk_next_tokens(), 4 * B)
-        check_step(self.h, s, self.desc, rows, lens, first_of=first if chunked else None)
+        check_step(self.h, s, self.desc, rows, lens, first_of=first if chunked else None,
+                   tasks=tasks if self.own_list else None)
         gsel = self.h.mk_debug_read(mk.MK_DBGK_ROUTE_SEL, (s.n_layers, B, s.top_k), np.int32)
         self.orc.pt = rows
         ol, onx, _, _ = self.orc.step(list(tokens), lens.astype(np.int64), gpu_sel=gsel)
@@ -154,3 +157,20 @@ def test_mixed_full_size():
     sq.step([(0, 1004)], [nxt[3]])
     sq.finish()
     print(f"mixed full size: worst logits rel L2 {sq.worst:.2e}")
+
+
+def test_mixed_prefill_merge_tasks():
+    """Tiny model: an 8-token prompt chunk after a 2000-position prefix, with the splits of every entry merged by
+    merge tasks (MK_DBG_MERGE_TASKS: a chunk's entries share a layer's split budget, so a chunk alone never
+    reaches the planner's 33 splits), then two decode steps of the same sequence."""
+    from decode_megakernel_wg_amd import mk
+
+    sq = Seqs(W.TINY, [2000], 16, flags=mk.MK_DBG_MERGE_TASKS)
+    nxt = sq.step([(0, 2000 + i) for i in range(CHUNK)], prompt(CHUNK, 5000))
+    assert (sq.last_tasks[:, 0] == 8).sum() == W.TINY.n_layers * W.TINY.n_kv_heads * CHUNK * 2
+    tok = nxt[-1]
+    for i in range(2):
+        tok = sq.step([(0, 2000 + CHUNK + i)], [tok])[0]
+    sq.check_kv()
+    sq.finish()
+    print(f"prefill with merge tasks: worst logits rel L2 {sq.worst:.2e}")

@@ -53,3 +53,18 @@ def test_static_step_full_size_batch_1():
     sess = Session(w)
     (l0, n0, _), (l1, n1, _) = _both(sess, np.array(w.ctx, np.int32), sess.kvc.pt_host, 1)
     assert np.array_equal(l0, l1) and np.array_equal(n0, n1)
+
+
+def test_static_step_long_context_merge_tasks():
+    """A 16384-position context of the tiny model, whose plan merges the splits in merge tasks: the static step
+    equals the regular one bit for bit."""
+    from decode_megakernel_wg_amd import mk
+    from decode_megakernel_wg_amd.session import Session
+
+    w = W.make("tiny_long", steps=1)
+    sess = Session(w)
+    tasks, _ = mk.mk_plan_tasks(sess.desc, w.ctx)
+    assert (tasks[:, 0] == 8).any()
+    (l0, n0, kv0), (l1, n1, kv1) = _both(sess, np.array(w.ctx, np.int32), sess.kvc.pt_host, 1)
+    assert np.isfinite(l0).all()
+    assert np.array_equal(l0, l1) and np.array_equal(n0, n1) and torch.equal(kv0, kv1)
