@@ -10,6 +10,9 @@
 //     stores of the same count: the cost of summing partial results with order-independent integer atomics.
 //  3. Re-read bandwidth of a buffer that fits the 256 MB last-level cache, right after a full read of it,
 //     against a 4 GB read: whether a second read of recently streamed data comes back faster.
+//  4. How fast one workgroup reads a 4-64 KB payload that a workgroup on another XCD has just published (the
+//     kernel's convention: agent-coherent stores, drain, counter; the consumer polls, acquires, reads), by
+//     direct 16-byte global->LDS loads, 16-byte loads into registers and 4-byte loads into registers.
 //
 // Every wait is bounded (a spin limit, then an error flag and an exit), and every background reader stops at
 // a flag or after a fixed number of passes, so each kernel ends.
@@ -210,6 +213,111 @@ __global__ __launch_bounds__(256) void read_kernel(const u4* buf, int64_t n16, u
   if (acc == 0x12345u) out[1] = acc;
 }
 
+// 4. fresh payloads: round r publishes NW words at pay + r * NW (never read before); workgroup 1 produces,
+// workgroup 0 consumes; out[r] = consumer ticks from the acquire to every word read, out[64 + r] = wrong words.
+constexpr int FR_NT = 512;
+constexpr int FR_MAXW = 16384;  // words per payload (64 KB)
+struct FreshArgs {
+  float* pay;
+  uint32_t* ctr;  // [0] produced rounds, [32] consumed rounds, [64] stop, [96] error
+  const u4* bg;
+  int64_t bg_n16;
+  uint64_t* out;
+  int NW, R, path, bg_on;
+};
+__device__ bool fresh_wait(FreshArgs& p, uint32_t* c, uint32_t target) {
+  uint32_t n = 0;
+  while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    if (++n > SPIN_LIMIT) {
+      atomicExch(p.ctr + 96, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+__global__ __launch_bounds__(FR_NT, 1) void fresh_kernel(FreshArgs p) {
+  const int wg = blockIdx.x, tid = threadIdx.x;
+  __shared__ float lds[FR_MAXW];
+  __shared__ int ok;
+  __shared__ uint64_t t0;
+  if (wg == 1) {
+    for (int r = 0; r < p.R; ++r) {
+      if (tid == 0) ok = fresh_wait(p, p.ctr + 32, (uint32_t)r);
+      __syncthreads();
+      if (!ok) return;
+      float* d = p.pay + (int64_t)r * p.NW;
+      for (int j = tid; j < p.NW; j += FR_NT) __hip_atomic_store(d + j, (float)(r + j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(p.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+  if (wg == 0) {
+    for (int r = 0; r < p.R; ++r) {
+      if (tid == 0) {
+        ok = fresh_wait(p, p.ctr, (uint32_t)(r + 1));
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        t0 = wall_clock64();
+      }
+      __syncthreads();
+      if (!ok) return;
+      const float* d = p.pay + (int64_t)r * p.NW;
+      int bad = 0;
+      if (p.path == 0) {  // direct 16-byte global->LDS loads, every one in flight at once
+        const int n16 = p.NW / 4, wave = tid >> 6, lane = tid & 63;
+        for (int c0 = wave * 64; c0 < n16; c0 += FR_NT)
+          if (c0 + lane < n16)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(d + (int64_t)(c0 + lane) * 4),
+                                             (__attribute__((address_space(3))) void*)(lds + (int64_t)c0 * 4), 16, 0, 0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        for (int j = tid; j < p.NW; j += FR_NT) bad += lds[j] != (float)(r + j);
+      } else if (p.path == 1) {  // 16-byte loads into registers
+        for (int j = 4 * tid; j < p.NW; j += 4 * FR_NT) {
+          const u4 v = *(gu4*)(d + j);
+          bad += (__uint_as_float(v.x) != (float)(r + j)) + (__uint_as_float(v.w) != (float)(r + j + 3));
+        }
+      } else {  // 4-byte loads into registers
+        for (int j = tid; j < p.NW; j += FR_NT) bad += d[j] != (float)(r + j);
+      }
+      const int tb = __syncthreads_count(bad);
+      if (tid == 0) {
+        p.out[r] = wall_clock64() - t0;
+        p.out[64 + r] = (uint64_t)tb;
+        __hip_atomic_fetch_add(p.ctr + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (tid == 0) __hip_atomic_store(p.ctr + 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (!p.bg_on) return;
+  const int nbg = gridDim.x - 2, me = wg - 2;
+  const int64_t stripe = p.bg_n16 / nbg;
+  const u4* base = p.bg + (int64_t)me * stripe;
+  uint32_t acc = 0;
+  __shared__ int stop;
+  for (int pass = 0; pass < 1000; ++pass) {
+    for (int64_t o = 0; o + 16 * FR_NT <= stripe; o += 16 * FR_NT) {
+      u4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = __builtin_nontemporal_load((gu4*)(base + o + u * FR_NT + tid));
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc += v[u].x ^ v[u].w;
+      if ((o & (16 * FR_NT * 16 - 1)) == 0) {
+        if (tid == 0) stop = (int)__hip_atomic_load(p.ctr + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (stop) {
+          if (acc == 0x12345u) p.out[200] = acc;
+          return;
+        }
+      }
+    }
+  }
+  if (acc == 0x12345u) p.out[200] = acc;
+}
+
 int main() {
   CK(hipSetDevice(0));
   const int64_t bg_bytes = 4ll << 30;
@@ -311,6 +419,43 @@ int main() {
   float ms;
   CK(hipEventElapsedTime(&ms, e0, e1));
   printf("| 4096 MB (one read) | %.0f | | |\n", bg_bytes / ms / 1e6);
+
+  printf("\n## 4. Reading a payload another workgroup has just published (agent-coherent stores, drain, counter; poll, acquire)\n\n");
+  printf("| background HBM stream | consumer loads | payload | us from the acquire to the last word (median of 30 rounds) | GB/s | wrong words |\n|---|---|---|---|---|---|\n");
+  const int FR_R = 32;
+  float* pay;
+  uint64_t* fout;
+  CK(hipMalloc(&pay, (size_t)FR_R * FR_MAXW * 4));
+  CK(hipMalloc(&fout, 256 * 8));
+  int ncu;
+  CK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, 0));
+  const char* paths[3] = {"16-byte direct to LDS", "16-byte to registers", "4-byte to registers"};
+  for (int bgon = 0; bgon < 2; ++bgon)
+    for (int nw : {1024, 4096, 16384})
+      for (int path = 0; path < 3; ++path) {
+        FreshArgs f{pay, ctr, (const u4*)bg, bg_bytes / 16, fout, nw, FR_R, path, bgon};
+        CK(hipMemset(ctr, 0, 4096));
+        CK(hipMemset(fout, 0, 256 * 8));
+        CK(hipMemset(pay, 0, (size_t)FR_R * FR_MAXW * 4));
+        hipLaunchKernelGGL(fresh_kernel, dim3(bgon ? ncu : 2), dim3(FR_NT), 0, 0, f);
+        CK(hipDeviceSynchronize());
+        uint64_t h[256];
+        uint32_t err;
+        CK(hipMemcpy(h, fout, sizeof(h), hipMemcpyDeviceToHost));
+        CK(hipMemcpy(&err, ctr + 96, 4, hipMemcpyDeviceToHost));
+        uint64_t t[FR_R - 2], wrong = 0;
+        for (int r = 2; r < FR_R; ++r) {
+          t[r - 2] = h[r];
+          wrong += h[64 + r];
+        }
+        for (int i = 0; i < FR_R - 2; ++i)  // median
+          for (int j = i + 1; j < FR_R - 2; ++j)
+            if (t[j] < t[i]) { uint64_t x = t[i]; t[i] = t[j]; t[j] = x; }
+        const double us = t[(FR_R - 2) / 2] * 0.01;
+        printf("| %s | %s | %d KB | %.2f | %.1f | %llu%s |\n", bgon ? "254 workgroups" : "none", paths[path], nw / 256, us,
+               nw * 4.0 / (us * 1e3), (unsigned long long)wrong, err ? " (wait timed out)" : "");
+        fflush(stdout);
+      }
   printf("\ndone\n");
   return 0;
 }

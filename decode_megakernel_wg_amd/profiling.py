@@ -240,8 +240,9 @@ def do_probe(a, out):
     lines = header("Synchronisation and streaming costs on this part (hop_probe)",
                    ["decode_megakernel_wg_amd/hop_probe   (built from decode_megakernel_wg_amd/hop_probe.hip by build.build_probe)"],
                    "A standalone program, not the decode kernel: one dependency hop between workgroups on different XCDs "
-                   "(counter protocol against a flag in the data), int64 atomic additions against plain stores, and "
-                   "re-reads of a buffer that fits the last-level cache.  Wall-clock ticks at 100 MHz; HIP events.")
+                   "(counter protocol against a flag in the data), int64 atomic additions against plain stores, "
+                   "re-reads of a buffer that fits the last-level cache, and reads of a payload another workgroup has "
+                   "just published.  Wall-clock ticks at 100 MHz; HIP events.")
     return "mk_probe_sync_and_streaming", lines + body
 
 
