@@ -1893,6 +1893,7 @@ __device__ __forceinline__ void attn_split(KA& a, Desc w, int t, Lds& S) {
 // block (eight lanes per head), then P.V on MFMA: O^T[d][h] += V^T[d][pos] P^T[pos][h] with V^T gathered
 // from the wave's LDS area and P as BF16 hi + lo parts.  Each wave keeps its own running (max, sum, O);
 // the waves are combined once at the end, then the new token (position len, last split only) is added.
+constexpr int WAVE_SHIFT_DIV = 16;
 template <int DH, int GRP>
 __device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
   static_assert(DH == 128 && GRP == 8, "wave-independent attention: d_head 128, eight heads per KV group");
@@ -1949,11 +1950,21 @@ __device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
     return ph < 0 ? 0 : (((int64_t)ph * 2) * Hkv + g) * 16 * DH + (pos & 15) * DH;
   };
   const int nblk = (jc1 - j0 + WB - 1) / WB;
+  // blocks of this wave: round-robin over the waves for R rounds, then the tail round-robin over the first
+  // half of the waves only (they share a SIMD with the second half and, older, are issued first: at many
+  // blocks per wave, the second half finishes last otherwise)
+  const int nb_base = nblk / NW;
+  const int wshift = nb_base / WAVE_SHIFT_DIV;
+  const int R = nb_base - wshift;
+  const int T = nblk - R * NW;
+  const int wcnt = wshift == 0 ? nb_base + (wave < nblk - nb_base * NW ? 1 : 0)
+                               : R + (wave < NW / 2 ? (T - wave + NW / 2 - 1) / (NW / 2) : 0);
+  auto blk = [&](int i) { return (wshift == 0 || i < R) ? i * NW + wave : R * NW + (i - R) * (NW / 2) + wave; };
   uint16_t* const va0 = reinterpret_cast<uint16_t*>(S.xs) + wave * VW;  // the wave's two V areas
   uint16_t* const va1 = S.xb + wave * VW;
   static_assert(NW * VW * 2 <= XS_FLOATS * 4 && NW * VW <= 16 * XBP + 64, "V areas fit the staging areas");
   auto load_k = [&](int i, u4 (&kk)[NKQ]) {  // block i of this wave
-    const int c0 = j0 + (i * NW + wave) * WB;
+    const int c0 = j0 + blk(i) * WB;
 #pragma unroll
     for (int u = 0; u < NKQ; ++u) {
       const int pos = c0 + 4 * u + ((lane & 15) >> 2);
@@ -1962,7 +1973,7 @@ __device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
   };
   // V row r of the block keeps its 16-byte chunk c in slot c ^ 2((r >> 3) & 3) of the row
   auto load_v = [&](int i, uint16_t* va) {
-    const int c0 = j0 + (i * NW + wave) * WB;
+    const int c0 = j0 + blk(i) * WB;
 #pragma unroll
     for (int j = 0; j < VLD; ++j) {
       const int n = j * 64 + lane;
@@ -2046,8 +2057,8 @@ __device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
 #pragma unroll
   for (int db = 0; db < DH / 16; ++db) oacc[db] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int i = 0; wave + i * NW < nblk; ++i) {
-    const int c0 = j0 + (i * NW + wave) * WB;
+  for (int i = 0; i < wcnt; ++i) {
+    const int c0 = j0 + blk(i) * WB;
     // scores: for position quad u and head group hg, D[4r + h][4s + h] is position 4u + r times head
     // 4hg + s over K-part h (hi, then lo); the parts are added across each lane quad
 #pragma unroll
@@ -2097,7 +2108,7 @@ __device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
     if ((lane & 7) == 0) alw[sh] = alpha;
     // this block's V has landed (the loads issued after it are the next block's NKQ + VLD, when that block
     // exists)
-    if (wave + (i + 1) * NW < nblk) __builtin_amdgcn_s_waitcnt((0x0F70 | ((NKQ + VLD) & 15)) | (((NKQ + VLD) >> 4) << 14));
+    if (i + 1 < wcnt) __builtin_amdgcn_s_waitcnt((0x0F70 | ((NKQ + VLD) & 15)) | (((NKQ + VLD) >> 4) << 14));
     else drain_stores();
     const uint16_t* va = i & 1 ? va1 : va0;
     const u4 ph = lds16(hc < GRP ? pbw + hc * WB + 8 * q4 : zrow + 8 * q4);
@@ -2136,7 +2147,7 @@ __device__ __forceinline__ void attn_split_w(KA& a, Desc w, int t, Lds& S) {
     __asm__ volatile("" ::: "memory");
 #pragma unroll
     for (int u = 0; u < NKQ; ++u) kc[u] = kx[u];
-    if (wave + (i + 2) * NW < nblk) {
+    if (i + 2 < wcnt) {
       load_k(i + 2, kx);
       load_v(i + 2, i & 1 ? va1 : va0);
     }
